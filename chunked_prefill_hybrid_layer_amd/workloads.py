@@ -1,0 +1,275 @@
+"""Seeded synthetic inputs for the hybrid-batch decoder layer.
+
+This module only draws random numbers and lays out caller-side arrays
+(weights, activations, batch composition, block tables, cached K/V contents).
+It holds none of the layer's arithmetic and none of the paged-KV indexing:
+positions, slots, norms, projections and attention live in the library and,
+independently, in the oracle.  Both sides consume exactly the arrays built
+here.
+
+Batch composition follows the hybrid batches of the Sarathi-Serve reading
+notes (zhongzhuzhou.org), §3.2 "Stall-free hybrid batching": prefill-chunk
+tokens of one or more prompts plus one token per running decode, with the
+total under a token budget tau.  Packing order is chunks first (argument
+order), then decodes.
+
+Value recipe (the pages give none; these are readings):
+  * projection weights N(0, 0.02), norm gains 1 + 0.02 N(0, 1), all rounded
+    to bf16;
+  * layer input x ~ N(0, x_std) rounded to bf16 and stored as fp32;
+  * cached K/V of synthesized prefixes N(0, 1) rounded to bf16;
+  * block tables: the pool holds every page the batch needs plus 12.5 %
+    decoy pages; a seeded permutation of the pool is dealt out in sequence
+    order, so no page is shared; unused table entries are -1.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional
+
+import numpy as np
+
+PAGE_SIZE = 16
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bf16 (ties to even); returns uint16 bits."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    nan = np.isnan(a)
+    if nan.any():
+        r[nan] = 0x7FC0
+    return r
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to float32."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+@dataclass
+class Dims:
+    hidden: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    ffn_dim: int
+    page_size: int = PAGE_SIZE
+    rms_eps: float = 1e-5
+    rope_theta: float = 10000.0
+
+    @property
+    def group(self) -> int:
+        return self.n_q_heads // self.n_kv_heads
+
+    @property
+    def qkv_dim(self) -> int:
+        return (self.n_q_heads + 2 * self.n_kv_heads) * self.head_dim
+
+
+@dataclass
+class Batch:
+    """One hybrid batch: chunk pieces (new tokens + already-cached prefix)
+    and decodes (context already cached), with per-sequence block tables.
+
+    Sequence order (= block-table row order) is the chunks, then the decodes.
+    """
+    chunk_len: np.ndarray          # int32 [n_chunks]
+    chunk_prefix: np.ndarray       # int32 [n_chunks]
+    decode_ctx: np.ndarray         # int32 [n_decodes]
+    block_table: np.ndarray        # int32 [n_seq][max_pages], -1 = unused
+    num_pages: int
+    token_budget: int
+
+    @property
+    def n_chunks(self) -> int:
+        return int(len(self.chunk_len))
+
+    @property
+    def n_decodes(self) -> int:
+        return int(len(self.decode_ctx))
+
+    @property
+    def n_seq(self) -> int:
+        return self.n_chunks + self.n_decodes
+
+    @property
+    def n_tokens(self) -> int:
+        return int(np.sum(self.chunk_len)) + self.n_decodes
+
+    def cached_lengths(self) -> np.ndarray:
+        """Tokens already in the cache per sequence (chunk prefix / decode context)."""
+        return np.concatenate([self.chunk_prefix, self.decode_ctx]).astype(np.int64)
+
+    def new_lengths(self) -> np.ndarray:
+        return np.concatenate([self.chunk_len, np.ones(self.n_decodes, np.int32)]).astype(np.int64)
+
+
+@dataclass
+class Workload:
+    name: str
+    dims: Dims
+    weights: Dict[str, np.ndarray]     # bf16 bits; projections [d_out][d_in]
+    x: np.ndarray                      # float32 [T][H], bf16-representable
+    batch: Batch
+    # cached K/V contents per sequence, logical order [len][n_kv][d] as bf16 bits
+    prefix_k: List[np.ndarray] = field(default_factory=list)
+    prefix_v: List[np.ndarray] = field(default_factory=list)
+    meta: Dict[str, object] = field(default_factory=dict)
+
+
+# --------------------------------------------------------------------------
+# building blocks
+
+
+def _streams(seed: int, n: int = 6):
+    ss = np.random.SeedSequence(seed)
+    return [np.random.Generator(np.random.PCG64(s)) for s in ss.spawn(n)]
+
+
+def make_weights(dims: Dims, rng: np.random.Generator, std: float = 0.02) -> Dict[str, np.ndarray]:
+    H, d, F = dims.hidden, dims.head_dim, dims.ffn_dim
+    shapes = {
+        "w_q": (dims.n_q_heads * d, H),
+        "w_k": (dims.n_kv_heads * d, H),
+        "w_v": (dims.n_kv_heads * d, H),
+        "w_o": (H, dims.n_q_heads * d),
+        "w_g": (F, H),
+        "w_u": (F, H),
+        "w_d": (H, F),
+    }
+    w = {}
+    for name, shp in shapes.items():
+        w[name] = f32_to_bf16_bits(rng.standard_normal(shp, dtype=np.float32) * np.float32(std))
+    for name in ("g_attn", "g_ffn"):
+        w[name] = f32_to_bf16_bits(1.0 + 0.02 * rng.standard_normal(H, dtype=np.float32))
+    return w
+
+
+def make_activations(n_tokens: int, hidden: int, rng: np.random.Generator, std: float) -> np.ndarray:
+    x = rng.standard_normal((n_tokens, hidden), dtype=np.float32) * np.float32(std)
+    return bf16_bits_to_f32(f32_to_bf16_bits(x))
+
+
+def deal_block_tables(kv_lens: np.ndarray, page_size: int, rng: np.random.Generator,
+                      decoy_frac: float = 0.125, max_pages: Optional[int] = None):
+    """Deal a shuffled page pool to sequences needing ceil(kv_len/page) pages each."""
+    kv_lens = np.asarray(kv_lens, dtype=np.int64)
+    need = (kv_lens + page_size - 1) // page_size
+    total = int(need.sum())
+    num_pages = total + max(1, int(np.ceil(total * decoy_frac)))
+    perm = rng.permutation(num_pages).astype(np.int32)
+    mp = int(need.max()) if max_pages is None else int(max_pages)
+    bt = np.full((len(kv_lens), max(mp, 1)), -1, dtype=np.int32)
+    cur = 0
+    for s, n in enumerate(need):
+        bt[s, :n] = perm[cur:cur + n]
+        cur += int(n)
+    return bt, num_pages
+
+
+def synth_prefix(length: int, dims: Dims, rng: np.random.Generator, std: float = 1.0):
+    shp = (int(length), dims.n_kv_heads, dims.head_dim)
+    k = f32_to_bf16_bits(rng.standard_normal(shp, dtype=np.float32) * np.float32(std))
+    v = f32_to_bf16_bits(rng.standard_normal(shp, dtype=np.float32) * np.float32(std))
+    return k, v
+
+
+def build_workload(name: str, dims: Dims, chunk_len, chunk_prefix, decode_ctx, seed: int,
+                   x_std: float = 1.0, token_budget: Optional[int] = None,
+                   synth_prefixes: bool = True, max_pages: Optional[int] = None,
+                   cache_std: float = 1.0) -> Workload:
+    rw, rx, _rl, rb, rc, _ = _streams(seed)
+    chunk_len = np.asarray(chunk_len, dtype=np.int32)
+    chunk_prefix = np.asarray(chunk_prefix, dtype=np.int32)
+    decode_ctx = np.asarray(decode_ctx, dtype=np.int32)
+    cached = np.concatenate([chunk_prefix, decode_ctx]).astype(np.int64)
+    new = np.concatenate([chunk_len, np.ones(len(decode_ctx), np.int32)]).astype(np.int64)
+    bt, num_pages = deal_block_tables(cached + new, dims.page_size, rb, max_pages=max_pages)
+    T = int(new.sum())
+    batch = Batch(chunk_len, chunk_prefix, decode_ctx, bt, num_pages,
+                  int(token_budget) if token_budget is not None else T)
+    w = make_weights(dims, rw)
+    x = make_activations(T, dims.hidden, rx, x_std)
+    wl = Workload(name, dims, w, x, batch)
+    if synth_prefixes:
+        # one child stream per sequence, so any subset can be regenerated alone
+        children = np.random.SeedSequence(int(rc.integers(2**63))).spawn(len(cached))
+        for s, c in enumerate(cached):
+            g = np.random.Generator(np.random.PCG64(children[s]))
+            k, v = synth_prefix(int(c), dims, g, cache_std)
+            wl.prefix_k.append(k)
+            wl.prefix_v.append(v)
+    return wl
+
+
+# --------------------------------------------------------------------------
+# named workloads (shapes and length mixes of the pages' configurations)
+
+TINY = Dims(hidden=256, n_q_heads=4, n_kv_heads=4, head_dim=64, ffn_dim=512)
+MISTRAL = Dims(hidden=4096, n_q_heads=32, n_kv_heads=8, head_dim=128, ffn_dim=14336)
+YI = Dims(hidden=7168, n_q_heads=56, n_kv_heads=8, head_dim=128, ffn_dim=20480)
+
+
+def _lognormal_ctx(rng, n, median, cap, sigma=1.0):
+    c = np.rint(rng.lognormal(np.log(median), sigma, size=n))
+    return np.clip(np.minimum(c, cap), 1, None).astype(np.int32)
+
+
+def tiny(seed: int = 0) -> Workload:
+    """Tiny layer: one 256-token prompt whose 3rd 64-token chunk (prefix 128)
+    runs with 4 decodes of context 16/40/77/128.  Weights and activations
+    N(0, 0.02).  The prompt's own prefix is not synthesized: callers produce it
+    by running chunks 1 and 2 through the layer (see ``tiny_prompt_chunks``)."""
+    wl = build_workload("tiny", TINY, [64], [128], [16, 40, 77, 128], seed,
+                        x_std=0.02, synth_prefixes=True)
+    wl.meta["prompt_len"] = 256
+    wl.meta["chunk_size"] = 64
+    return wl
+
+
+def tiny_prompt_chunks(wl: Workload, seed: int = 0):
+    """Inputs for chunks 1 and 2 of the tiny prompt (positions 0..127): x rows
+    drawn from their own stream so chunk 3's x stays that of ``tiny``."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 1])))
+    return [make_activations(64, wl.dims.hidden, rng, 0.02) for _ in range(2)]
+
+
+def mistral_tau512(seed: int = 0) -> Workload:
+    """Mistral-7B-shaped layer, tau = 512: one 480-token chunk with prefix
+    U{0..3584} plus 32 decodes with context U{512..4096}."""
+    _, _, rl, _, _, _ = _streams(seed)
+    prefix = int(rl.integers(0, 3584, endpoint=True))
+    ctx = rl.integers(512, 4096, size=32, endpoint=True).astype(np.int32)
+    wl = build_workload("mistral_tau512", MISTRAL, [480], [prefix], ctx, seed, token_budget=512)
+    return wl
+
+
+def tau_sweep(tau: int, seed: int = 0) -> Workload:
+    """tau sweep point: one chunk of tau-64 tokens (prefix 1792) plus 64
+    decodes with context lognormal(median 1024, sigma 1) capped at 8192."""
+    _, _, rl, _, _, _ = _streams(seed)
+    ctx = _lognormal_ctx(rl, 64, 1024, 8192)
+    return build_workload(f"tau_sweep_{tau}", MISTRAL, [tau - 64], [1792], ctx, seed,
+                          token_budget=tau)
+
+
+def yi_tau2048(seed: int = 0) -> Workload:
+    """Yi-34B-shaped layer, tau = 2048: chunks of 768 at prefixes 0 and 6144
+    plus 512 decodes with context lognormal(median 2048, sigma 1) capped at 16384."""
+    _, _, rl, _, _, _ = _streams(seed)
+    ctx = _lognormal_ctx(rl, 512, 2048, 16384)
+    return build_workload("yi_tau2048", YI, [768, 768], [0, 6144], ctx, seed, token_budget=2048)
+
+
+def small(seed: int = 0, n_q: int = 8, n_kv: int = 2, head_dim: int = 128,
+          chunk_len=(77, 130), chunk_prefix=(45, 0), decode_ctx=(1, 15, 16, 17, 200, 333, 1000),
+          hidden: int = 512, ffn: int = 1024) -> Workload:
+    """Small layer for full-output parity: several GEMM and attention tiles,
+    ragged chunks starting mid-page, decodes around page boundaries."""
+    d = Dims(hidden=hidden, n_q_heads=n_q, n_kv_heads=n_kv, head_dim=head_dim, ffn_dim=ffn)
+    return build_workload(f"small_g{n_q // n_kv}_d{head_dim}", d, list(chunk_len), list(chunk_prefix),
+                          list(decode_ctx), seed)

@@ -1,0 +1,339 @@
+"""Oracle for one decoder-layer forward over a hybrid (chunked-prefill + decode) batch.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the library imports, links or calls this
+module; only the tests, the smoke check and the benchmark's CPU-baseline leg do.
+It shares no code with the HIP path: it derives token positions, page slots,
+norms, rotary embeddings, attention and the gated FFN on its own, in float64
+with numpy (the linear layers use numpy's matrix product; every other
+reduction is an elementwise product followed by numpy's sum over one axis, so
+each output row depends only on that row's inputs, not on the batch around it).
+
+Sources (the pages):
+  [notes]  "Sarathi-Serve reading notes" (zhongzhuzhou.org, 2026-05-20):
+           §1.6 linear-layer cost, §2.3/§3.1 chunked prefills, §3.2 hybrid
+           batches, §3.4 scheduling loop, §3.5 paged KV, §7.5b chunked
+           attention work identity, §7.6 worked Yi-34B iteration.
+  [cp]     "Chunked Prefill" (bowenzhou.top): "mechanism" (chunks continue the
+           KV through paged blocks) and the hybrid-iteration roofline.
+
+What the layer computes.  The pages never write a layer out; they state that a
+chunk's tokens attend to everything earlier chunks of the same prompt wrote
+plus, causally, themselves ([notes] §3.1, §7.5b), that a decode attends to its
+own cached context ([notes] §3.2), and that all tokens of the batch share the
+linear layers ([notes] §1.6, [cp] roofline).  The decoder block itself is the
+pre-norm Llama/Mistral form (RMSNorm, rotary embedding on q/k, grouped-query
+attention, SwiGLU FFN, two residual adds, no biases).  Readings taken where the
+pages are silent:
+  * RMSNorm eps = 1e-5 (from dims); gains multiply after normalisation.
+  * RoPE: rotate-half pairing (i, i + d/2), inv_freq_i = theta^(-2i/d),
+    theta from dims (1e4); angles and cos/sin in float64.
+  * Softmax scale 1/sqrt(d); q head h reads kv head floor(h / g), g = n_q/n_kv.
+  * A decode's context length counts tokens already cached: its token sits at
+    position ctx, is appended there and attends ctx + 1 keys -- a 1-token
+    chunk whose prefix is ctx.
+  * Sequence order is chunks (argument order) then decodes; tokens are packed
+    in that order.
+  * Storage precision.  "bf16 layer" is read as: every activation tensor that
+    passes between steps is held in bf16 -- the normed input, q/k/v after the
+    rotary embedding (k/v are what the bf16 KV cache stores), the attention
+    output, the normed residual and the gated FFN activation -- while the
+    residual stream x, h1, y stays fp32.  With ``storage="bf16"`` the oracle
+    computes every step exactly (float64) from its stored inputs and rounds its
+    output once to that storage type (round to nearest even).  With
+    ``storage="exact"`` nothing is rounded.
+
+Page layout of the oracle's own cache: ``k[page][kv_head][slot][d]`` (logical
+order, float64); a sequence's position p lives in page
+``block_table[s][p // page_size]`` at slot ``p % page_size`` ([notes] §3.5,
+[cp] "mechanism": KV continues across chunks through paged blocks).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+# ----------------------------------------------------------------------------
+# number formats
+
+
+def bf16_bits_to_float(bits) -> np.ndarray:
+    """bf16 bit patterns -> float64 (exact)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def round_bf16(x) -> np.ndarray:
+    """Round float64 values to the nearest bf16 value, ties to even, in one step
+    (no intermediate float32).  bf16 keeps 8 significant bits and float32's
+    exponent range; below 2**-126 the spacing is fixed at 2**-133."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.array(x, copy=True)
+    finite = np.isfinite(x) & (x != 0)
+    xf = x[finite]
+    _, e = np.frexp(xf)                      # xf = m * 2**e, 0.5 <= |m| < 1
+    q = np.ldexp(1.0, np.maximum(e - 8, -133))  # spacing of bf16 values near xf
+    r = np.rint(xf / q) * q                  # np.rint rounds half to even
+    over = np.abs(r) > 3.3895313892515355e38   # largest finite bf16
+    r[over] = np.copysign(np.inf, xf[over])
+    out[finite] = r
+    return out
+
+
+def round_f32(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def bf16_bits(x) -> np.ndarray:
+    """float64 values already on the bf16 grid -> bit patterns."""
+    f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+# ----------------------------------------------------------------------------
+# batch layout: which token sits at which position of which sequence
+
+
+@dataclass
+class TokenLayout:
+    seq: np.ndarray       # int64 [T]  sequence of each packed token
+    pos: np.ndarray       # int64 [T]  position of the token in its sequence
+    q_start: np.ndarray   # int64 [S+1] first packed token of each sequence
+    cached: np.ndarray    # int64 [S]  tokens already cached before this batch
+    kv_len: np.ndarray    # int64 [S]  cached + new tokens
+
+
+def token_layout(chunk_len: Sequence[int], chunk_prefix: Sequence[int],
+                 decode_ctx: Sequence[int]) -> TokenLayout:
+    """Chunk i of a prompt covers positions [prefix, prefix + len) ([notes] §3.1:
+    chunk i covers [(i-1)C, iC)); a decode is one token at position ctx.
+    Chunks first, then decodes ([notes] §3.2 hybrid batch)."""
+    cached = [int(p) for p in chunk_prefix] + [int(c) for c in decode_ctx]
+    new = [int(n) for n in chunk_len] + [1] * len(decode_ctx)
+    seq, pos, q_start = [], [], [0]
+    for s, (c, n) in enumerate(zip(cached, new)):
+        for j in range(n):
+            seq.append(s)
+            pos.append(c + j)
+        q_start.append(q_start[-1] + n)
+    cached_a = np.array(cached, dtype=np.int64)
+    return TokenLayout(np.array(seq, dtype=np.int64), np.array(pos, dtype=np.int64),
+                       np.array(q_start, dtype=np.int64), cached_a,
+                       cached_a + np.array(new, dtype=np.int64))
+
+
+def page_of(block_table: np.ndarray, seq: int, pos: int, page_size: int):
+    """Physical (page, slot) of position ``pos`` of sequence ``seq``."""
+    page = int(block_table[seq][pos // page_size])
+    return page, pos % page_size
+
+
+def hybrid_batch_budget(n_decodes: int, chunk_takes: Sequence[int], tau: int):
+    """Token accounting of one hybrid batch ([notes] §3.2, §3.4): decodes are
+    admitted first (one token each), then chunk pieces; returns the budget left
+    after the decodes and after each chunk, and the batch's token count.
+    Raises if the batch exceeds tau."""
+    left = [tau - n_decodes]
+    for c in chunk_takes:
+        left.append(left[-1] - int(c))
+    total = n_decodes + sum(int(c) for c in chunk_takes)
+    if total > tau:
+        raise ValueError(f"hybrid batch of {total} tokens exceeds the budget {tau}")
+    return left, total
+
+
+# ----------------------------------------------------------------------------
+# the oracle's paged KV cache
+
+
+class PagedCache:
+    """K and V pages in logical order [page][kv_head][slot][d], float64."""
+
+    def __init__(self, num_pages: int, n_kv: int, page_size: int, head_dim: int,
+                 fill: float = np.nan):
+        shp = (num_pages, n_kv, page_size, head_dim)
+        self.k = np.full(shp, fill, dtype=np.float64)
+        self.v = np.full(shp, fill, dtype=np.float64)
+        self.page_size = page_size
+
+    def write(self, block_table, seq: int, pos: int, k_row: np.ndarray, v_row: np.ndarray):
+        page, slot = page_of(block_table, seq, pos, self.page_size)
+        self.k[page, :, slot, :] = k_row
+        self.v[page, :, slot, :] = v_row
+
+    def gather(self, block_table, seq: int, length: int):
+        """Keys/values of positions 0..length-1 of ``seq``: [length][n_kv][d]."""
+        pos = np.arange(length)
+        pages = np.asarray(block_table[seq])[pos // self.page_size]
+        slots = pos % self.page_size
+        return self.k[pages, :, slots, :], self.v[pages, :, slots, :]
+
+    def load_prefix(self, block_table, seq: int, k_rows: np.ndarray, v_rows: np.ndarray):
+        """Place already-cached K/V (positions 0..len-1) of ``seq``."""
+        n = k_rows.shape[0]
+        pos = np.arange(n)
+        pages = np.asarray(block_table[seq])[pos // self.page_size]
+        slots = pos % self.page_size
+        self.k[pages, :, slots, :] = k_rows
+        self.v[pages, :, slots, :] = v_rows
+
+
+# ----------------------------------------------------------------------------
+# layer pieces
+
+
+def rmsnorm(x: np.ndarray, gain: np.ndarray, eps: float) -> np.ndarray:
+    """x / sqrt(mean(x^2) + eps) * gain, row-wise."""
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * gain
+
+
+def rope_angles(pos: np.ndarray, head_dim: int, theta: float) -> np.ndarray:
+    """angle[t][i] = pos_t * theta^(-2i/d), i < d/2."""
+    half = head_dim // 2
+    inv_freq = theta ** (-(2.0 * np.arange(half, dtype=np.float64)) / head_dim)
+    return np.asarray(pos, dtype=np.float64)[:, None] * inv_freq[None, :]
+
+
+def rope(u: np.ndarray, pos: np.ndarray, theta: float) -> np.ndarray:
+    """Rotate-half rotary embedding of u[t][head][d] by position pos[t]."""
+    d = u.shape[-1]
+    half = d // 2
+    ang = rope_angles(pos, d, theta)[:, None, :]
+    c, s = np.cos(ang), np.sin(ang)
+    a, b = u[..., :half], u[..., half:]
+    return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    return z / (1.0 + np.exp(-z))
+
+
+def linear(x: np.ndarray, w: np.ndarray):
+    """y = x . w^T for w stored [d_out][d_in]; returns y and the flop count
+    2 * n * d_in * d_out of the product ([notes] §1.6).
+
+    numpy's BLAS sends products with very few rows to dedicated small-matrix
+    routines whose summation order differs from the general one; fewer than 16
+    rows are therefore padded with zero rows, so that every row's result is
+    independent of how many rows share the call."""
+    n, d_in = x.shape
+    d_out = w.shape[0]
+    if n < 16:
+        y = (np.concatenate([x, np.zeros((16 - n, d_in))]) @ w.T)[:n]
+    else:
+        y = x @ w.T
+    return y, 2 * n * d_in * d_out
+
+
+def paged_attention(q: np.ndarray, tok_seq: np.ndarray, tok_pos: np.ndarray,
+                    cache: PagedCache, block_table: np.ndarray, n_kv: int):
+    """Attention of queries q[i][head][d] over their own sequences' paged KV.
+
+    Query i (sequence tok_seq[i], position tok_pos[i]) sees exactly keys
+    0..tok_pos[i] of its sequence -- a chunk's token sees every earlier chunk's KV plus,
+    causally, its own chunk ([notes] §3.1, §7.5b); a decode sees its whole
+    context plus itself.  Scores q.k / sqrt(d), softmax (max first, then
+    exp(s - max), then the weighted sum of V over the total weight); q head h
+    reads kv head h // (n_q / n_kv).  Returns o[i][head][d] and the number of
+    (query, key) pairs attended.
+    """
+    n, nq, d = q.shape
+    g = nq // n_kv
+    scale = 1.0 / math.sqrt(d)
+    o = np.zeros((n, nq, d), dtype=np.float64)
+    pairs = 0
+    by_seq: Dict[int, list] = {}
+    for i in range(n):
+        by_seq.setdefault(int(tok_seq[i]), []).append(i)
+    for s, idx in by_seq.items():
+        length = int(np.max(np.asarray(tok_pos)[idx])) + 1
+        ks, vs = cache.gather(block_table, s, length)
+        for i in idx:
+            p = int(tok_pos[i])
+            pairs += p + 1
+            for h in range(nq):
+                kvh = h // g
+                kk, vv = ks[:p + 1, kvh], vs[:p + 1, kvh]
+                sc = np.sum(kk * q[i, h], axis=1) * scale      # q . k_j / sqrt(d)
+                e = np.exp(sc - np.max(sc))
+                o[i, h] = np.sum(e[:, None] * vv, axis=0) / np.sum(e)
+    return o, pairs
+
+
+# ----------------------------------------------------------------------------
+# the layer
+
+
+@dataclass
+class LayerResult:
+    y: np.ndarray            # [len(rows)][H]
+    rows: np.ndarray         # packed token indices of y's rows
+    pairs: int               # (query, key) pairs attended by the computed rows
+    linear_flops: int        # 2 n d_in d_out summed over the products actually run
+    attn_out: Optional[np.ndarray] = None   # [len(rows)][n_q*d] (stored precision)
+
+
+def layer_forward(dims, w: Dict[str, np.ndarray], x: np.ndarray, chunk_len, chunk_prefix,
+                  decode_ctx, block_table: np.ndarray, cache: PagedCache,
+                  storage: str = "bf16", rows: Optional[Sequence[int]] = None,
+                  keep_attn: bool = False) -> LayerResult:
+    """One pre-norm decoder layer over the hybrid batch; writes the batch's new
+    K/V into ``cache`` and returns y for ``rows`` (all tokens by default).
+
+    ``w`` holds float64 arrays: w_q [n_q d][H], w_k, w_v [n_kv d][H],
+    w_o [H][n_q d], w_g, w_u [F][H], w_d [H][F], g_attn, g_ffn [H].
+    K/V are computed for every token (the cache needs them); steps after the
+    projections run only for ``rows`` -- exact for those rows.
+    """
+    if storage == "bf16":
+        act, res = round_bf16, round_f32
+    elif storage == "exact":
+        act = res = (lambda a: a)
+    else:
+        raise ValueError(storage)
+    lay = token_layout(chunk_len, chunk_prefix, decode_ctx)
+    T = len(lay.seq)
+    d = dims.head_dim
+    nq, nkv = dims.n_q_heads, dims.n_kv_heads
+    rows = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
+    x = np.asarray(x, dtype=np.float64)
+    flops = 0
+
+    # a1: RMSNorm of the input (all tokens: K/V need it)
+    xn = act(rmsnorm(x, w["g_attn"], dims.rms_eps))
+    # a2 + a3: projections and rotary embedding
+    k, f = linear(xn, w["w_k"]); flops += f
+    v, f = linear(xn, w["w_v"]); flops += f
+    q, f = linear(xn[rows], w["w_q"]); flops += f
+    k = act(rope(k.reshape(T, nkv, d), lay.pos, dims.rope_theta))
+    v = act(v.reshape(T, nkv, d))
+    q = act(rope(q.reshape(len(rows), nq, d), lay.pos[rows], dims.rope_theta))
+
+    # a4: new K/V go into the paged cache at their sequence positions
+    for t in range(T):
+        cache.write(block_table, int(lay.seq[t]), int(lay.pos[t]), k[t], v[t])
+
+    # a5: each token attends causally to positions 0..pos of its own sequence
+    o, pairs = paged_attention(q, lay.seq[rows], lay.pos[rows], cache, block_table, nkv)
+    o = act(o.reshape(len(rows), nq * d))
+
+    # a6: output projection + residual
+    ao, f = linear(o, w["w_o"]); flops += f
+    h1 = res(x[rows] + ao)
+    # a7 + a8: RMSNorm, gate/up projections and SwiGLU
+    h1n = act(rmsnorm(h1, w["g_ffn"], dims.rms_eps))
+    gt, f1 = linear(h1n, w["w_g"])
+    up, f2 = linear(h1n, w["w_u"])
+    a = act(silu(gt) * up)
+    # a9: down projection + residual
+    dn, f3 = linear(a, w["w_d"])
+    flops += f1 + f2 + f3
+    y = res(h1 + dn)
+    return LayerResult(y, rows, pairs, flops, o if keep_attn else None)
+
+
+def weights_to_float(wbits: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
+    return {k: bf16_bits_to_float(v) for k, v in wbits.items()}

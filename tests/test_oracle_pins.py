@@ -1,0 +1,422 @@
+"""Pins for the oracle: each check ties an oracle function to something other
+than itself -- a value the pages print, a closed form, an invariant the pages
+state, a special case with a known answer, an independent library routine, or
+brute force on tiny inputs.  CPU only."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import hybrid_layer as O
+from chunked_prefill_hybrid_layer_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- bf16 rounding
+
+def test_round_bf16_matches_torch_on_float32_inputs():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(1)
+    x = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32) * 3,
+        (rng.standard_normal(2000) * 1e-30).astype(np.float32),
+        np.array([1 + 2**-8, 1 + 3 * 2**-8, -(1 + 2**-8), 65504, 1e-40, 3e38], np.float32),
+    ])
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    got = O.round_bf16(x.astype(np.float64))
+    assert np.array_equal(got, ref)
+
+
+def test_round_bf16_single_step_closed_forms():
+    # ties go to the even significand
+    assert O.round_bf16(np.array([1 + 2**-8]))[0] == 1.0
+    assert O.round_bf16(np.array([1 + 3 * 2**-8]))[0] == 1 + 2**-6
+    # a value just above a tie rounds up; going through float32 first would lose that
+    assert O.round_bf16(np.array([1 + 2**-8 + 2**-40]))[0] == 1 + 2**-7
+    assert O.round_bf16(np.array([-2.0**-130]))[0] == -2.0**-130  # subnormal grid 2^-133
+    assert O.round_bf16(np.array([0.0]))[0] == 0.0
+
+
+# ---------------------------------------------------------------- batch layout
+
+def test_worked_example_token_accounting():
+    g = json.load(open(os.path.join(GOLDEN, "worked_example_yi34b.json")))
+    e = g["expected"]
+    ra, rb = g["R_A"], g["R_B"]
+    left, total = O.hybrid_batch_budget(g["n_decodes"], [ra["chunk"], rb["chunk"]], g["tau"])
+    assert left == [e["budget_after_decodes"], e["budget_after_R_A"], e["budget_after_R_B"]]
+    assert total == e["total_tokens"]
+    assert ra["prompt_len"] - ra["cached_before"] == e["R_A_prefill_remaining_before"]
+    ctx = [100, 250, 3000, 17, 64, 999]
+    lay = O.token_layout([ra["chunk"], rb["chunk"]], [ra["cached_before"], rb["cached_before"]], ctx)
+    assert len(lay.seq) == e["total_tokens"]
+    assert lay.kv_len[0] == e["R_A_kv_len_after"]
+    assert lay.kv_len[1] == e["R_B_kv_len_after"]
+    assert ra["prompt_len"] - lay.kv_len[0] == e["R_A_remaining_prefill_after"]
+    assert e["R_A_remaining_prefill_after"] - g["chunk_size"] == e["R_A_tail_after_next_chunk"]
+    assert list(lay.q_start) == [0, 1024, 1824, 1825, 1826, 1827, 1828, 1829, 1830]
+    with pytest.raises(ValueError):
+        O.hybrid_batch_budget(g["n_decodes"], [ra["chunk"], rb["chunk"]], e["total_tokens"] - 1)
+
+
+def test_chunk_i_covers_its_prompt_slice():
+    # chunk i (1-based) of size C covers positions [(i-1)C, iC)
+    C = 64
+    for i in range(1, 5):
+        lay = O.token_layout([C], [(i - 1) * C], [])
+        assert list(lay.pos) == list(range((i - 1) * C, i * C))
+    lay = O.token_layout([3], [5], [0, 7])
+    assert list(lay.pos) == [5, 6, 7, 0, 7]
+    assert list(lay.seq) == [0, 0, 0, 1, 2]
+    assert list(lay.kv_len) == [8, 1, 8]
+
+
+def test_page_of_follows_block_table():
+    bt = np.array([[7, 2, 9], [4, 0, -1]])
+    assert O.page_of(bt, 0, 0, 16) == (7, 0)
+    assert O.page_of(bt, 0, 17, 16) == (2, 1)
+    assert O.page_of(bt, 0, 47, 16) == (9, 15)
+    assert O.page_of(bt, 1, 16, 16) == (0, 0)
+
+
+# ---------------------------------------------------------------- small pieces
+
+def test_rmsnorm_closed_forms():
+    eps = 1e-5
+    gain = np.array([1.0, 2.0, 0.5, -1.0])
+    c = 3.0
+    got = O.rmsnorm(np.full((1, 4), c), gain, eps)
+    assert np.allclose(got, c / math.sqrt(c * c + eps) * gain, rtol=1e-15, atol=0)
+    got = O.rmsnorm(np.array([[3.0, 4.0]]), np.ones(2), eps)
+    assert np.allclose(got, np.array([[3.0, 4.0]]) / math.sqrt(12.5 + eps), rtol=1e-15, atol=0)
+
+
+def test_rope_closed_forms():
+    theta = 10000.0
+    u = np.array([[[0.3, -1.7]]])                     # d = 2: one pair, frequency 1
+    for p in (0, 1, 5, 1000):
+        got = O.rope(u, np.array([p]), theta)[0, 0]
+        c, s = math.cos(p), math.sin(p)
+        assert np.allclose(got, [0.3 * c + 1.7 * s, -1.7 * c + 0.3 * s], rtol=0, atol=1e-14)
+    # d = 4: pairs (0, 2) at frequency 1 and (1, 3) at theta^(-1/2); rotate-half pairing
+    u = np.array([[[1.0, 2.0, 3.0, 4.0]]])
+    p = 7
+    got = O.rope(u, np.array([p]), theta)[0, 0]
+    a0, a1 = p * 1.0, p * theta ** -0.5
+    exp = [1 * math.cos(a0) - 3 * math.sin(a0), 2 * math.cos(a1) - 4 * math.sin(a1),
+           3 * math.cos(a0) + 1 * math.sin(a0), 4 * math.cos(a1) + 2 * math.sin(a1)]
+    assert np.allclose(got, exp, rtol=0, atol=1e-13)
+
+
+def test_rope_invariants():
+    rng = np.random.default_rng(2)
+    q = rng.standard_normal((1, 1, 64))
+    k = rng.standard_normal((1, 1, 64))
+    assert np.array_equal(O.rope(q, np.array([0]), 1e4), q)       # position 0 is identity
+    r = O.rope(q, np.array([123]), 1e4)
+    assert np.allclose(r[..., :32] ** 2 + r[..., 32:] ** 2, q[..., :32] ** 2 + q[..., 32:] ** 2,
+                       rtol=1e-12)
+    # <R(m) q, R(n) k> depends on m - n only
+    def dot(m, n):
+        return float(np.sum(O.rope(q, np.array([m]), 1e4) * O.rope(k, np.array([n]), 1e4)))
+    for (m, n, dlt) in [(10, 3, 40), (0, 17, 1000), (500, 499, 7)]:
+        assert math.isclose(dot(m, n), dot(m + dlt, n + dlt), rel_tol=1e-9, abs_tol=1e-9)
+
+
+def test_silu_closed_forms():
+    z = np.array([0.0, 1.0, -1.0, 40.0, -40.0])
+    s = O.silu(z)
+    assert s[0] == 0.0
+    assert math.isclose(s[1], 1 / (1 + math.exp(-1)), rel_tol=1e-15)
+    assert math.isclose(s[2], -1 / (1 + math.e), rel_tol=1e-15)
+    assert math.isclose(s[3], 40.0, rel_tol=1e-15)
+    assert abs(s[4]) < 1e-15
+
+
+def test_linear_against_brute_force_loops_and_flop_count():
+    rng = np.random.default_rng(3)
+    n, d_in, d_out = 3, 5, 4
+    x = rng.standard_normal((n, d_in))
+    w = rng.standard_normal((d_out, d_in))
+    y, flops = O.linear(x, w)
+    ops = 0
+    ref = [[0.0] * d_out for _ in range(n)]
+    for i in range(n):
+        for j in range(d_out):
+            acc = 0.0
+            for kk in range(d_in):
+                acc += x[i][kk] * w[j][kk]
+                ops += 2
+            ref[i][j] = acc
+    assert np.allclose(y, np.array(ref), rtol=1e-14, atol=1e-14)
+    assert flops == ops == 2 * n * d_in * d_out
+    # one-hot rows pick out weight columns
+    eye = np.eye(d_in)
+    assert np.array_equal(O.linear(eye, w)[0], w.T)
+
+
+# ---------------------------------------------------------------- attention
+
+def _cache_with(keys, vals, page_size=4, n_pages=None, seed=0):
+    """Put one sequence's K/V (positions 0..L-1) on shuffled pages."""
+    L, nkv, d = keys.shape
+    need = (L + page_size - 1) // page_size
+    n_pages = n_pages or need + 3
+    rng = np.random.default_rng(seed)
+    pages = rng.permutation(n_pages)[:need]
+    bt = np.full((1, need), -1, dtype=np.int64)
+    bt[0] = pages
+    cache = O.PagedCache(n_pages, nkv, page_size, d)
+    cache.load_prefix(bt, 0, keys, vals)
+    return cache, bt
+
+
+def test_attention_brute_force_tiny():
+    rng = np.random.default_rng(4)
+    L, d = 6, 4
+    keys = rng.standard_normal((L, 1, d))
+    vals = rng.standard_normal((L, 1, d))
+    cache, bt = _cache_with(keys, vals)
+    q = rng.standard_normal((3, 1, d))
+    pos = np.array([5, 2, 0])
+    o, pairs = O.paged_attention(q, np.zeros(3, int), pos, cache, bt, 1)
+    assert pairs == 6 + 3 + 1
+    for i in range(3):
+        w = [math.exp(sum(q[i, 0, c] * keys[j, 0, c] for c in range(d)) / math.sqrt(d))
+             for j in range(pos[i] + 1)]
+        tot = sum(w)
+        for c in range(d):
+            ref = sum(w[j] * vals[j, 0, c] for j in range(pos[i] + 1)) / tot
+            assert math.isclose(o[i, 0, c], ref, rel_tol=1e-12, abs_tol=1e-13)
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(5)
+    d = 8
+    keys = rng.standard_normal((9, 1, d))
+    vals = rng.standard_normal((9, 1, d))
+    cache, bt = _cache_with(keys, vals)
+    # a token at position 0 sees only itself: o = v_0 exactly
+    o, _ = O.paged_attention(rng.standard_normal((1, 1, d)), [0], [0], cache, bt, 1)
+    assert np.array_equal(o[0, 0], vals[0, 0])
+    # q = 0: equal weights, o = mean of the visible values
+    o, _ = O.paged_attention(np.zeros((1, 1, d)), [0], [8], cache, bt, 1)
+    assert np.allclose(o[0, 0], vals[:9, 0].mean(axis=0), rtol=1e-13, atol=1e-14)
+    # identical value rows: o equals that row
+    same = np.repeat(vals[:1], 9, axis=0)
+    c2, bt2 = _cache_with(keys, same)
+    o, _ = O.paged_attention(rng.standard_normal((1, 1, d)) * 3, [0], [8], c2, bt2, 1)
+    assert np.allclose(o[0, 0], same[0, 0], rtol=1e-14, atol=1e-15)
+    # huge logits stay finite; a key ahead by > 800 in score takes all the weight
+    kq = np.zeros((9, 1, d)); kq[3, 0, 0] = 1.0
+    c3, bt3 = _cache_with(kq, vals)
+    qq = np.zeros((1, 1, d)); qq[0, 0, 0] = 5000.0
+    o, _ = O.paged_attention(qq, [0], [8], c3, bt3, 1)
+    assert np.array_equal(o[0, 0], vals[3, 0])
+
+
+def test_attention_gqa_equals_duplicated_kv_heads():
+    rng = np.random.default_rng(6)
+    d, L = 8, 11
+    keys = rng.standard_normal((L, 2, d))
+    vals = rng.standard_normal((L, 2, d))
+    c_g, bt = _cache_with(keys, vals)
+    c_f, bt_f = _cache_with(np.repeat(keys, 3, axis=1), np.repeat(vals, 3, axis=1))
+    q = rng.standard_normal((2, 6, d))
+    pos = np.array([10, 4])
+    o_g, _ = O.paged_attention(q, [0, 0], pos, c_g, bt, 2)      # g = 3
+    o_f, _ = O.paged_attention(q, [0, 0], pos, c_f, bt_f, 6)    # g = 1
+    assert np.array_equal(o_g, o_f)
+
+
+def test_attention_page_permutation_invariant():
+    rng = np.random.default_rng(7)
+    keys = rng.standard_normal((37, 2, 8))
+    vals = rng.standard_normal((37, 2, 8))
+    q = rng.standard_normal((5, 4, 8))
+    pos = np.array([36, 0, 15, 16, 20])
+    outs = []
+    for seed in range(3):
+        c, bt = _cache_with(keys, vals, n_pages=20, seed=seed)
+        outs.append(O.paged_attention(q, np.zeros(5, int), pos, c, bt, 2)[0])
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
+# ---------------------------------------------------------------- the layer
+
+def _tiny_float(seed=0, **kw):
+    wl = W.build_workload("t", W.Dims(64, 4, 2, 16, 96), [1], [0], [], seed, x_std=1.0, **kw)
+    return wl, O.weights_to_float(wl.weights)
+
+
+def _prompt_run(dims, w, x, chunks, storage, bt, num_pages):
+    """Run one prompt through the layer as consecutive chunks of the given sizes."""
+    cache = O.PagedCache(num_pages, dims.n_kv_heads, dims.page_size, dims.head_dim)
+    ys, pairs, start = [], 0, 0
+    for c in chunks:
+        r = O.layer_forward(dims, w, x[start:start + c], [c], [start], [], bt, cache, storage)
+        ys.append(r.y)
+        pairs += r.pairs
+        start += c
+    return np.concatenate(ys), cache, pairs
+
+
+@pytest.mark.parametrize("storage", ["bf16", "exact"])
+def test_chunked_prefill_equals_unchunked(storage):
+    """Running a prompt as N chunks equals one unchunked prefill ([notes] §3.1,
+    §7.5b): same outputs, same cache, same (query, key) work L(L+1)/2."""
+    dims = W.TINY
+    wl = W.tiny(0)
+    w = O.weights_to_float(wl.weights)
+    L = 256
+    rng = np.random.default_rng(8)
+    x = O.bf16_bits_to_float(W.f32_to_bf16_bits(rng.standard_normal((L, dims.hidden)).astype(np.float32)))
+    bt, num_pages = W.deal_block_tables(np.array([L]), dims.page_size, np.random.default_rng(9))
+    ref_y, ref_cache, ref_pairs = _prompt_run(dims, w, x, [L], storage, bt, num_pages)
+    assert ref_pairs == L * (L + 1) // 2
+    for chunks in ([64] * 4, [50, 78, 128], [1] * 5 + [251], [200, 56]):
+        y, cache, pairs = _prompt_run(dims, w, x, chunks, storage, bt, num_pages)
+        assert pairs == L * (L + 1) // 2
+        assert np.array_equal(y, ref_y), chunks
+        assert np.array_equal(cache.k, ref_cache.k, equal_nan=True)
+        assert np.array_equal(cache.v, ref_cache.v, equal_nan=True)
+
+
+def test_chunk_pair_count_closed_form():
+    """Chunk k of size C attends (k-1)C^2 + C(C+1)/2 pairs ([notes] §7.5b)."""
+    dims = W.Dims(32, 2, 1, 16, 32)
+    wl = W.build_workload("p", dims, [1], [0], [], 0)
+    w = O.weights_to_float(wl.weights)
+    C, K = 8, 5
+    x = np.random.default_rng(0).standard_normal((C * K, 32))
+    bt, npg = W.deal_block_tables(np.array([C * K]), 16, np.random.default_rng(1))
+    cache = O.PagedCache(npg, 1, 16, 16)
+    for k in range(1, K + 1):
+        r = O.layer_forward(dims, w, x[(k - 1) * C:k * C], [C], [(k - 1) * C], [], bt, cache)
+        assert r.pairs == (k - 1) * C * C + C * (C + 1) // 2
+
+
+def test_decode_equals_last_row_of_prefill():
+    dims = W.Dims(64, 4, 2, 16, 96)
+    wl = W.build_workload("d", dims, [1], [0], [], 0)
+    w = O.weights_to_float(wl.weights)
+    n = 21
+    x = np.random.default_rng(1).standard_normal((n, 64))
+    bt, npg = W.deal_block_tables(np.array([n]), 16, np.random.default_rng(2))
+    full, _, _ = _prompt_run(dims, w, x, [n], "bf16", bt, npg)
+    cache = O.PagedCache(npg, 2, 16, 16)
+    O.layer_forward(dims, w, x[:n - 1], [n - 1], [0], [], bt, cache)
+    r = O.layer_forward(dims, w, x[n - 1:], [], [], [n - 1], bt, cache)
+    assert np.array_equal(r.y[0], full[n - 1])
+
+
+def test_layer_linear_flops_are_2_T_psi():
+    """The batch's linear work is 2 * T * Psi with Psi the layer's projection
+    parameter count (every token passes every matrix once; [notes] §1.6,
+    [cp] hybrid-iteration roofline 2(c+b)Psi)."""
+    wl = W.small(0, n_q=4, n_kv=2, head_dim=16, hidden=64, ffn=96, chunk_len=(9,), chunk_prefix=(3,),
+                 decode_ctx=(5, 1))
+    w = O.weights_to_float(wl.weights)
+    psi = sum(wl.weights[k].size for k in ("w_q", "w_k", "w_v", "w_o", "w_g", "w_u", "w_d"))
+    cache = O.PagedCache(wl.batch.num_pages, 2, 16, 16)
+    for s, (k, v) in enumerate(zip(wl.prefix_k, wl.prefix_v)):
+        cache.load_prefix(wl.batch.block_table, s, O.bf16_bits_to_float(k), O.bf16_bits_to_float(v))
+    b = wl.batch
+    r = O.layer_forward(wl.dims, w, wl.x, b.chunk_len, b.chunk_prefix, b.decode_ctx, b.block_table, cache)
+    assert r.linear_flops == 2 * b.n_tokens * psi
+
+
+def test_layer_residual_paths():
+    wl, w = _tiny_float()
+    dims = wl.dims
+    x = wl.x.astype(np.float64)
+    for zero in (("w_o", "w_d"),):
+        w0 = dict(w)
+        for k in zero:
+            w0[k] = np.zeros_like(w[k])
+        cache = O.PagedCache(wl.batch.num_pages, 2, 16, 16)
+        r = O.layer_forward(dims, w0, x, [1], [0], [], wl.batch.block_table, cache)
+        assert np.array_equal(r.y, x)
+
+
+def test_layer_composition_transparent_weights():
+    """With W_q = W_k = 0 every visible key gets equal weight, so with identity
+    W_v, W_o and W_d = 0 the layer returns x + (running mean of rmsnorm(x) over
+    positions 0..p) -- checked with plain loops."""
+    dims = W.Dims(hidden=8, n_q_heads=2, n_kv_heads=2, head_dim=4, ffn_dim=8)
+    H = 8
+    w = {"w_q": np.zeros((8, 8)), "w_k": np.zeros((8, 8)), "w_v": np.eye(8), "w_o": np.eye(8),
+         "w_g": np.ones((8, 8)), "w_u": np.ones((8, 8)), "w_d": np.zeros((8, 8)),
+         "g_attn": np.linspace(0.5, 1.5, 8), "g_ffn": np.ones(8)}
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((7, H))
+    bt = np.array([[2, 0]])
+    cache = O.PagedCache(3, 2, 16, 4)
+    r = O.layer_forward(dims, w, x, [7], [0], [], bt, cache, storage="exact")
+    xn = []
+    for t in range(7):
+        ms = sum(v * v for v in x[t]) / H
+        xn.append([x[t][c] / math.sqrt(ms + dims.rms_eps) * w["g_attn"][c] for c in range(H)])
+    for t in range(7):
+        for c in range(H):
+            mean = sum(xn[j][c] for j in range(t + 1)) / (t + 1)
+            assert math.isclose(r.y[t][c], x[t][c] + mean, rel_tol=1e-12, abs_tol=1e-12)
+
+
+def test_layer_writes_only_its_slots():
+    wl = W.small(0, n_q=4, n_kv=2, head_dim=16, hidden=64, ffn=96, chunk_len=(9,), chunk_prefix=(3,),
+                 decode_ctx=(5, 0))
+    w = O.weights_to_float(wl.weights)
+    b = wl.batch
+    cache = O.PagedCache(b.num_pages, 2, 16, 16)
+    for s, (k, v) in enumerate(zip(wl.prefix_k, wl.prefix_v)):
+        cache.load_prefix(b.block_table, s, O.bf16_bits_to_float(k), O.bf16_bits_to_float(v))
+    before_k = cache.k.copy()
+    O.layer_forward(wl.dims, w, wl.x, b.chunk_len, b.chunk_prefix, b.decode_ctx, b.block_table, cache)
+    changed = ~((cache.k == before_k) | (np.isnan(cache.k) & np.isnan(before_k)))
+    # new positions: chunk 3..11, decode0 5, decode1 0 -> 9 + 1 + 1 token slots, each n_kv*d values
+    assert changed.sum() == 11 * 2 * 16
+    # every written value is on the bf16 grid and finite
+    assert np.all(np.isfinite(cache.k[changed]))
+    assert np.array_equal(O.round_bf16(cache.k[changed]), cache.k[changed])
+
+
+def test_layer_ffn_composition():
+    """With W_v = 0 the attention output is 0, so h1 = x; with W_g = I,
+    W_u = 2 I and W_d = I the layer returns x + silu(n) * 2 n, n = rmsnorm(x)
+    -- checked with plain loops (gate goes through silu, up does not)."""
+    H = 8
+    dims = W.Dims(hidden=H, n_q_heads=2, n_kv_heads=1, head_dim=4, ffn_dim=H)
+    rng = np.random.default_rng(12)
+    w = {"w_q": rng.standard_normal((8, 8)), "w_k": rng.standard_normal((4, 8)), "w_v": np.zeros((4, 8)),
+         "w_o": rng.standard_normal((8, 8)), "w_g": np.eye(H), "w_u": 2 * np.eye(H), "w_d": np.eye(H),
+         "g_attn": np.ones(H), "g_ffn": np.linspace(0.8, 1.2, H)}
+    x = rng.standard_normal((3, H))
+    cache = O.PagedCache(2, 1, 16, 4)
+    r = O.layer_forward(dims, w, x, [3], [0], [], np.array([[1]]), cache, storage="exact")
+    for t in range(3):
+        ms = sum(v * v for v in x[t]) / H
+        for c in range(H):
+            n = x[t][c] / math.sqrt(ms + dims.rms_eps) * w["g_ffn"][c]
+            ref = x[t][c] + n / (1 + math.exp(-n)) * 2 * n
+            assert math.isclose(r.y[t][c], ref, rel_tol=1e-12, abs_tol=1e-12)
+
+
+def test_bf16_storage_points():
+    wl = W.small(0, n_q=4, n_kv=2, head_dim=16, hidden=64, ffn=96, chunk_len=(9,), chunk_prefix=(0,),
+                 decode_ctx=())
+    w = O.weights_to_float(wl.weights)
+    b = wl.batch
+    cache = O.PagedCache(b.num_pages, 2, 16, 16)
+    r = O.layer_forward(wl.dims, w, wl.x, b.chunk_len, b.chunk_prefix, b.decode_ctx, b.block_table, cache,
+                        keep_attn=True)
+    assert np.array_equal(O.round_bf16(r.attn_out), r.attn_out)
+    assert np.array_equal(O.round_f32(r.y), r.y)
+    r2 = O.layer_forward(wl.dims, w, wl.x, b.chunk_len, b.chunk_prefix, b.decode_ctx, b.block_table,
+                         O.PagedCache(b.num_pages, 2, 16, 16), storage="exact", keep_attn=True)
+    assert not np.array_equal(O.round_bf16(r2.attn_out), r2.attn_out)
+    # the two precisions agree to bf16 accuracy
+    assert np.max(np.abs(r.y - r2.y)) < 0.05
