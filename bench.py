@@ -1,0 +1,275 @@
+#!/usr/bin/env python3
+"""Hybrid-batch decoder layer on one MI355X: tokens/s at tau = 512 on the
+Mistral-7B-shaped layer (one 480-token prefill chunk + 32 decodes), with the
+dominant kernel's roofline fraction and the CPU oracle timed beside it.
+
+One step = the whole hot path over one batch: hb_pack_metadata on the host
+into a pinned buffer, the asynchronous copy of the blob to the device, and
+hb_layer_forward (RMSNorm, QKV + RoPE + KV append, hybrid attention, O +
+residual, RMSNorm, gate/up + SwiGLU, down + residual).  Weights, KV cache and
+activations are resident in HBM before the timed region.  Four independent
+copies of weights and KV pools are used in turn so that the 256 MB
+Infinity Cache cannot serve a step from the previous step's data.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def workload_by_name(name):
+    from chunked_prefill_hybrid_layer_amd import workloads as W
+    if name == "mistral_tau512":
+        return W.mistral_tau512(0)
+    if name.startswith("tau_sweep_"):
+        return W.tau_sweep(int(name.rsplit("_", 1)[1]), 0)
+    if name == "yi_tau2048":
+        return W.yi_tau2048(0)
+    raise SystemExit(f"unknown workload {name}")
+
+
+def stage_model(wl):
+    """Algorithmic work of each stage for one launch: (flops, bytes, bound)."""
+    from chunked_prefill_hybrid_layer_amd import hb
+    d, b = wl.dims, wl.batch
+    T = b.n_tokens
+    H, nq, nkv, D, F = d.hidden, d.n_q_heads, d.n_kv_heads, d.head_dim, d.ffn_dim
+    cached = b.cached_lengths()
+    new = b.new_lengths()
+    # attention (query, key) pairs: chunk token at position p sees p+1 keys
+    chunk_pairs = 0
+    for c, n in zip(b.chunk_prefix, b.chunk_len):
+        chunk_pairs += int(n) * int(c) + int(n) * (int(n) + 1) // 2
+    dec_pairs = int(np.sum(b.decode_ctx.astype(np.int64) + 1))
+    kv_bytes_per_key = nkv * D * 2 * 2                      # K and V, bf16
+    chunk_kv_keys = int(np.sum(cached[:b.n_chunks] + new[:b.n_chunks]))
+    blob, _ = hb.pack_metadata(hb.make_dims(d), b.chunk_len, b.chunk_prefix, b.decode_ctx, b.block_table,
+                               b.num_pages, b.token_budget)
+    npart = hb.header(blob).n_partials
+    part_bytes = npart * nq * (D + 2) * 4
+    m = {
+        "rmsnorm_attn": (0, T * H * 4 + T * H * 2 + H * 2, "hbm"),
+        "qkv_rope_append": (2 * T * H * (nq + 2 * nkv) * D,
+                            (nq + 2 * nkv) * D * H * 2 + T * H * 2 + T * (nq + 2 * nkv) * D * 2, "mfma"),
+        "attn_chunk": (4 * chunk_pairs * nq * D, chunk_kv_keys * kv_bytes_per_key, "mfma"),
+        "attn_decode": (4 * dec_pairs * nq * D, dec_pairs * kv_bytes_per_key, "hbm"),
+        "attn_merge": (0, part_bytes + T * nq * D * 2, "hbm"),
+        "o_proj_residual": (2 * T * nq * D * H, nq * D * H * 2 + T * nq * D * 2 + 2 * T * H * 4, "mfma"),
+        "rmsnorm_ffn": (0, T * H * 4 + T * H * 2 + H * 2, "hbm"),
+        "gate_up_swiglu": (2 * T * H * 2 * F, 2 * F * H * 2 + T * H * 2 + T * F * 2, "mfma"),
+        "down_residual": (2 * T * F * H, F * H * 2 + T * F * 2 + 2 * T * H * 4, "mfma"),
+    }
+    return m
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "gate_up_swiglu": ["chunked_prefill_hybrid_layer_amd/csrc/gemm.hip"],
+    "qkv_rope_append": ["chunked_prefill_hybrid_layer_amd/csrc/gemm.hip"],
+    "o_proj_residual": ["chunked_prefill_hybrid_layer_amd/csrc/gemm.hip"],
+    "down_residual": ["chunked_prefill_hybrid_layer_amd/csrc/gemm.hip"],
+    "attn_chunk": ["chunked_prefill_hybrid_layer_amd/csrc/attention.hip"],
+    "attn_decode": ["chunked_prefill_hybrid_layer_amd/csrc/attention.hip"],
+    "attn_merge": ["chunked_prefill_hybrid_layer_amd/csrc/attention.hip"],
+    "rmsnorm_attn": ["chunked_prefill_hybrid_layer_amd/csrc/elementwise.hip"],
+    "rmsnorm_ffn": ["chunked_prefill_hybrid_layer_amd/csrc/elementwise.hip"],
+}
+
+
+def measured_traffic(stage, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    e = rec.get(workload, {}).get(stage)
+    if not e or e.get("source_hash") != source_hash(KERNEL_SOURCES[stage]):
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, stride=4):
+    """The oracle (float64 numpy) on every `stride`-th packed token of the same
+    batch; K/V of all tokens are computed since the cache needs them."""
+    from oracle import hybrid_layer as O
+    b = wl.batch
+    cache = O.PagedCache(b.num_pages, wl.dims.n_kv_heads, wl.dims.page_size, wl.dims.head_dim)
+    for s in range(b.n_seq):
+        if wl.prefix_k[s].shape[0]:
+            cache.load_prefix(b.block_table, s, O.bf16_bits_to_float(wl.prefix_k[s]),
+                              O.bf16_bits_to_float(wl.prefix_v[s]))
+    w = O.weights_to_float(wl.weights)
+    rows = np.arange(0, b.n_tokens, stride)
+    t0 = time.perf_counter()
+    O.layer_forward(wl.dims, w, wl.x.astype(np.float64), b.chunk_len, b.chunk_prefix, b.decode_ctx,
+                    b.block_table, cache, rows=rows)
+    dt = time.perf_counter() - t0
+    threads = int(os.environ.get("OPENBLAS_NUM_THREADS") or os.environ.get("OMP_NUM_THREADS") or
+                  len(os.sched_getaffinity(0)))
+    threads = min(threads, len(os.sched_getaffinity(0)))
+    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(rows)} of the {b.n_tokens} packed tokens (every {stride}th; K/V for all "
+                      f"{b.n_tokens}) of the same batch, float64 numpy oracle, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mistral_tau512")
+    ap.add_argument("--copies", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs the hybrid-batch layer on one GPU only; "
+                                   "--gpus above 1 is not supported (see the sharding note in DESIGN.md)"}))
+        sys.exit(2)
+
+    import torch
+    from chunked_prefill_hybrid_layer_amd import hb
+    from chunked_prefill_hybrid_layer_amd.runtime import DeviceLayer, stream_handle
+
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    wl = workload_by_name(args.workload)
+    d, b = wl.dims, wl.batch
+    T = b.n_tokens
+    max_pos = int(np.max(b.cached_lengths() + b.new_lengths())) + 1
+    layers = []
+    for _ in range(args.copies):
+        L = DeviceLayer(d, wl.weights, b.num_pages, max_pos)
+        L.fill_prefixes(b.block_table, range(b.n_seq), wl.prefix_k, wl.prefix_v)
+        layers.append(L)
+    hd = hb.make_dims(d)
+    x = torch.from_numpy(wl.x).cuda()
+    y = torch.empty_like(x)
+    # metadata: pinned host blobs and device blobs, double-buffered
+    size = hb.pack_metadata(hd, b.chunk_len, b.chunk_prefix, b.decode_ctx, b.block_table, b.num_pages,
+                            b.token_budget)[0].nbytes
+    pin = [torch.empty(size, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
+    pin_np = [p.numpy() for p in pin]
+    dev = [torch.empty(size, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    copied = [None, None]
+    ws = torch.empty(hb.workspace_bytes(hd, hb.pack_metadata(hd, b.chunk_len, b.chunk_prefix, b.decode_ctx,
+                                                               b.block_table, b.num_pages, b.token_budget)[0]),
+                     dtype=torch.uint8, device="cuda")
+    stream = stream_handle()
+
+    def step(i, events=None):
+        j = i & 1
+        if copied[j] is not None:
+            copied[j].synchronize()            # the copy that last read this pinned buffer is done
+        hb.pack_metadata(hd, b.chunk_len, b.chunk_prefix, b.decode_ctx, b.block_table, b.num_pages,
+                         b.token_budget, out=pin_np[j])
+        dev[j].copy_(pin[j], non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record()
+        copied[j] = ev
+        L = layers[i % len(layers)]
+        hb.layer_forward(hd, L.hw, pin_np[j], dev[j].data_ptr(), L.rope.data_ptr(), L.rope_max_pos,
+                         x.data_ptr(), y.data_ptr(), L.k_cache.data_ptr(), L.v_cache.data_ptr(),
+                         ws.data_ptr(), ws.numel(), stream, events)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    nst = hb.NUM_STAGES
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(args.steps)]
+    for row in evs:            # torch creates the hipEvent on first record
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+    assert all(e.cuda_event for row in evs for e in row)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(args.steps):
+        step(args.warmup + i, [e.cuda_event for e in evs[i]])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = t_start.elapsed_time(t_end) / args.steps
+    stage_ms = np.array([[evs[i][k].elapsed_time(evs[i][k + 1]) for k in range(nst)]
+                         for i in range(args.steps)])
+    stage_mean = stage_ms.mean(axis=0)
+
+    model = stage_model(wl)
+    stages = {}
+    t_roof = 0.0
+    for k, name in enumerate(hb.STAGE_NAMES):
+        fl, by, bound = model[name]
+        t = float(stage_mean[k]) * 1e-3
+        t_ideal = max(fl / (PEAK_BF16_TFLOPS * 1e12), by / (PEAK_HBM_GBS * 1e9))
+        t_roof += t_ideal
+        stages[name] = {"ms": round(float(stage_mean[k]), 5), "tflops": round(fl / t / 1e12, 2) if t > 0 else None,
+                        "gbs": round(by / t / 1e9, 1) if t > 0 else None, "bound": bound,
+                        "roofline_frac": round(t_ideal / t, 4) if t > 0 else None}
+    dom = max(hb.STAGE_NAMES, key=lambda n: stages[n]["ms"])
+    fl, by, bound = model[dom]
+    tdom = stages[dom]["ms"] * 1e-3
+    if bound == "mfma":
+        roof = {"bound": "mfma", "achieved": round(fl / tdom / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(by / tdom / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = measured_traffic(dom, args.workload)
+    roof["kernel"] = dom
+    roof["per_launch"] = {"flops": fl, "bytes": by}
+
+    out = {
+        "metric": "hybrid-layer tokens/s at tau=512 (Mistral-7B-shaped layer) + % of MFMA/HBM roofline",
+        "value": round(T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "hidden": d.hidden, "n_q_heads": d.n_q_heads,
+                   "n_kv_heads": d.n_kv_heads, "head_dim": d.head_dim, "ffn_dim": d.ffn_dim,
+                   "tokens": T, "chunks": [int(c) for c in b.chunk_len],
+                   "chunk_prefix": [int(c) for c in b.chunk_prefix], "decodes": b.n_decodes,
+                   "decode_ctx_mean": float(np.mean(b.decode_ctx)) if b.n_decodes else 0.0,
+                   "token_budget": b.token_budget, "page_size": d.page_size, "copies_rotated": args.copies},
+        "layer_iters_per_s": round(1e3 / ms, 1),
+        "layer_roofline_frac": round(t_roof / (ms * 1e-3), 4),
+        "wall_s_timed": round(wall, 3),
+        "roofline": roof,
+        "stages": stages,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,121 @@
+// Internal definitions shared by the host code and the HIP kernels of the
+// hybrid-batch layer library.  Not part of the public ABI (see include/hb.h).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "../../include/hb.h"
+
+namespace hb {
+
+// --- attention tiling (fixed by the kernels; recorded in the metadata) -----
+constexpr int kChunkRows = 128;       // (token, head) rows per chunk attention tile
+constexpr int kChunkKeyTile = 64;     // keys staged per step (4 pages of 16)
+constexpr int kChunkKvSplit = 1024;   // keys per chunk attention item (multiple of 64)
+constexpr int kDecodeKeyStep = 32;    // keys per decode step (2 pages)
+constexpr int kDecodeKvSplit = 256;   // keys per decode attention item (multiple of 32)
+constexpr int kPageSize = 16;
+constexpr int kMaxGroup = 16;         // decode path holds a kv group in one 16-row MFMA tile
+
+// --- GEMM tiling -------------------------------------------------------------
+constexpr int kGemmBM = 128;
+constexpr int kGemmBN = 128;
+constexpr int kGemmBK = 64;
+
+inline int chunk_q_tile(int group) { return group >= kChunkRows ? 1 : kChunkRows / group; }
+
+// Thread-local error detail.
+void set_error(const std::string& msg);
+hb_status fail(hb_status s, const std::string& msg);
+
+// Validates dims against what the kernels support.
+hb_status check_dims(const hb_dims* d);
+
+// Byte layout of the device workspace for one batch.
+struct WsLayout {
+  size_t xn, q, o, h1, h1n, act, part_o, part_ml, total;
+};
+WsLayout ws_layout(const hb_dims& d, int n_tokens, int n_partials);
+
+// Validates a metadata blob against dims (magic, version, dims it was built for).
+hb_status check_meta(const hb_dims* d, const void* meta_host);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace hb
+
+// Device-side launch helpers (defined in the .hip files).
+namespace hb {
+
+struct DevMeta {            // device pointers into the copied metadata blob
+  const int32_t* q_start;
+  const int32_t* cached;
+  const int32_t* kv_len;
+  const int32_t* tok_seq;
+  const int32_t* tok_pos;
+  const int32_t* slot;
+  const int32_t* part_off;
+  const int32_t* part_cnt;
+  const int32_t* block_table;
+  const hb_attn_item* chunk_items;
+  const hb_attn_item* decode_items;
+};
+DevMeta dev_meta(const hb_meta_header* h, const void* meta_dev);
+
+typedef struct ihipStream_t* stream_t;
+
+hb_status launch_rmsnorm(const float* x, const uint16_t* gain, uint16_t* out, int rows, int hidden,
+                         float eps, stream_t s);
+hb_status launch_kv_append(const hb_dims& d, const DevMeta& m, int n_tokens, const uint16_t* k,
+                           const uint16_t* v, int64_t row_stride, uint16_t* kc, uint16_t* vc,
+                           stream_t s);
+
+enum GemmMode { kGemmQkvRope = 0, kGemmResidual = 1, kGemmSwiglu = 2 };
+
+struct GemmArgs {
+  int mode;
+  const uint16_t* a;  // [M][K] bf16
+  int lda;
+  int M, N, K;
+  // weights: QKV concatenates w0 (n0 rows), w1 (n1 rows), w2; SwiGLU pairs w0 (gate) and w1 (up);
+  // the residual mode uses w0 only.
+  const uint16_t* w0;
+  const uint16_t* w1;
+  const uint16_t* w2;
+  int n0, n1;
+  // residual: out_f = res + acc
+  const float* res;
+  float* out_f;
+  int ldo;
+  // SwiGLU / QKV bf16 output
+  uint16_t* out_b;
+  // QKV epilogue
+  const float* rope;
+  const int32_t* tok_pos;
+  const int32_t* slot;
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+  int n_q_heads, n_kv_heads, head_dim;
+};
+hb_status launch_gemm(const GemmArgs& g, stream_t s);
+
+struct AttnArgs {
+  const uint16_t* q;       // [T][n_q * d]
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  DevMeta meta;
+  int max_pages;
+  int n_q_heads, n_kv_heads, head_dim, group;
+  int n_chunk_items, n_decode_items, n_tokens;
+  float* part_o;           // [n_partials][n_q][d]
+  float* part_ml;          // [n_partials][n_q][2]
+  uint16_t* out;           // [T][n_q * d]
+};
+// Attention in three launches (chunk items, decode items, merge); ev, if not
+// NULL, holds the events to record before each launch (3 entries).
+hb_status launch_attention(const AttnArgs& a, stream_t s, void* const* ev);
+
+}  // namespace hb

@@ -1,0 +1,198 @@
+// Device entry points of the hybrid-batch layer library: hb_kv_append and
+// hb_layer_forward.  Validation happens here, on the host, before anything is
+// enqueued; the kernels assume validated metadata.
+//
+// hb_layer_forward is the one-layer slice of the serving iteration
+// run_iteration(B) of the "Sarathi-Serve reading notes" (§3.4): the hybrid
+// batch B (decodes plus chunk pieces under tau, §3.2) passes once through
+//   RMSNorm -> QKV projection (+RoPE, +KV append) -> paged hybrid attention ->
+//   O projection (+residual) -> RMSNorm -> gate/up projection (+SwiGLU) ->
+//   down projection (+residual).
+
+#include "device_common.h"
+
+namespace hb {
+
+DevMeta dev_meta(const hb_meta_header* h, const void* meta_dev) {
+  const char* b = (const char*)meta_dev;
+  DevMeta m;
+  m.q_start = (const int32_t*)(b + h->off_q_start);
+  m.cached = (const int32_t*)(b + h->off_cached);
+  m.kv_len = (const int32_t*)(b + h->off_kv_len);
+  m.tok_seq = (const int32_t*)(b + h->off_tok_seq);
+  m.tok_pos = (const int32_t*)(b + h->off_tok_pos);
+  m.slot = (const int32_t*)(b + h->off_slot);
+  m.part_off = (const int32_t*)(b + h->off_part_off);
+  m.part_cnt = (const int32_t*)(b + h->off_part_cnt);
+  m.block_table = (const int32_t*)(b + h->off_block_table);
+  m.chunk_items = (const hb_attn_item*)(b + h->off_chunk_items);
+  m.decode_items = (const hb_attn_item*)(b + h->off_decode_items);
+  return m;
+}
+
+}  // namespace hb
+
+using namespace hb;
+
+#define HB_TRY(expr)                 \
+  do {                               \
+    hb_status _st = (expr);          \
+    if (_st != HB_OK) return _st;    \
+  } while (0)
+
+extern "C" hb_status hb_kv_append(const hb_dims* dims, const void* meta_host, const void* meta_dev,
+                                  const uint16_t* k, const uint16_t* v, int64_t row_stride, uint16_t* k_cache,
+                                  uint16_t* v_cache, void* stream) {
+  HB_TRY(check_dims(dims));
+  HB_TRY(check_meta(dims, meta_host));
+  if (!meta_dev || !k || !v || !k_cache || !v_cache) return fail(HB_E_NULL, "kv_append: NULL pointer");
+  if (row_stride < (int64_t)dims->n_kv_heads * dims->head_dim || row_stride % 8)
+    return fail(HB_E_SHAPE, "kv_append: row_stride must be >= n_kv*head_dim and a multiple of 8");
+  if (((uintptr_t)k | (uintptr_t)v | (uintptr_t)k_cache | (uintptr_t)v_cache) & 15)
+    return fail(HB_E_SHAPE, "kv_append: buffers must be 16-byte aligned");
+  const hb_meta_header* h = (const hb_meta_header*)meta_host;
+  return launch_kv_append(*dims, dev_meta(h, meta_dev), h->n_tokens, k, v, row_stride, k_cache, v_cache,
+                          (stream_t)stream);
+}
+
+extern "C" hb_status hb_layer_forward(const hb_dims* dims, const hb_weights* w, const void* meta_host,
+                                      const void* meta_dev, const float* rope_cs, int32_t rope_max_pos,
+                                      const float* x, float* y, uint16_t* k_cache, uint16_t* v_cache,
+                                      void* workspace, size_t workspace_bytes, void* stream,
+                                      void* const* stage_events) {
+  HB_TRY(check_dims(dims));
+  HB_TRY(check_meta(dims, meta_host));
+  if (!w || !meta_dev || !rope_cs || !x || !y || !k_cache || !v_cache || !workspace)
+    return fail(HB_E_NULL, "layer_forward: NULL pointer");
+  if (!w->w_q || !w->w_k || !w->w_v || !w->w_o || !w->w_g || !w->w_u || !w->w_d || !w->g_attn || !w->g_ffn)
+    return fail(HB_E_NULL, "layer_forward: NULL weight");
+  if ((const void*)x == (const void*)y) return fail(HB_E_SHAPE, "layer_forward: x and y alias");
+  const hb_meta_header* h = (const hb_meta_header*)meta_host;
+  if (h->max_kv_len > rope_max_pos)
+    return fail(HB_E_CAPACITY, "rope table holds " + std::to_string(rope_max_pos) + " positions, batch reaches " +
+                                   std::to_string(h->max_kv_len));
+  const int T = h->n_tokens;
+  const WsLayout L = ws_layout(*dims, T, h->n_partials);
+  if (workspace_bytes < L.total)
+    return fail(HB_E_CAPACITY, "workspace needs " + std::to_string(L.total) + " bytes");
+  const uintptr_t al = (uintptr_t)workspace | (uintptr_t)x | (uintptr_t)y | (uintptr_t)k_cache |
+                       (uintptr_t)v_cache | (uintptr_t)rope_cs | (uintptr_t)w->w_q | (uintptr_t)w->w_k |
+                       (uintptr_t)w->w_v | (uintptr_t)w->w_o | (uintptr_t)w->w_g | (uintptr_t)w->w_u |
+                       (uintptr_t)w->w_d | (uintptr_t)w->g_attn | (uintptr_t)w->g_ffn;
+  if (al & 15) return fail(HB_E_SHAPE, "layer_forward: device buffers must be 16-byte aligned");
+
+  const stream_t s = (stream_t)stream;
+  // optional per-stage timing events (see HB_STAGE_NAMES)
+  auto mark = [&](int i) {
+    if (stage_events) hipEventRecord((hipEvent_t)stage_events[i], (hipStream_t)stream);
+  };
+  const DevMeta m = dev_meta(h, meta_dev);
+  char* ws = (char*)workspace;
+  uint16_t* xn = (uint16_t*)(ws + L.xn);
+  uint16_t* qb = (uint16_t*)(ws + L.q);
+  uint16_t* ob = (uint16_t*)(ws + L.o);
+  float* h1 = (float*)(ws + L.h1);
+  uint16_t* h1n = (uint16_t*)(ws + L.h1n);
+  uint16_t* act = (uint16_t*)(ws + L.act);
+  const int H = dims->hidden, d = dims->head_dim, nq = dims->n_q_heads, nkv = dims->n_kv_heads;
+  const int F = dims->ffn_dim;
+
+  // a1: RMSNorm of the input
+  mark(0);
+  HB_TRY(launch_rmsnorm(x, w->g_attn, xn, T, H, dims->rms_eps, s));
+
+  // a2-a4: QKV projection, RoPE, KV append
+  GemmArgs g{};
+  g.mode = kGemmQkvRope;
+  g.a = xn;
+  g.lda = H;
+  g.M = T;
+  g.N = (nq + 2 * nkv) * d;
+  g.K = H;
+  g.w0 = w->w_q;
+  g.w1 = w->w_k;
+  g.w2 = w->w_v;
+  g.n0 = nq * d;
+  g.n1 = nkv * d;
+  g.out_b = qb;
+  g.rope = rope_cs;
+  g.tok_pos = m.tok_pos;
+  g.slot = m.slot;
+  g.k_cache = k_cache;
+  g.v_cache = v_cache;
+  g.n_q_heads = nq;
+  g.n_kv_heads = nkv;
+  g.head_dim = d;
+  mark(1);
+  HB_TRY(launch_gemm(g, s));
+
+  // a5: hybrid attention over the paged cache
+  AttnArgs at{};
+  at.q = qb;
+  at.k_cache = k_cache;
+  at.v_cache = v_cache;
+  at.meta = m;
+  at.max_pages = h->max_pages;
+  at.n_q_heads = nq;
+  at.n_kv_heads = nkv;
+  at.head_dim = d;
+  at.group = nq / nkv;
+  at.n_chunk_items = h->n_chunk_items;
+  at.n_decode_items = h->n_decode_items;
+  at.n_tokens = T;
+  at.part_o = (float*)(ws + L.part_o);
+  at.part_ml = (float*)(ws + L.part_ml);
+  at.out = ob;
+  HB_TRY(launch_attention(at, s, stage_events ? stage_events + 2 : nullptr));
+
+  // a6: O projection + residual
+  GemmArgs go{};
+  go.mode = kGemmResidual;
+  go.a = ob;
+  go.lda = nq * d;
+  go.M = T;
+  go.N = H;
+  go.K = nq * d;
+  go.w0 = w->w_o;
+  go.res = x;
+  go.out_f = h1;
+  go.ldo = H;
+  mark(5);
+  HB_TRY(launch_gemm(go, s));
+
+  // a7: RMSNorm
+  mark(6);
+  HB_TRY(launch_rmsnorm(h1, w->g_ffn, h1n, T, H, dims->rms_eps, s));
+
+  // a8: gate/up projection + SwiGLU
+  GemmArgs gu{};
+  gu.mode = kGemmSwiglu;
+  gu.a = h1n;
+  gu.lda = H;
+  gu.M = T;
+  gu.N = 2 * F;
+  gu.K = H;
+  gu.w0 = w->w_g;
+  gu.w1 = w->w_u;
+  gu.out_b = act;
+  gu.ldo = F;
+  mark(7);
+  HB_TRY(launch_gemm(gu, s));
+
+  // a9: down projection + residual
+  GemmArgs gd{};
+  gd.mode = kGemmResidual;
+  gd.a = act;
+  gd.lda = F;
+  gd.M = T;
+  gd.N = H;
+  gd.K = F;
+  gd.w0 = w->w_d;
+  gd.res = h1;
+  gd.out_f = y;
+  gd.ldo = H;
+  mark(8);
+  HB_TRY(launch_gemm(gd, s));
+  mark(9);
+  return HB_OK;
+}

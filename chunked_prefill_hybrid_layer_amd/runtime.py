@@ -1,0 +1,107 @@
+"""Device-side state for driving the library from Python.
+
+torch provides device memory, host-to-device copies and the stream; every
+computation is one of the library's entry points (hb.py).  This module holds
+weights, the paged KV cache, the rotary table and the workspace for one layer.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import hb
+
+BF16_NAN = 0x7FC0
+WEIGHT_NAMES = ("w_q", "w_k", "w_v", "w_o", "w_g", "w_u", "w_d", "g_attn", "g_ffn")
+
+
+def to_device_u16(a: np.ndarray, device) -> torch.Tensor:
+    """uint16 bit patterns -> int16 device tensor with the same bits."""
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).to(device)
+
+
+def stream_handle() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+@dataclass
+class Prepared:
+    """A hybrid batch's metadata on host and device."""
+    blob: np.ndarray
+    meta_dev: torch.Tensor
+    n_tokens: int
+
+    @property
+    def header(self):
+        return hb.header(self.blob)
+
+
+class DeviceLayer:
+    """Weights, paged KV cache (NaN-filled: unwritten slots are poison), rotary
+    table and workspace of one decoder layer on one GPU."""
+
+    def __init__(self, dims, weights: dict, num_pages: int, rope_max_pos: int, device: str = "cuda"):
+        self.dims = dims
+        self.hd = hb.make_dims(dims)
+        self.device = device
+        self.w = {n: to_device_u16(weights[n], device) for n in WEIGHT_NAMES}
+        self.hw = hb.Weights(*[self.w[n].data_ptr() for n in WEIGHT_NAMES])
+        self.num_pages = int(num_pages)
+        self.k_cache = torch.full((self.num_pages, dims.n_kv_heads, dims.page_size, dims.head_dim), BF16_NAN,
+                                  dtype=torch.int16, device=device)
+        self.v_cache = torch.full((self.num_pages, dims.n_kv_heads, dims.head_dim, dims.page_size), BF16_NAN,
+                                  dtype=torch.int16, device=device)
+        self.rope_max_pos = int(rope_max_pos)
+        self.rope = torch.from_numpy(hb.rope_table(self.hd, self.rope_max_pos)).to(device)
+        self.ws: Optional[torch.Tensor] = None
+
+    # -- metadata ---------------------------------------------------------
+    def prepare(self, chunk_len, chunk_prefix, decode_ctx, block_table, token_budget=None) -> Prepared:
+        T = int(np.sum(chunk_len)) + len(decode_ctx)
+        blob, n = hb.pack_metadata(self.hd, chunk_len, chunk_prefix, decode_ctx, block_table, self.num_pages,
+                                   T if token_budget is None else token_budget)
+        meta_dev = torch.from_numpy(blob).to(self.device)
+        return Prepared(blob, meta_dev, n)
+
+    def _workspace(self, prep: Prepared) -> torch.Tensor:
+        need = hb.workspace_bytes(self.hd, prep.blob)
+        if self.ws is None or self.ws.numel() < need:
+            self.ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        return self.ws
+
+    # -- entry points -----------------------------------------------------
+    def append(self, prep: Prepared, k: torch.Tensor, v: torch.Tensor):
+        """hb_kv_append of k, v [T][n_kv][d] (int16 bf16 bits) at the batch's slots."""
+        row_stride = k.stride(0)
+        hb.kv_append(self.hd, prep.blob, prep.meta_dev.data_ptr(), k.data_ptr(), v.data_ptr(), row_stride,
+                     self.k_cache.data_ptr(), self.v_cache.data_ptr(), stream_handle())
+
+    def forward(self, prep: Prepared, x: torch.Tensor, y: torch.Tensor, stage_events=None):
+        ws = self._workspace(prep)
+        hb.layer_forward(self.hd, self.hw, prep.blob, prep.meta_dev.data_ptr(), self.rope.data_ptr(),
+                         self.rope_max_pos, x.data_ptr(), y.data_ptr(), self.k_cache.data_ptr(),
+                         self.v_cache.data_ptr(), ws.data_ptr(), ws.numel(), stream_handle(), stage_events)
+
+    def fill_prefixes(self, block_table: np.ndarray, seqs: Sequence[int], prefix_k, prefix_v):
+        """Write already-cached K/V (positions 0..len-1) of the given sequences
+        through hb_kv_append, as one batch of prefix-0 chunks."""
+        rows = [s for s in seqs if s < len(prefix_k) and prefix_k[s].shape[0] > 0]
+        if not rows:
+            return
+        lens = [int(prefix_k[s].shape[0]) for s in rows]
+        bt = np.ascontiguousarray(block_table[rows])
+        prep = self.prepare(lens, [0] * len(rows), [], bt)
+        k = to_device_u16(np.concatenate([prefix_k[s] for s in rows]), self.device)
+        v = to_device_u16(np.concatenate([prefix_v[s] for s in rows]), self.device)
+        self.append(prep, k, v)
+        torch.cuda.synchronize()
+
+    # -- views for checking ---------------------------------------------------
+    def cache_logical(self):
+        """(K, V) as uint16 numpy arrays in logical order [page][kv][slot][d]."""
+        k = self.k_cache.cpu().numpy().view(np.uint16)
+        v = self.v_cache.cpu().numpy().view(np.uint16).transpose(0, 1, 3, 2)
+        return k, np.ascontiguousarray(v)

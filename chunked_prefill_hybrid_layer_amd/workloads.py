@@ -25,6 +25,7 @@ Value recipe (the pages give none; these are readings):
 from __future__ import annotations
 
 from dataclasses import dataclass, field
+import os
 from typing import Dict, List, Optional
 
 import numpy as np
@@ -35,13 +36,52 @@ PAGE_SIZE = 16
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bf16 (ties to even); returns uint16 bits."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    u = a.view(np.uint32)
+    r = ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
     nan = np.isnan(a)
     if nan.any():
         r[nan] = 0x7FC0
     return r
+
+
+_BLOCK = 1 << 22            # elements per independently seeded block
+_POOL = None
+
+
+def _pool():
+    global _POOL
+    if _POOL is None:
+        import concurrent.futures as cf
+        _POOL = cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1))
+    return _POOL
+
+
+def normal_bf16(seed: np.random.SeedSequence, shape, std: float = 1.0, mean: float = 0.0,
+                parallel: bool = True) -> np.ndarray:
+    """mean + std * N(0, 1), rounded to bf16 bits.  The flat array is cut into
+    fixed blocks, each drawn from its own child of ``seed``, so the values do
+    not depend on how many threads draw them."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16)
+    nblk = (n + _BLOCK - 1) // _BLOCK
+    kids = seed.spawn(nblk)
+
+    def work(i):
+        lo, hi = i * _BLOCK, min(n, (i + 1) * _BLOCK)
+        g = np.random.Generator(np.random.PCG64(kids[i]))
+        v = g.standard_normal(hi - lo, dtype=np.float32)
+        if std != 1.0:
+            v *= np.float32(std)
+        if mean != 0.0:
+            v += np.float32(mean)
+        out[lo:hi] = f32_to_bf16_bits(v)
+
+    if parallel and nblk > 1:
+        list(_pool().map(work, range(nblk)))
+    else:
+        for i in range(nblk):
+            work(i)
+    return out.reshape(shape)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
@@ -141,11 +181,13 @@ def make_weights(dims: Dims, rng: np.random.Generator, std: float = 0.02) -> Dic
         "w_u": (F, H),
         "w_d": (H, F),
     }
+    root = np.random.SeedSequence(int(rng.integers(2**63)))
+    kids = root.spawn(len(shapes) + 2)
     w = {}
-    for name, shp in shapes.items():
-        w[name] = f32_to_bf16_bits(rng.standard_normal(shp, dtype=np.float32) * np.float32(std))
-    for name in ("g_attn", "g_ffn"):
-        w[name] = f32_to_bf16_bits(1.0 + 0.02 * rng.standard_normal(H, dtype=np.float32))
+    for kid, (name, shp) in zip(kids, shapes.items()):
+        w[name] = normal_bf16(kid, shp, std)
+    w["g_attn"] = normal_bf16(kids[-2], (H,), 0.02, 1.0)
+    w["g_ffn"] = normal_bf16(kids[-1], (H,), 0.02, 1.0)
     return w
 
 
@@ -171,11 +213,10 @@ def deal_block_tables(kv_lens: np.ndarray, page_size: int, rng: np.random.Genera
     return bt, num_pages
 
 
-def synth_prefix(length: int, dims: Dims, rng: np.random.Generator, std: float = 1.0):
+def synth_prefix(length: int, dims: Dims, seed: np.random.SeedSequence, std: float = 1.0):
     shp = (int(length), dims.n_kv_heads, dims.head_dim)
-    k = f32_to_bf16_bits(rng.standard_normal(shp, dtype=np.float32) * np.float32(std))
-    v = f32_to_bf16_bits(rng.standard_normal(shp, dtype=np.float32) * np.float32(std))
-    return k, v
+    ks, vs = seed.spawn(2)
+    return normal_bf16(ks, shp, std, parallel=False), normal_bf16(vs, shp, std, parallel=False)
 
 
 def build_workload(name: str, dims: Dims, chunk_len, chunk_prefix, decode_ctx, seed: int,
@@ -198,11 +239,10 @@ def build_workload(name: str, dims: Dims, chunk_len, chunk_prefix, decode_ctx, s
     if synth_prefixes:
         # one child stream per sequence, so any subset can be regenerated alone
         children = np.random.SeedSequence(int(rc.integers(2**63))).spawn(len(cached))
-        for s, c in enumerate(cached):
-            g = np.random.Generator(np.random.PCG64(children[s]))
-            k, v = synth_prefix(int(c), dims, g, cache_std)
-            wl.prefix_k.append(k)
-            wl.prefix_v.append(v)
+        kv = list(_pool().map(lambda s: synth_prefix(int(cached[s]), dims, children[s], cache_std),
+                              range(len(cached))))
+        wl.prefix_k = [k for k, _ in kv]
+        wl.prefix_v = [v for _, v in kv]
     return wl
 
 

@@ -149,35 +149,62 @@ def hybrid_batch_budget(n_decodes: int, chunk_takes: Sequence[int], tau: int):
 
 
 class PagedCache:
-    """K and V pages in logical order [page][kv_head][slot][d], float64."""
+    """K and V pages in logical order [kv_head][slot][d], float64.
 
-    def __init__(self, num_pages: int, n_kv: int, page_size: int, head_dim: int,
-                 fill: float = np.nan):
-        shp = (num_pages, n_kv, page_size, head_dim)
-        self.k = np.full(shp, fill, dtype=np.float64)
-        self.v = np.full(shp, fill, dtype=np.float64)
+    Pages are held sparsely: a page comes into being, filled with NaN, the
+    first time something is written to it, so a cache over a large pool costs
+    only the pages actually used.  Reading a slot nobody wrote returns NaN."""
+
+    def __init__(self, num_pages: int, n_kv: int, page_size: int, head_dim: int):
+        self.num_pages = num_pages
+        self.n_kv = n_kv
         self.page_size = page_size
+        self.head_dim = head_dim
+        self.pages: Dict[int, np.ndarray] = {}   # page -> [2 (K, V)][n_kv][slot][d]
+
+    def _page(self, page: int) -> np.ndarray:
+        if not 0 <= page < self.num_pages:
+            raise IndexError(f"page {page} outside the pool of {self.num_pages}")
+        pg = self.pages.get(page)
+        if pg is None:
+            pg = np.full((2, self.n_kv, self.page_size, self.head_dim), np.nan)
+            self.pages[page] = pg
+        return pg
 
     def write(self, block_table, seq: int, pos: int, k_row: np.ndarray, v_row: np.ndarray):
         page, slot = page_of(block_table, seq, pos, self.page_size)
-        self.k[page, :, slot, :] = k_row
-        self.v[page, :, slot, :] = v_row
-
-    def gather(self, block_table, seq: int, length: int):
-        """Keys/values of positions 0..length-1 of ``seq``: [length][n_kv][d]."""
-        pos = np.arange(length)
-        pages = np.asarray(block_table[seq])[pos // self.page_size]
-        slots = pos % self.page_size
-        return self.k[pages, :, slots, :], self.v[pages, :, slots, :]
+        pg = self._page(page)
+        pg[0, :, slot, :] = k_row
+        pg[1, :, slot, :] = v_row
 
     def load_prefix(self, block_table, seq: int, k_rows: np.ndarray, v_rows: np.ndarray):
         """Place already-cached K/V (positions 0..len-1) of ``seq``."""
-        n = k_rows.shape[0]
-        pos = np.arange(n)
-        pages = np.asarray(block_table[seq])[pos // self.page_size]
-        slots = pos % self.page_size
-        self.k[pages, :, slots, :] = k_rows
-        self.v[pages, :, slots, :] = v_rows
+        for pos in range(k_rows.shape[0]):
+            self.write(block_table, seq, pos, k_rows[pos], v_rows[pos])
+
+    def gather(self, block_table, seq: int, length: int):
+        """Keys/values of positions 0..length-1 of ``seq``: [length][n_kv][d]."""
+        ks = np.empty((length, self.n_kv, self.head_dim))
+        vs = np.empty_like(ks)
+        for pos in range(length):
+            page, slot = page_of(block_table, seq, pos, self.page_size)
+            pg = self.pages.get(page)
+            if pg is None:
+                ks[pos] = vs[pos] = np.nan
+            else:
+                ks[pos] = pg[0, :, slot, :]
+                vs[pos] = pg[1, :, slot, :]
+        return ks, vs
+
+    def dense(self):
+        """Whole pool as (K, V), each [num_pages][n_kv][slot][d]; NaN where unwritten."""
+        shp = (self.num_pages, self.n_kv, self.page_size, self.head_dim)
+        k = np.full(shp, np.nan)
+        v = np.full(shp, np.nan)
+        for page, pg in self.pages.items():
+            k[page] = pg[0]
+            v[page] = pg[1]
+        return k, v
 
 
 # ----------------------------------------------------------------------------

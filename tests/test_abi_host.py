@@ -1,0 +1,169 @@
+"""Host side of the C ABI (no GPU needed): the library loads and exports every
+declared entry point; hb_pack_metadata agrees bit for bit with the oracle's
+own token layout and page slots, rejects every invalid batch, and builds
+attention work lists that partition each token's keys."""
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import hybrid_layer as O
+from chunked_prefill_hybrid_layer_amd import workloads as W
+from chunked_prefill_hybrid_layer_amd import hb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_library_exports_every_declared_symbol():
+    text = open(os.path.join(ROOT, "include", "hb.h")).read()
+    declared = sorted(set(re.findall(r"\b(hb_[a-z_]+)\s*\(", text)))
+    assert declared == sorted(hb.EXPORTS)
+    for name in declared:
+        assert hasattr(hb.lib, name), name
+
+
+def _pack(dims, cl, cp, dc, bt, num_pages, tau=None):
+    tau = int(np.sum(cl)) + len(dc) if tau is None else tau
+    return hb.pack_metadata(hb.make_dims(dims), cl, cp, dc, bt, num_pages, tau)
+
+
+def _random_batch(rng, n_chunks, n_dec, max_len=300):
+    cl = rng.integers(1, max_len, n_chunks)
+    cp = rng.integers(0, max_len * 3, n_chunks)
+    dc = rng.integers(0, max_len * 4, n_dec)
+    kv = np.concatenate([cp + cl, dc + 1])
+    bt, npg = W.deal_block_tables(kv, 16, rng, max_pages=int(((kv + 15) // 16).max()) + 3)
+    return cl, cp, dc, bt, npg
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_pack_matches_oracle_layout_and_slots(seed):
+    rng = np.random.default_rng(100 + seed)
+    dims = [W.MISTRAL, W.YI, W.TINY][seed % 3]
+    cl, cp, dc, bt, npg = _random_batch(rng, int(rng.integers(0, 4)), int(rng.integers(1, 40)))
+    blob, T = _pack(dims, cl, cp, dc, bt, npg)
+    lay = O.token_layout(cl, cp, dc)
+    assert T == len(lay.seq)
+    h = hb.header(blob)
+    assert h.magic == hb.META_MAGIC and h.n_tokens == T and h.n_seq == len(cl) + len(dc)
+    assert np.array_equal(hb.meta_array(blob, "q_start"), lay.q_start)
+    assert np.array_equal(hb.meta_array(blob, "cached"), lay.cached)
+    assert np.array_equal(hb.meta_array(blob, "kv_len"), lay.kv_len)
+    assert np.array_equal(hb.meta_array(blob, "tok_seq"), lay.seq)
+    assert np.array_equal(hb.meta_array(blob, "tok_pos"), lay.pos)
+    slots = [O.page_of(bt, int(s), int(p), 16) for s, p in zip(lay.seq, lay.pos)]
+    assert np.array_equal(hb.meta_array(blob, "slot"), [pg * 16 + sl for pg, sl in slots])
+    assert np.array_equal(hb.meta_array(blob, "block_table").reshape(bt.shape), bt)
+    assert h.max_kv_len == int(lay.kv_len.max())
+    assert hb.meta_bytes(hb.make_dims(dims), h.n_seq, T, bt.shape[1]) >= h.bytes
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_attention_work_lists_partition_keys(seed):
+    """Every token's attention items cover keys [0, pos+1) of its sequence
+    exactly once, in split order, and its partial slots are contiguous."""
+    rng = np.random.default_rng(200 + seed)
+    dims = [W.MISTRAL, W.YI, W.TINY][seed % 3]
+    cl, cp, dc, bt, npg = _random_batch(rng, int(rng.integers(1, 4)), int(rng.integers(0, 30)), max_len=2500)
+    blob, T = _pack(dims, cl, cp, dc, bt, npg)
+    lay = O.token_layout(cl, cp, dc)
+    h = hb.header(blob)
+    pos = hb.meta_array(blob, "tok_pos")
+    poff = hb.meta_array(blob, "part_off")
+    pcnt = hb.meta_array(blob, "part_cnt")
+    covered = {t: [] for t in range(T)}
+    for kind in ("chunk", "decode"):
+        for seq, tok0, n_tok, k0, k1, split, _, _ in hb.attn_items(blob, kind):
+            assert k0 < k1 and n_tok >= 1
+            if kind == "decode":
+                assert n_tok == 1 and seq >= len(cl)
+            else:
+                assert seq < len(cl) and n_tok <= h.chunk_q_tile
+            for t in range(tok0, tok0 + n_tok):
+                assert lay.seq[t] == seq
+                covered[t].append((split, k0, k1))
+    assert int(pcnt.sum()) == h.n_partials
+    assert np.array_equal(poff, np.concatenate([[0], np.cumsum(pcnt)[:-1]]))
+    for t in range(T):
+        c = sorted(covered[t])
+        assert [s for s, _, _ in c] == list(range(pcnt[t]))
+        assert c[0][1] == 0 and c[-1][2] >= pos[t] + 1
+        for (_, _, a1), (_, b0, _) in zip(c, c[1:]):
+            assert a1 == b0
+
+
+def test_worked_example_through_pack():
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "worked_example_yi34b.json")))
+    e = g["expected"]
+    ra, rb = g["R_A"], g["R_B"]
+    ctx = [100, 250, 3000, 17, 64, 999]
+    cl, cp = [ra["chunk"], rb["chunk"]], [ra["cached_before"], rb["cached_before"]]
+    kv = np.array([cp[0] + cl[0], cp[1] + cl[1]] + [c + 1 for c in ctx])
+    bt, npg = W.deal_block_tables(kv, 16, np.random.default_rng(0))
+    blob, T = _pack(W.YI, cl, cp, ctx, bt, npg, tau=g["tau"])
+    assert T == e["total_tokens"]
+    assert list(hb.meta_array(blob, "q_start")) == [0, 1024, 1824, 1825, 1826, 1827, 1828, 1829, 1830]
+    kvl = hb.meta_array(blob, "kv_len")
+    assert kvl[0] == e["R_A_kv_len_after"] and kvl[1] == e["R_B_kv_len_after"]
+    with pytest.raises(hb.HbError) as ei:
+        _pack(W.YI, cl, cp, ctx, bt, npg, tau=e["total_tokens"] - 1)
+    assert ei.value.name == "HB_E_BUDGET"
+
+
+def _err(fn):
+    with pytest.raises(hb.HbError) as ei:
+        fn()
+    return ei.value.name
+
+
+def test_pack_rejects_invalid_batches():
+    d = W.TINY
+    bt = np.array([[0, 1, -1], [2, -1, -1]], dtype=np.int32)
+    ok = lambda **kw: _pack(d, kw.get("cl", [20]), kw.get("cp", [5]), kw.get("dc", [3]), kw.get("bt", bt),
+                           kw.get("npg", 4), kw.get("tau"))
+    ok()
+    assert _err(lambda: ok(tau=20)) == "HB_E_BUDGET"
+    assert _err(lambda: ok(cl=[0])) == "HB_E_LENGTH"
+    assert _err(lambda: ok(cp=[-1])) == "HB_E_LENGTH"
+    assert _err(lambda: ok(dc=[-2])) == "HB_E_LENGTH"
+    assert _err(lambda: ok(npg=2)) == "HB_E_PAGE"                        # page 2 outside the pool
+    assert _err(lambda: ok(bt=np.array([[0, -1, -1], [2, -1, -1]]))) == "HB_E_PAGE"   # needed entry is -1
+    assert _err(lambda: ok(bt=np.array([[0, 1, -1], [1, -1, -1]]))) == "HB_E_ALIAS"
+    assert _err(lambda: ok(cl=[40], bt=np.array([[0, 1], [2, -1]]))) == "HB_E_PAGE"  # 45 keys > 2 pages
+    assert _err(lambda: ok(cl=[], cp=[], dc=[], bt=np.zeros((0, 3)))) == "HB_E_SHAPE"
+    bad = W.Dims(256, 4, 4, 96, 512)
+    assert _err(lambda: _pack(bad, [4], [0], [], np.array([[0]]), 1)) == "HB_E_SHAPE"
+    bad = W.Dims(256, 6, 4, 64, 512)
+    assert _err(lambda: _pack(bad, [4], [0], [], np.array([[0]]), 1)) == "HB_E_SHAPE"
+    bad = W.Dims(256, 34, 2, 64, 512)   # group 17
+    assert _err(lambda: _pack(bad, [4], [0], [], np.array([[0]]), 1)) == "HB_E_SHAPE"
+    # a too-small buffer is reported, and nothing is written
+    dims = hb.make_dims(d)
+    with pytest.raises(hb.HbError) as ei:
+        hb.pack_metadata(dims, [20], [5], [3], bt, 4, 100, capacity=64)
+    assert ei.value.name == "HB_E_CAPACITY"
+
+
+def test_rope_table_matches_oracle_angles():
+    for dims in (W.TINY, W.MISTRAL):
+        tab = hb.rope_table(hb.make_dims(dims), 5000)
+        ang = O.rope_angles(np.arange(5000), dims.head_dim, dims.rope_theta)
+        assert np.allclose(tab[..., 0], np.cos(ang), rtol=0, atol=1.2e-7)
+        assert np.allclose(tab[..., 1], np.sin(ang), rtol=0, atol=1.2e-7)
+        assert np.all(tab[0, :, 0] == 1.0) and np.all(tab[0, :, 1] == 0.0)
+
+
+def test_workspace_size_covers_buffers():
+    wl = W.mistral_tau512(0)
+    b = wl.batch
+    dims = hb.make_dims(wl.dims)
+    blob, T = hb.pack_metadata(dims, b.chunk_len, b.chunk_prefix, b.decode_ctx, b.block_table, b.num_pages,
+                               b.token_budget)
+    h = hb.header(blob)
+    need = hb.workspace_bytes(dims, blob)
+    d = wl.dims
+    floor = T * (d.hidden * (2 + 4 + 2) + d.n_q_heads * d.head_dim * 4 + d.ffn_dim * 2) + \
+        h.n_partials * d.n_q_heads * (d.head_dim + 2) * 4
+    assert floor <= need <= floor + 16 * 256
