@@ -67,32 +67,19 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
 
   // global -> LDS mapping: 4 passes of 32 rows x 8 chunks of 16 bytes
   const int lr = tid >> 3, lc = tid & 7;
-  const uint16_t* ga[4];
-  const uint16_t* gb[4];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int r = lr + 32 * p;
-    const int am = min(m0 + r, g.M - 1);
-    ga[p] = g.a + (size_t)am * g.lda + lc * 8;
-    gb[p] = weight_row<MODE>(g, n0 + r, n0) + lc * 8;
-  }
-  uint4 ra[4], rb[4];
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      ra[p] = *reinterpret_cast<const uint4*>(ga[p] + kt * BK);
-      rb[p] = *reinterpret_cast<const uint4*>(gb[p] + kt * BK);
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int r = lr + 32 * p;
-      const int o = r * BK + swz(r, lc) * 8;
-      *reinterpret_cast<uint4*>(As + buf * BM * BK + o) = ra[p];
-      *reinterpret_cast<uint4*>(Bs + buf * BN * BK + o) = rb[p];
-    }
-  };
+  const uint16_t* ga0 = g.a + (size_t)min(m0 + lr, g.M - 1) * g.lda + lc * 8;
+  const uint16_t* ga1 = g.a + (size_t)min(m0 + lr + 32, g.M - 1) * g.lda + lc * 8;
+  const uint16_t* ga2 = g.a + (size_t)min(m0 + lr + 64, g.M - 1) * g.lda + lc * 8;
+  const uint16_t* ga3 = g.a + (size_t)min(m0 + lr + 96, g.M - 1) * g.lda + lc * 8;
+  const uint16_t* gb0 = weight_row<MODE>(g, n0 + lr, n0) + lc * 8;
+  const uint16_t* gb1 = weight_row<MODE>(g, n0 + lr + 32, n0) + lc * 8;
+  const uint16_t* gb2 = weight_row<MODE>(g, n0 + lr + 64, n0) + lc * 8;
+  const uint16_t* gb3 = weight_row<MODE>(g, n0 + lr + 96, n0) + lc * 8;
+  // LDS element offsets of this thread's 4 chunks (rows lr + 32p, chunk lc)
+  const int so0 = (lr) * BK + swz(lr, lc) * 8;
+  const int so1 = (lr + 32) * BK + swz(lr + 32, lc) * 8;
+  const int so2 = (lr + 64) * BK + swz(lr + 64, lc) * 8;
+  const int so3 = (lr + 96) * BK + swz(lr + 96, lc) * 8;
 
   f32x4 acc[4][4];
 #pragma unroll
@@ -101,12 +88,33 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nk = g.K / BK;
-  gload(0);
-  lstore(0);
+  uint4 ra0 = *reinterpret_cast<const uint4*>(ga0), ra1 = *reinterpret_cast<const uint4*>(ga1);
+  uint4 ra2 = *reinterpret_cast<const uint4*>(ga2), ra3 = *reinterpret_cast<const uint4*>(ga3);
+  uint4 rb0 = *reinterpret_cast<const uint4*>(gb0), rb1 = *reinterpret_cast<const uint4*>(gb1);
+  uint4 rb2 = *reinterpret_cast<const uint4*>(gb2), rb3 = *reinterpret_cast<const uint4*>(gb3);
+  *reinterpret_cast<uint4*>(As + so0) = ra0;
+  *reinterpret_cast<uint4*>(As + so1) = ra1;
+  *reinterpret_cast<uint4*>(As + so2) = ra2;
+  *reinterpret_cast<uint4*>(As + so3) = ra3;
+  *reinterpret_cast<uint4*>(Bs + so0) = rb0;
+  *reinterpret_cast<uint4*>(Bs + so1) = rb1;
+  *reinterpret_cast<uint4*>(Bs + so2) = rb2;
+  *reinterpret_cast<uint4*>(Bs + so3) = rb3;
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
+    const bool more = kt + 1 < nk;
+    if (more) {
+      const int ko = (kt + 1) * BK;
+      ra0 = *reinterpret_cast<const uint4*>(ga0 + ko);
+      ra1 = *reinterpret_cast<const uint4*>(ga1 + ko);
+      ra2 = *reinterpret_cast<const uint4*>(ga2 + ko);
+      ra3 = *reinterpret_cast<const uint4*>(ga3 + ko);
+      rb0 = *reinterpret_cast<const uint4*>(gb0 + ko);
+      rb1 = *reinterpret_cast<const uint4*>(gb1 + ko);
+      rb2 = *reinterpret_cast<const uint4*>(gb2 + ko);
+      rb3 = *reinterpret_cast<const uint4*>(gb3 + ko);
+    }
     const uint16_t* as = As + cur * BM * BK;
     const uint16_t* bs = Bs + cur * BN * BK;
 #pragma unroll
@@ -128,7 +136,18 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(af[i], bfr[j], acc[i][j]);
     }
-    if (kt + 1 < nk) lstore(cur ^ 1);
+    if (more) {
+      uint16_t* an = As + (cur ^ 1) * BM * BK;
+      uint16_t* bn = Bs + (cur ^ 1) * BN * BK;
+      *reinterpret_cast<uint4*>(an + so0) = ra0;
+      *reinterpret_cast<uint4*>(an + so1) = ra1;
+      *reinterpret_cast<uint4*>(an + so2) = ra2;
+      *reinterpret_cast<uint4*>(an + so3) = ra3;
+      *reinterpret_cast<uint4*>(bn + so0) = rb0;
+      *reinterpret_cast<uint4*>(bn + so1) = rb1;
+      *reinterpret_cast<uint4*>(bn + so2) = rb2;
+      *reinterpret_cast<uint4*>(bn + so3) = rb3;
+    }
     __syncthreads();
   }
 
