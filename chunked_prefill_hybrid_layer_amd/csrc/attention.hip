@@ -41,30 +41,109 @@ __device__ __forceinline__ uint2 keep_first(uint2 v, int n) {
 // of values that largely cancel, that error does not shrink with the number
 // of keys.
 __device__ __forceinline__ void split_p(const float* p, bf16x8& hi, bf16x8& lo) {
-  uint32_t h[8];
-  float r[8];
+  uint32_t h[4], l[4];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    h[e] = f2bf(p[e]);
-    r[e] = p[e] - bf2f((uint16_t)h[e]);
+  for (int e = 0; e < 4; ++e) {
+    h[e] = pack2bf(p[2 * e], p[2 * e + 1]);
+    const float r0 = p[2 * e] - __uint_as_float(h[e] << 16);
+    const float r1 = p[2 * e + 1] - __uint_as_float(h[e] & 0xffff0000u);
+    l[e] = pack2bf(r0, r1);
   }
-  uint4 uh, ul;
-  uh.x = h[0] | (h[1] << 16);
-  uh.y = h[2] | (h[3] << 16);
-  uh.z = h[4] | (h[5] << 16);
-  uh.w = h[6] | (h[7] << 16);
-  ul.x = pack2bf(r[0], r[1]);
-  ul.y = pack2bf(r[2], r[3]);
-  ul.z = pack2bf(r[4], r[5]);
-  ul.w = pack2bf(r[6], r[7]);
-  hi = as_bf16x8(uh);
-  lo = as_bf16x8(ul);
+  hi = as_bf16x8(make_uint4(h[0], h[1], h[2], h[3]));
+  lo = as_bf16x8(make_uint4(l[0], l[1], l[2], l[3]));
 }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ----------------------------------------------------------------------------
 // decode items
+//
+// One step covers 32 keys (2 pages).  The item's page ids (at most 16: a
+// decode item spans at most kDecodeKvSplit = 256 keys) sit one per lane and
+// are broadcast with readlane, so no step waits on a block-table load.  K/V of
+// step j+1 are in flight while step j computes (two register buffers, the
+// loop unrolled by two).
+
+// Issue the K (4 x 16 B per page) and V^T (8 x 8 B per page) fragment loads of
+// the step starting at key KB into buffer set SFX.
+#define DEC_LOAD(KB, SFX)                                                                     \
+  {                                                                                           \
+    const int _j = ((KB) - it.key0) >> 4;                                                     \
+    const bool _has1 = (KB) + 16 < it.key1;                                                   \
+    const int _pg0 = __builtin_amdgcn_readlane(my_pg, _j);                                    \
+    const int _pg1 = __builtin_amdgcn_readlane(my_pg, _has1 ? _j + 1 : _j);                   \
+    const uint16_t* _K0 = a.k_cache + ((size_t)_pg0 * nkv + kvh) * hs + r * D + qd * 8;       \
+    const uint16_t* _K1 = a.k_cache + ((size_t)_pg1 * nkv + kvh) * hs + r * D + qd * 8;       \
+    const uint16_t* _V0 = a.v_cache + ((size_t)_pg0 * nkv + kvh) * hs + r * 16 + qd * 4;      \
+    const uint16_t* _V1 = a.v_cache + ((size_t)_pg1 * nkv + kvh) * hs + r * 16 + qd * 4;      \
+    _Pragma("unroll") for (int kk = 0; kk < KK; ++kk)                                         \
+        k0##SFX[kk] = *reinterpret_cast<const uint4*>(_K0 + kk * 32);                        \
+    _Pragma("unroll") for (int jj = 0; jj < NJ; ++jj)                                         \
+        v0##SFX[jj] = *reinterpret_cast<const uint2*>(_V0 + jj * 256);                        \
+    if (_has1) {                                                                              \
+      _Pragma("unroll") for (int kk = 0; kk < KK; ++kk)                                       \
+          k1##SFX[kk] = *reinterpret_cast<const uint4*>(_K1 + kk * 32);                      \
+      _Pragma("unroll") for (int jj = 0; jj < NJ; ++jj)                                       \
+          v1##SFX[jj] = *reinterpret_cast<const uint2*>(_V1 + jj * 256);                      \
+    } else {                                                                                  \
+      _Pragma("unroll") for (int kk = 0; kk < KK; ++kk) k1##SFX[kk] = make_uint4(0, 0, 0, 0); \
+      _Pragma("unroll") for (int jj = 0; jj < NJ; ++jj) v1##SFX[jj] = make_uint2(0, 0);       \
+    }                                                                                         \
+  }
+
+// Scores, online softmax and PV for the step starting at key KB from buffer SFX.
+#define DEC_COMPUTE(KB, SFX)                                                                  \
+  {                                                                                           \
+    const bool _has1 = (KB) + 16 < it.key1;                                                   \
+    f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;                                            \
+    _Pragma("unroll") for (int kk = 0; kk < KK; ++kk)                                         \
+        s0 = mfma16x16x32(as_bf16x8(k0##SFX[kk]), qf[kk], s0);                               \
+    if (_has1) {                                                                              \
+      _Pragma("unroll") for (int kk = 0; kk < KK; ++kk)                                       \
+          s1 = mfma16x16x32(as_bf16x8(k1##SFX[kk]), qf[kk], s1);                             \
+    }                                                                                         \
+    /* raw scores; keys past the item's end are masked (tail step only) */                   \
+    float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};                   \
+    if ((KB) + 32 > it.key1) {                                                                \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                         \
+        if ((KB) + 4 * qd + i >= it.key1) sv[i] = -INFINITY;                                  \
+        if ((KB) + 16 + 4 * qd + i >= it.key1) sv[4 + i] = -INFINITY;                         \
+      }                                                                                       \
+    }                                                                                         \
+    float mb = sv[0];                                                                         \
+    _Pragma("unroll") for (int e = 1; e < 8; ++e) mb = fmaxf(mb, sv[e]);                      \
+    mb = fmaxf(mb, __shfl_xor(mb, 16, 64));                                                   \
+    mb = fmaxf(mb, __shfl_xor(mb, 32, 64));                                                   \
+    /* running max in log2 units; the first step always has a valid key */                    \
+    const float mn = fmaxf(m, mb * scale_log2);                                               \
+    const float alpha = fast_exp2(m - mn);                                                    \
+    float ps[8], lsum = 0.f;                                                                  \
+    _Pragma("unroll") for (int e = 0; e < 8; ++e) {                                           \
+      ps[e] = fast_exp2(fmaf(sv[e], scale_log2, -mn));                                        \
+      lsum += ps[e];                                                                          \
+    }                                                                                         \
+    l = l * alpha + lsum;                                                                     \
+    m = mn;                                                                                   \
+    bf16x8 pf, pfl;                                                                           \
+    split_p(ps, pf, pfl);                                                                     \
+    if ((KB) + 32 > it.key1) { /* tail: values past the last key may be poisoned */           \
+      const int n0 = it.key1 - ((KB) + 4 * qd), n1 = it.key1 - ((KB) + 16 + 4 * qd);         \
+      _Pragma("unroll") for (int jj = 0; jj < NJ; ++jj) {                                     \
+        v0##SFX[jj] = keep_first(v0##SFX[jj], n0);                                            \
+        v1##SFX[jj] = keep_first(v1##SFX[jj], n1);                                            \
+      }                                                                                       \
+    }                                                                                         \
+    _Pragma("unroll") for (int jj = 0; jj < NJ; ++jj) {                                       \
+      acc[jj] *= alpha;                                                                       \
+      const bf16x8 vf =                                                                       \
+          as_bf16x8(make_uint4(v0##SFX[jj].x, v0##SFX[jj].y, v1##SFX[jj].x, v1##SFX[jj].y));  \
+      acc[jj] = mfma16x16x32(vf, pf, acc[jj]);                                                \
+      acc[jj] = mfma16x16x32(vf, pfl, acc[jj]);                                               \
+    }                                                                                         \
+  }
+
 template <int D>
-__global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, float scale_log2) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_decode_kernel(AttnArgs a, float scale_log2) {
   constexpr int KK = D / 32;  // MFMA k-steps over the head dim
   constexpr int NJ = D / 16;  // 16-dim output blocks
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -76,6 +155,8 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, float scal
   const int r = lane & 15, qd = lane >> 4;
   const int t = it.tok0;
   const int32_t* bt = a.meta.block_table + (size_t)it.seq * a.max_pages;
+  const int npg = (it.key1 - it.key0 + 15) >> 4;
+  const int my_pg = (lane < npg) ? bt[(it.key0 >> 4) + lane] : 0;
 
   bf16x8 qf[KK];
   {
@@ -90,77 +171,20 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, float scal
   float m = -INFINITY, l = 0.f;
   const size_t hs = (size_t)16 * D;  // elements of one (page, kv head) block
 
-  for (int kb = it.key0; kb < it.key1; kb += 32) {
-    const bool has1 = kb + 16 < it.key1;
-    const int pg0 = bt[kb >> 4];
-    const int pg1 = has1 ? bt[(kb >> 4) + 1] : pg0;
-    const uint16_t* K0 = a.k_cache + ((size_t)pg0 * nkv + kvh) * hs;
-    const uint16_t* K1 = a.k_cache + ((size_t)pg1 * nkv + kvh) * hs;
-    const uint16_t* V0 = a.v_cache + ((size_t)pg0 * nkv + kvh) * hs;
-    const uint16_t* V1 = a.v_cache + ((size_t)pg1 * nkv + kvh) * hs;
-    uint4 k0[KK], k1[KK];
-    uint2 v0[NJ], v1[NJ];
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) k0[kk] = *reinterpret_cast<const uint4*>(K0 + r * D + kk * 32 + qd * 8);
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) v0[j] = *reinterpret_cast<const uint2*>(V0 + (j * 16 + r) * 16 + qd * 4);
-    if (has1) {
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) k1[kk] = *reinterpret_cast<const uint4*>(K1 + r * D + kk * 32 + qd * 8);
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) v1[j] = *reinterpret_cast<const uint2*>(V1 + (j * 16 + r) * 16 + qd * 4);
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) k1[kk] = make_uint4(0, 0, 0, 0);
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) v1[j] = make_uint2(0, 0);
-    }
-    // S^T tiles: s0[i] = score(key kb + 4qd + i, row r), s1[i] = score(key kb + 16 + 4qd + i, row r)
-    f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) s0 = mfma16x16x32(as_bf16x8(k0[kk]), qf[kk], s0);
-    if (has1) {
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) s1 = mfma16x16x32(as_bf16x8(k1[kk]), qf[kk], s1);
-    }
-    float sv[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sv[i] = (kb + 4 * qd + i < it.key1) ? s0[i] * scale_log2 : -INFINITY;
-      sv[4 + i] = (kb + 16 + 4 * qd + i < it.key1) ? s1[i] * scale_log2 : -INFINITY;
-    }
-    float mb = sv[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) mb = fmaxf(mb, sv[e]);
-    mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
-    mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-    const float mn = fmaxf(m, mb);
-    const float alpha = (mn == -INFINITY) ? 1.f : exp2f(m - mn);
-    float ps[8], lsum = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      ps[e] = (sv[e] == -INFINITY) ? 0.f : exp2f(sv[e] - mn);
-      lsum += ps[e];
-    }
-    l = l * alpha + lsum;
-    m = mn;
-    bf16x8 pf, pfl;
-    split_p(ps, pf, pfl);
-    if (kb + 32 > it.key1) {  // tail: values past the last key may be poisoned
-      const int n0 = it.key1 - (kb + 4 * qd), n1 = it.key1 - (kb + 16 + 4 * qd);
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        v0[j] = keep_first(v0[j], n0);
-        v1[j] = keep_first(v1[j], n1);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      acc[j] *= alpha;
-      const bf16x8 vf = as_bf16x8(make_uint4(v0[j].x, v0[j].y, v1[j].x, v1[j].y));
-      acc[j] = mfma16x16x32(vf, pf, acc[j]);
-      acc[j] = mfma16x16x32(vf, pfl, acc[j]);
-    }
+  uint4 k0A[KK], k1A[KK], k0B[KK], k1B[KK];
+  uint2 v0A[NJ], v1A[NJ], v0B[NJ], v1B[NJ];
+  int kb = it.key0;
+  DEC_LOAD(kb, A);
+  while (true) {
+    const int kbB = kb + 32;
+    if (kbB < it.key1) DEC_LOAD(kbB, B);
+    DEC_COMPUTE(kb, A);
+    if (kbB >= it.key1) break;
+    const int kbA = kbB + 32;
+    if (kbA < it.key1) DEC_LOAD(kbA, A);
+    DEC_COMPUTE(kbB, B);
+    if (kbA >= it.key1) break;
+    kb = kbA;
   }
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
@@ -177,6 +201,9 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, float scal
     }
   }
 }
+
+#undef DEC_LOAD
+#undef DEC_COMPUTE
 
 // ----------------------------------------------------------------------------
 // chunk items
@@ -218,51 +245,60 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(AttnArgs a, float scale
     for (int j = 0; j < NJ; ++j) acc[rb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
 
+  // the item's page ids (at most kChunkKvSplit / 16 = 64), staged once
+  __shared__ int pids[kChunkKvSplit / 16];
+  const int npg = (it.key1 - it.key0 + 15) >> 4;
+  if (tid < npg) pids[tid] = bt[(it.key0 >> 4) + tid];
+  __syncthreads();
+
+  // thread tid moves 16-byte chunk ci = tid + 256 u of the 4-page tile:
+  // page ci / (2 D), chunk `within` = ci % (2 D) of that (page, kv head) block
   uint4 kr[NLD], vr[NLD];
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int u = 0; u < NLD; ++u) {
-      const int ci = tid + 256 * u;
-      const int pg = ci / (2 * D), within = ci % (2 * D);
-      const int key_base = kt + pg * 16;
-      if (key_base < it.key1) {
-        const int page = bt[key_base >> 4];
-        const size_t base = ((size_t)page * nkv + kvh) * PAGE + (size_t)within * 8;
-        kr[u] = *reinterpret_cast<const uint4*>(a.k_cache + base);
-        uint4 v = *reinterpret_cast<const uint4*>(a.v_cache + base);
-        // V chunk `within` holds dim within/2, keys 8*(within&1) .. +7 of the page
-        const int nvalid = it.key1 - (key_base + 8 * (within & 1));
-        const uint2 lo = keep_first(make_uint2(v.x, v.y), nvalid);
-        const uint2 hi = keep_first(make_uint2(v.z, v.w), nvalid - 4);
-        vr[u] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-      } else {
-        kr[u] = make_uint4(0, 0, 0, 0);
-        vr[u] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < NLD; ++u) {
-      const int ci = tid + 256 * u;
-      const int pg = ci / (2 * D), within = ci % (2 * D);
-      const int key = within / KCH, c = within % KCH;
-      *reinterpret_cast<uint4*>(&Ks[buf][(pg * 16 + key) * D + (c ^ (key & (KCH - 1))) * 8]) = kr[u];
-      const int dd = within >> 1, hf = within & 1, s = (dd >> 3) & 3;
-      uint16_t* vrow = &Vs[buf][pg * PAGE + dd * 16];
-      *reinterpret_cast<uint2*>(vrow + ((2 * hf) ^ s) * 4) = make_uint2(vr[u].x, vr[u].y);
-      *reinterpret_cast<uint2*>(vrow + ((2 * hf + 1) ^ s) * 4) = make_uint2(vr[u].z, vr[u].w);
-    }
-  };
+#define CHUNK_GLOAD(KT)                                                                       \
+  _Pragma("unroll") for (int u = 0; u < NLD; ++u) {                                           \
+    const int ci = tid + 256 * u;                                                             \
+    const int pg = ci / (2 * D), within = ci % (2 * D);                                       \
+    const int key_base = (KT) + pg * 16;                                                      \
+    if (key_base < it.key1) {                                                                 \
+      const int page = pids[(key_base - it.key0) >> 4];                                       \
+      const size_t base = ((size_t)page * nkv + kvh) * PAGE + (size_t)within * 8;             \
+      kr[u] = *reinterpret_cast<const uint4*>(a.k_cache + base);                              \
+      vr[u] = *reinterpret_cast<const uint4*>(a.v_cache + base);                              \
+    } else {                                                                                  \
+      kr[u] = make_uint4(0, 0, 0, 0);                                                         \
+      vr[u] = make_uint4(0, 0, 0, 0);                                                         \
+    }                                                                                         \
+  }
+  // K rows go to Ks swizzled by key; V^T chunk `within` holds dim within / 2,
+  // keys 8 (within & 1) .. +7 of its page: values past the item's last key are
+  // zeroed (the cache may hold poison there), and each 4-key group is placed at
+  // group ^ ((dim >> 3) & 3) so the PV fragment reads are conflict free.
+#define CHUNK_LSTORE(KT, BUF)                                                                 \
+  _Pragma("unroll") for (int u = 0; u < NLD; ++u) {                                           \
+    const int ci = tid + 256 * u;                                                             \
+    const int pg = ci / (2 * D), within = ci % (2 * D);                                       \
+    const int key = within / KCH, c = within % KCH;                                           \
+    *reinterpret_cast<uint4*>(&Ks[BUF][(pg * 16 + key) * D + (c ^ (key & (KCH - 1))) * 8]) = kr[u]; \
+    const int nvalid = it.key1 - ((KT) + pg * 16 + 8 * (within & 1));                         \
+    const uint2 lo = keep_first(make_uint2(vr[u].x, vr[u].y), nvalid);                        \
+    const uint2 hi = keep_first(make_uint2(vr[u].z, vr[u].w), nvalid - 4);                    \
+    const int dd = within >> 1, hf = within & 1, sw = (dd >> 3) & 3;                          \
+    uint16_t* vrow = &Vs[BUF][pg * PAGE + dd * 16];                                           \
+    *reinterpret_cast<uint2*>(vrow + ((2 * hf) ^ sw) * 4) = lo;                               \
+    *reinterpret_cast<uint2*>(vrow + ((2 * hf + 1) ^ sw) * 4) = hi;                           \
+  }
 
   const int ntiles = (it.key1 - it.key0 + 63) / 64;
-  gload(it.key0);
-  lstore(0);
+  const int first_pos = a.meta.tok_pos[it.tok0];
+  CHUNK_GLOAD(it.key0);
+  CHUNK_LSTORE(it.key0, 0);
   __syncthreads();
   for (int ti = 0; ti < ntiles; ++ti) {
     const int kt = it.key0 + ti * 64;
     const int cur = ti & 1;
-    if (ti + 1 < ntiles) gload(kt + 64);
+    if (ti + 1 < ntiles) {
+      CHUNK_GLOAD(kt + 64);
+    }
     f32x4 s[4][2];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -278,33 +314,45 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(AttnArgs a, float scale
       }
     }
     bf16x8 pf[2][2], pfl[2][2];
+    // causal / end-of-range masks matter only on tiles reaching past the first
+    // row's position or past the item's last key (wave-uniform test)
+    const bool need_mask = (kt + 64 > it.key1) || (kt + 63 > first_pos);
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       float sv[16];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kt + kb * 16 + 4 * qd + i;
-          sv[kb * 4 + i] = (key <= rpos[rb] && key < it.key1) ? s[kb][rb][i] * scale_log2 : -INFINITY;
-        }
+        for (int i = 0; i < 4; ++i) sv[kb * 4 + i] = s[kb][rb][i];
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = kt + kb * 16 + 4 * qd + i;
+            if (!(key <= rpos[rb] && key < it.key1)) sv[kb * 4 + i] = -INFINITY;
+          }
+      }
       float mb = sv[0];
 #pragma unroll
       for (int e = 1; e < 16; ++e) mb = fmaxf(mb, sv[e]);
       mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
       mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-      const float mn = fmaxf(m[rb], mb);
-      const float alpha = (mn == -INFINITY) ? 1.f : exp2f(m[rb] - mn);
+      const float mn = fmaxf(m[rb], mb * scale_log2);   // log2 units; -inf while a row saw no key
+      const float ms = (mn == -INFINITY) ? 0.f : mn;
+      const float alpha = fast_exp2(m[rb] - ms);
       float ps[16], lsum = 0.f;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        ps[e] = (sv[e] == -INFINITY) ? 0.f : exp2f(sv[e] - mn);
+        ps[e] = fast_exp2(fmaf(sv[e], scale_log2, -ms));
         lsum += ps[e];
       }
       l[rb] = l[rb] * alpha + lsum;
       m[rb] = mn;
+      if (__any(alpha != 1.0f)) {
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) acc[rb][j] *= alpha;
+        for (int j = 0; j < NJ; ++j) acc[rb][j] *= alpha;
+      }
       // keys 32c + 4qd + e (e < 4) and 32c + 16 + 4qd + (e - 4) (e >= 4)
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
@@ -331,9 +379,13 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(AttnArgs a, float scale
         acc[1][j] = mfma16x16x32(vf, pfl[1][c], acc[1][j]);
       }
     }
-    if (ti + 1 < ntiles) lstore(cur ^ 1);
+    if (ti + 1 < ntiles) {
+      CHUNK_LSTORE(kt + 64, cur ^ 1);
+    }
     __syncthreads();
   }
+#undef CHUNK_GLOAD
+#undef CHUNK_LSTORE
 
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
@@ -378,7 +430,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   for (int p = 0; p < pc; ++p) {
     const size_t pr = (size_t)(p0 + p) * nq + h;
     const float mp = a.part_ml[pr * 2], lp = a.part_ml[pr * 2 + 1];
-    const float w = (mp == -INFINITY) ? 0.f : exp2f(mp - M);
+    const float w = (mp == -INFINITY) ? 0.f : fast_exp2(mp - M);
     L += w * lp;
     const float* src = a.part_o + pr * D + lane * E;
 #pragma unroll
