@@ -24,6 +24,7 @@ constexpr int kMaxGroup = 16;         // decode path holds a kv group in one 16-
 constexpr int kGemmBM = 128;
 constexpr int kGemmBN = 128;
 constexpr int kGemmBK = 64;
+constexpr int kNumCU = 256;           // MI355X compute units (split-K sizing)
 
 inline int chunk_q_tile(int group) { return group >= kChunkRows ? 1 : kChunkRows / group; }
 
@@ -36,7 +37,7 @@ hb_status check_dims(const hb_dims* d);
 
 // Byte layout of the device workspace for one batch.
 struct WsLayout {
-  size_t xn, q, o, h1, h1n, act, part_o, part_ml, total;
+  size_t xn, q, o, h1, h1n, act, part_o, part_ml, gemm_part, total;
 };
 WsLayout ws_layout(const hb_dims& d, int n_tokens, int n_partials);
 
@@ -99,8 +100,19 @@ struct GemmArgs {
   uint16_t* k_cache;
   uint16_t* v_cache;
   int n_q_heads, n_kv_heads, head_dim;
+  // split-K partials [splits][M][N] fp32 (used when the plan splits K)
+  float* part;
 };
+// Tile shape (waves along M: 2 -> 128-row tiles, 4 -> 256-row tiles) and
+// split-K factor the GEMM launcher uses for a problem; the QKV launch reduces
+// its own split, residual-mode callers reduce with launch_splitk_reduce.
+struct GemmPlan {
+  int wm, splits;
+};
+GemmPlan gemm_plan(int mode, int M, int N, int K);
 hb_status launch_gemm(const GemmArgs& g, stream_t s);
+hb_status launch_splitk_reduce(const float* part, int splits, const float* res, float* out, int M, int N,
+                               const uint16_t* gain, uint16_t* norm_out, float eps, stream_t s);
 
 struct AttnArgs {
   const uint16_t* q;       // [T][n_q * d]

@@ -123,6 +123,7 @@ extern "C" hb_status hb_layer_forward(const hb_dims* dims, const hb_weights* w, 
   g.n_q_heads = nq;
   g.n_kv_heads = nkv;
   g.head_dim = d;
+  g.part = (float*)(ws + L.gemm_part);
   mark(1);
   HB_TRY(launch_gemm(g, s));
 
@@ -145,7 +146,11 @@ extern "C" hb_status hb_layer_forward(const hb_dims* dims, const hb_weights* w, 
   at.out = ob;
   HB_TRY(launch_attention(at, s, stage_events ? stage_events + 2 : nullptr));
 
-  // a6: O projection + residual
+  // a6: O projection + residual, a7: RMSNorm (split-K: the reduce adds the
+  // residual and normalises in one pass)
+  float* gpart = (float*)(ws + L.gemm_part);
+  const GemmPlan po = gemm_plan(kGemmResidual, T, H, nq * d);
+  const GemmPlan pd = gemm_plan(kGemmResidual, T, H, F);
   GemmArgs go{};
   go.mode = kGemmResidual;
   go.a = ob;
@@ -157,12 +162,15 @@ extern "C" hb_status hb_layer_forward(const hb_dims* dims, const hb_weights* w, 
   go.res = x;
   go.out_f = h1;
   go.ldo = H;
+  go.part = gpart;
   mark(5);
   HB_TRY(launch_gemm(go, s));
-
-  // a7: RMSNorm
   mark(6);
-  HB_TRY(launch_rmsnorm(h1, w->g_ffn, h1n, T, H, dims->rms_eps, s));
+  if (po.splits > 1) {
+    HB_TRY(launch_splitk_reduce(gpart, po.splits, x, h1, T, H, w->g_ffn, h1n, dims->rms_eps, s));
+  } else {
+    HB_TRY(launch_rmsnorm(h1, w->g_ffn, h1n, T, H, dims->rms_eps, s));
+  }
 
   // a8: gate/up projection + SwiGLU
   GemmArgs gu{};
@@ -191,8 +199,10 @@ extern "C" hb_status hb_layer_forward(const hb_dims* dims, const hb_weights* w, 
   gd.res = h1;
   gd.out_f = y;
   gd.ldo = H;
+  gd.part = gpart;
   mark(8);
   HB_TRY(launch_gemm(gd, s));
+  if (pd.splits > 1) HB_TRY(launch_splitk_reduce(gpart, pd.splits, h1, y, T, H, nullptr, nullptr, 0.f, s));
   mark(9);
   return HB_OK;
 }
