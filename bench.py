@@ -142,6 +142,8 @@ def main():
     ap.add_argument("--workload", default="mistral_tau512")
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the timed steps, copy 256 MiB device-to-device once (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this build runs the hybrid-batch layer on one GPU only; "
@@ -213,6 +215,12 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms = t_start.elapsed_time(t_end) / args.steps
+    if args.calibrate_copy:
+        src = torch.empty(64 << 20, dtype=torch.int32, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
     stage_ms = np.array([[evs[i][k].elapsed_time(evs[i][k + 1]) for k in range(nst)]
                          for i in range(args.steps)])
     stage_mean = stage_ms.mean(axis=0)
