@@ -173,26 +173,37 @@ def main():
     pin = [torch.empty(size, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
     pin_np = [p.numpy() for p in pin]
     dev = [torch.empty(size, dtype=torch.uint8, device="cuda") for _ in range(2)]
-    copied = [None, None]
     ws = torch.empty(hb.workspace_bytes(hd, hb.pack_metadata(hd, b.chunk_len, b.chunk_prefix, b.decode_ctx,
                                                                b.block_table, b.num_pages, b.token_budget)[0]),
                      dtype=torch.uint8, device="cuda")
     stream = stream_handle()
+    # per-step host work is one C call each for packing and for the forward
+    packers = [hb.Packer(hd, b.chunk_len, b.chunk_prefix, b.decode_ctx, b.block_table, b.num_pages,
+                         b.token_budget, pin_np[j]) for j in range(2)]
+    fwds = [[hb.Forward(hd, L.hw, pin_np[j], dev[j].data_ptr(), L.rope.data_ptr(), L.rope_max_pos, x.data_ptr(),
+                        y.data_ptr(), L.k_cache.data_ptr(), L.v_cache.data_ptr(), ws.data_ptr(), ws.numel(), stream)
+             for j in range(2)] for L in layers]
+    # The metadata upload of step i+1 runs on its own stream while step i
+    # computes; the compute stream waits only for that copy, and a device
+    # buffer is refilled only after the forward that read it has finished.
+    compute = torch.cuda.current_stream()
+    upload = torch.cuda.Stream()
+    copied = [torch.cuda.Event(), torch.cuda.Event()]
+    consumed = [torch.cuda.Event(), torch.cuda.Event()]
+    for e in copied + consumed:
+        e.record(compute)
 
     def step(i, events=None):
         j = i & 1
-        if copied[j] is not None:
-            copied[j].synchronize()            # the copy that last read this pinned buffer is done
-        hb.pack_metadata(hd, b.chunk_len, b.chunk_prefix, b.decode_ctx, b.block_table, b.num_pages,
-                         b.token_budget, out=pin_np[j])
-        dev[j].copy_(pin[j], non_blocking=True)
-        ev = torch.cuda.Event()
-        ev.record()
-        copied[j] = ev
-        L = layers[i % len(layers)]
-        hb.layer_forward(hd, L.hw, pin_np[j], dev[j].data_ptr(), L.rope.data_ptr(), L.rope_max_pos,
-                         x.data_ptr(), y.data_ptr(), L.k_cache.data_ptr(), L.v_cache.data_ptr(),
-                         ws.data_ptr(), ws.numel(), stream, events)
+        copied[j].synchronize()                # the copy that last read this pinned buffer is done
+        packers[j]()
+        upload.wait_event(consumed[j])
+        with torch.cuda.stream(upload):
+            dev[j].copy_(pin[j], non_blocking=True)
+        copied[j].record(upload)
+        compute.wait_event(copied[j])
+        fwds[i % len(layers)][j](events)
+        consumed[j].record(compute)
 
     for i in range(args.warmup):
         step(i)
@@ -204,13 +215,14 @@ def main():
             e.record()
     torch.cuda.synchronize()
     assert all(e.cuda_event for row in evs for e in row)
+    ev_arrays = [hb.make_events([e.cuda_event for e in row]) for row in evs]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record()
     for i in range(args.steps):
-        step(args.warmup + i, [e.cuda_event for e in evs[i]])
+        step(args.warmup + i, ev_arrays[i])
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0

@@ -208,7 +208,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 // ----------------------------------------------------------------------------
 // chunk items
 template <int D>
-__global__ __launch_bounds__(256) void attn_chunk_kernel(AttnArgs a, float scale_log2) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_chunk_kernel(AttnArgs a, float scale_log2) {
   constexpr int KK = D / 32;
   constexpr int NJ = D / 16;
   constexpr int KCH = D / 8;      // 16-byte chunks per K row
@@ -272,7 +272,7 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(AttnArgs a, float scale
   // K rows go to Ks swizzled by key; V^T chunk `within` holds dim within / 2,
   // keys 8 (within & 1) .. +7 of its page: values past the item's last key are
   // zeroed (the cache may hold poison there), and each 4-key group is placed at
-  // group ^ ((dim >> 3) & 3) so the PV fragment reads are conflict free.
+  // group ^ ((dim >> 2) & 3): the PV fragment reads (ds_read_b64) then have no bank conflicts.
 #define CHUNK_LSTORE(KT, BUF)                                                                 \
   _Pragma("unroll") for (int u = 0; u < NLD; ++u) {                                           \
     const int ci = tid + 256 * u;                                                             \
@@ -282,7 +282,7 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(AttnArgs a, float scale
     const int nvalid = it.key1 - ((KT) + pg * 16 + 8 * (within & 1));                         \
     const uint2 lo = keep_first(make_uint2(vr[u].x, vr[u].y), nvalid);                        \
     const uint2 hi = keep_first(make_uint2(vr[u].z, vr[u].w), nvalid - 4);                    \
-    const int dd = within >> 1, hf = within & 1, sw = (dd >> 3) & 3;                          \
+    const int dd = within >> 1, hf = within & 1, sw = (dd >> 2) & 3;                          \
     uint16_t* vrow = &Vs[BUF][pg * PAGE + dd * 16];                                           \
     *reinterpret_cast<uint2*>(vrow + ((2 * hf) ^ sw) * 4) = lo;                               \
     *reinterpret_cast<uint2*>(vrow + ((2 * hf + 1) ^ sw) * 4) = hi;                           \
@@ -369,7 +369,7 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(AttnArgs a, float scale
     for (int c = 0; c < 2; ++c) {
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        const int dd = j * 16 + r, sw = (dd >> 3) & 3;
+        const int dd = j * 16 + r, sw = (dd >> 2) & 3;
         const uint2 lo = *reinterpret_cast<const uint2*>(&Vs[cur][(2 * c) * PAGE + dd * 16 + (qd ^ sw) * 4]);
         const uint2 hi = *reinterpret_cast<const uint2*>(&Vs[cur][(2 * c + 1) * PAGE + dd * 16 + (qd ^ sw) * 4]);
         const bf16x8 vf = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
@@ -412,34 +412,39 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(AttnArgs a, float scale
 }
 
 // ----------------------------------------------------------------------------
-// merge: o = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p, one wave per (token, head)
+// merge: o = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p over a token's
+// partials.  D/4 lanes per (token, head), each owning 4 consecutive dims.
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
-  constexpr int E = D / 64;
-  const int lane = threadIdx.x & 63;
-  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  constexpr int LPH = D / 4;                 // lanes per (token, head)
+  constexpr int PER_BLOCK = 256 / LPH;
+  const int sub = threadIdx.x / LPH, l4 = threadIdx.x % LPH;
+  const int64_t wid = (int64_t)blockIdx.x * PER_BLOCK + sub;
   const int nq = a.n_q_heads;
   if (wid >= (int64_t)a.n_tokens * nq) return;
   const int t = (int)(wid / nq), h = (int)(wid % nq);
   const int p0 = a.meta.part_off[t], pc = a.meta.part_cnt[t];
+  const float* ml = a.part_ml + ((size_t)p0 * nq + h) * 2;
   float M = -INFINITY;
-  for (int p = 0; p < pc; ++p) M = fmaxf(M, a.part_ml[((size_t)(p0 + p) * nq + h) * 2]);
-  float L = 0.f, o[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) o[e] = 0.f;
+  for (int p = 0; p < pc; ++p) M = fmaxf(M, ml[(size_t)p * nq * 2]);
+  float L = 0.f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  const float* src = a.part_o + ((size_t)p0 * nq + h) * D + l4 * 4;
   for (int p = 0; p < pc; ++p) {
-    const size_t pr = (size_t)(p0 + p) * nq + h;
-    const float mp = a.part_ml[pr * 2], lp = a.part_ml[pr * 2 + 1];
+    const float mp = ml[(size_t)p * nq * 2], lp = ml[(size_t)p * nq * 2 + 1];
     const float w = (mp == -INFINITY) ? 0.f : fast_exp2(mp - M);
     L += w * lp;
-    const float* src = a.part_o + pr * D + lane * E;
-#pragma unroll
-    for (int e = 0; e < E; ++e) o[e] += w * src[e];
+    const float4 v = *reinterpret_cast<const float4*>(src + (size_t)p * nq * D);
+    o.x += w * v.x;
+    o.y += w * v.y;
+    o.z += w * v.z;
+    o.w += w * v.w;
   }
   const float inv = 1.0f / L;
-  uint16_t* dst = a.out + (size_t)t * nq * D + (size_t)h * D + lane * E;
-#pragma unroll
-  for (int e = 0; e < E; ++e) dst[e] = f2bf(o[e] * inv);
+  uint2 pk;
+  pk.x = pack2bf(o.x * inv, o.y * inv);
+  pk.y = pack2bf(o.z * inv, o.w * inv);
+  *reinterpret_cast<uint2*>(a.out + (size_t)t * nq * D + (size_t)h * D + l4 * 4) = pk;
 }
 
 template <int D>
@@ -454,8 +459,9 @@ static hb_status launch_attention_d(const AttnArgs& a, stream_t s, void* const* 
     hipLaunchKernelGGL(attn_decode_kernel<D>, dim3((a.n_decode_items + 3) / 4, a.n_kv_heads), dim3(256), 0, st, a,
                        scale_log2);
   if (ev) hipEventRecord((hipEvent_t)ev[2], st);
-  const int64_t waves = (int64_t)a.n_tokens * a.n_q_heads;
-  hipLaunchKernelGGL(attn_merge_kernel<D>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, a);
+  const int64_t pairs = (int64_t)a.n_tokens * a.n_q_heads, per_block = 256 / (D / 4);
+  hipLaunchKernelGGL(attn_merge_kernel<D>, dim3((unsigned)((pairs + per_block - 1) / per_block)), dim3(256), 0, st,
+                     a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(HB_E_HIP, std::string("attention launch: ") + hipGetErrorString(e));
   return HB_OK;

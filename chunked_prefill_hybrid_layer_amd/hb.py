@@ -210,3 +210,47 @@ def layer_forward(dims: Dims, weights: Weights, blob: np.ndarray, meta_dev: int,
     _check(lib.hb_layer_forward(ctypes.byref(dims), ctypes.byref(weights), blob.ctypes.data_as(ctypes.c_void_p),
                                 meta_dev, rope_cs, int(rope_max_pos), x, y, k_cache, v_cache, workspace,
                                 int(workspace_bytes_), stream, ev))
+
+
+class Packer:
+    """hb_pack_metadata bound once to fixed input arrays and an output buffer,
+    so that a per-iteration call is one C call (the arrays may be refilled in
+    place between calls; their shapes must not change)."""
+
+    def __init__(self, dims: Dims, chunk_len, chunk_prefix, decode_ctx, block_table, num_pages: int,
+                 token_budget: int, out: np.ndarray):
+        self.arrays = [_i32(chunk_len), _i32(chunk_prefix), _i32(decode_ctx), _i32(block_table)]
+        cl, cp, dc, bt = self.arrays
+        self.dims, self.out = dims, out
+        self.need = ctypes.c_size_t(0)
+        self.ntok = ctypes.c_int32(0)
+        self.args = (ctypes.byref(dims), len(cl), _ptr(cl), _ptr(cp), len(dc), _ptr(dc), _ptr(bt), bt.shape[1],
+                     int(num_pages), int(token_budget), out.ctypes.data_as(ctypes.c_void_p), out.nbytes,
+                     ctypes.byref(self.need), ctypes.byref(self.ntok))
+
+    def __call__(self) -> int:
+        _check(lib.hb_pack_metadata(*self.args))
+        return self.need.value
+
+
+class Forward:
+    """hb_layer_forward bound once to its buffers; call(events) enqueues one
+    layer forward (events: None or a ctypes array from make_events)."""
+
+    def __init__(self, dims: Dims, weights: Weights, meta_host: np.ndarray, meta_dev: int, rope_cs: int,
+                 rope_max_pos: int, x: int, y: int, k_cache: int, v_cache: int, workspace: int,
+                 workspace_bytes_: int, stream: int = 0):
+        self.keep = (dims, weights, meta_host)
+        self.args = (ctypes.byref(dims), ctypes.byref(weights), meta_host.ctypes.data_as(ctypes.c_void_p),
+                     meta_dev, rope_cs, int(rope_max_pos), x, y, k_cache, v_cache, workspace, int(workspace_bytes_),
+                     stream)
+
+    def __call__(self, events=None):
+        _check(lib.hb_layer_forward(*self.args, events))
+
+
+def make_events(handles: Sequence[int]):
+    """ctypes array of NUM_STAGES + 1 hipEvent_t handles for Forward.__call__."""
+    if len(handles) != NUM_STAGES + 1:
+        raise ValueError(f"need {NUM_STAGES + 1} stage events")
+    return (ctypes.c_void_p * len(handles))(*handles)
