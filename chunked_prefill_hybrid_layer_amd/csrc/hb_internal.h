@@ -20,11 +20,8 @@ constexpr int kDecodeKvSplit = 256;   // keys per decode attention item (multipl
 constexpr int kPageSize = 16;
 constexpr int kMaxGroup = 16;         // decode path holds a kv group in one 16-row MFMA tile
 
-// --- GEMM tiling -------------------------------------------------------------
-constexpr int kGemmBM = 128;
-constexpr int kGemmBN = 128;
-constexpr int kGemmBK = 64;
-constexpr int kNumCU = 256;           // MI355X compute units (split-K sizing)
+// --- GEMM -------------------------------------------------------------------
+constexpr int kNumCU = 256;           // MI355X compute units (tile / split-K planning)
 
 inline int chunk_q_tile(int group) { return group >= kChunkRows ? 1 : kChunkRows / group; }
 
@@ -103,11 +100,11 @@ struct GemmArgs {
   // split-K partials [splits][M][N] fp32 (used when the plan splits K)
   float* part;
 };
-// Tile shape (waves along M: 2 -> 128-row tiles, 4 -> 256-row tiles) and
-// split-K factor the GEMM launcher uses for a problem; the QKV launch reduces
-// its own split, residual-mode callers reduce with launch_splitk_reduce.
+// Tile configuration (an index into the kernel's tile table) and split-K
+// factor the GEMM launcher uses for a problem; the QKV launch reduces its own
+// split, residual-mode callers reduce with launch_splitk_reduce.
 struct GemmPlan {
-  int wm, splits;
+  int tile, splits;
 };
 GemmPlan gemm_plan(int mode, int M, int N, int K);
 hb_status launch_gemm(const GemmArgs& g, stream_t s);
