@@ -423,3 +423,17 @@ def test_bf16_storage_points():
     assert not np.array_equal(O.round_bf16(r2.attn_out), r2.attn_out)
     # the two precisions agree to bf16 accuracy
     assert np.max(np.abs(r.y - r2.y)) < 0.05
+
+
+def test_row_block_evaluation_is_bit_identical():
+    """Large inputs of round_bf16 and rmsnorm are evaluated in row blocks on a
+    thread pool; each element (row) sees the same arithmetic, so the result is
+    bit-identical to the single-call evaluation."""
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((6000, 1024)) * np.exp(rng.uniform(-30, 30, (6000, 1)))
+    x[5, :7] = [0.0, -0.0, np.inf, -np.inf, 3.3895313892515355e38 * 1.001, 1e-45, np.nan]
+    a = O.round_bf16(x)
+    b = O._round_bf16(x)
+    assert np.array_equal(a, b, equal_nan=True)
+    g = rng.standard_normal(1024)
+    assert np.array_equal(O.rmsnorm(x[6:], g, 1e-5), O._rmsnorm(x[6:], g, 1e-5))
