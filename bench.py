@@ -12,6 +12,9 @@ copies of weights and KV pools are used in turn so that the 256 MB
 Infinity Cache cannot serve a step from the previous step's data.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py --sweep-tau      # token budget 128 .. 2048, one line per tau
+    python bench.py --kv-append      # hb_kv_append GB/s at T = 32768
+    python bench.py --long-prompt    # 32768-token prompt, 64 chunks of 512 vs unchunked
 """
 import argparse
 import hashlib
@@ -134,33 +137,18 @@ def cpu_baseline(wl, stride=4):
                       f"{b.n_tokens}) of the same batch, float64 numpy oracle, {dt:.1f} s"}
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="mistral_tau512")
-    ap.add_argument("--copies", type=int, default=4)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help="after the timed steps, copy 256 MiB device-to-device once (counter calibration)")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs the hybrid-batch layer on one GPU only; "
-                                   "--gpus above 1 is not supported (see the sharding note in DESIGN.md)"}))
-        sys.exit(2)
-
+def bench_batch(wl, name, steps, warmup, copies, calibrate_copy=False):
+    """Time `steps` layer steps over one fixed hybrid batch; returns the
+    result line (without cpu_baseline)."""
     import torch
     from chunked_prefill_hybrid_layer_amd import hb
     from chunked_prefill_hybrid_layer_amd.runtime import DeviceLayer, stream_handle
 
-    assert torch.cuda.is_available(), "bench needs a GPU"
-    wl = workload_by_name(args.workload)
     d, b = wl.dims, wl.batch
     T = b.n_tokens
     max_pos = int(np.max(b.cached_lengths() + b.new_lengths())) + 1
     layers = []
-    for _ in range(args.copies):
+    for _ in range(copies):
         L = DeviceLayer(d, wl.weights, b.num_pages, max_pos)
         L.fill_prefixes(b.block_table, range(b.n_seq), wl.prefix_k, wl.prefix_v)
         layers.append(L)
@@ -168,14 +156,13 @@ def main():
     x = torch.from_numpy(wl.x).cuda()
     y = torch.empty_like(x)
     # metadata: pinned host blobs and device blobs, double-buffered
-    size = hb.pack_metadata(hd, b.chunk_len, b.chunk_prefix, b.decode_ctx, b.block_table, b.num_pages,
-                            b.token_budget)[0].nbytes
+    blob0 = hb.pack_metadata(hd, b.chunk_len, b.chunk_prefix, b.decode_ctx, b.block_table, b.num_pages,
+                             b.token_budget)[0]
+    size = blob0.nbytes
     pin = [torch.empty(size, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
     pin_np = [p.numpy() for p in pin]
     dev = [torch.empty(size, dtype=torch.uint8, device="cuda") for _ in range(2)]
-    ws = torch.empty(hb.workspace_bytes(hd, hb.pack_metadata(hd, b.chunk_len, b.chunk_prefix, b.decode_ctx,
-                                                               b.block_table, b.num_pages, b.token_budget)[0]),
-                     dtype=torch.uint8, device="cuda")
+    ws = torch.empty(hb.workspace_bytes(hd, blob0), dtype=torch.uint8, device="cuda")
     stream = stream_handle()
     # per-step host work is one C call each for packing and for the forward
     packers = [hb.Packer(hd, b.chunk_len, b.chunk_prefix, b.decode_ctx, b.block_table, b.num_pages,
@@ -205,11 +192,11 @@ def main():
         fwds[i % len(layers)][j](events)
         consumed[j].record(compute)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     nst = hb.NUM_STAGES
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(steps)]
     for row in evs:            # torch creates the hipEvent on first record
         for e in row:
             e.record()
@@ -221,33 +208,34 @@ def main():
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record()
-    for i in range(args.steps):
-        step(args.warmup + i, ev_arrays[i])
+    for i in range(steps):
+        step(warmup + i, ev_arrays[i])
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms = t_start.elapsed_time(t_end) / args.steps
-    if args.calibrate_copy:
+    ms = t_start.elapsed_time(t_end) / steps
+    if calibrate_copy:
         src = torch.empty(64 << 20, dtype=torch.int32, device="cuda").fill_(1)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
+    step_ms = np.array([evs[i][0].elapsed_time(evs[i][nst]) for i in range(steps)])
     stage_ms = np.array([[evs[i][k].elapsed_time(evs[i][k + 1]) for k in range(nst)]
-                         for i in range(args.steps)])
+                         for i in range(steps)])
     stage_mean = stage_ms.mean(axis=0)
 
     model = stage_model(wl)
     stages = {}
     t_roof = 0.0
-    for k, name in enumerate(hb.STAGE_NAMES):
-        fl, by, bound = model[name]
+    for k, sname in enumerate(hb.STAGE_NAMES):
+        fl, by, bound = model[sname]
         t = float(stage_mean[k]) * 1e-3
         t_ideal = max(fl / (PEAK_BF16_TFLOPS * 1e12), by / (PEAK_HBM_GBS * 1e9))
         t_roof += t_ideal
-        stages[name] = {"ms": round(float(stage_mean[k]), 5), "tflops": round(fl / t / 1e12, 2) if t > 0 else None,
-                        "gbs": round(by / t / 1e9, 1) if t > 0 else None, "bound": bound,
-                        "roofline_frac": round(t_ideal / t, 4) if t > 0 else None}
+        stages[sname] = {"ms": round(float(stage_mean[k]), 5), "tflops": round(fl / t / 1e12, 2) if t > 0 else None,
+                         "gbs": round(by / t / 1e9, 1) if t > 0 else None, "bound": bound,
+                         "roofline_frac": round(t_ideal / t, 4) if t > 0 else None}
     dom = max(hb.STAGE_NAMES, key=lambda n: stages[n]["ms"])
     fl, by, bound = model[dom]
     tdom = stages[dom]["ms"] * 1e-3
@@ -257,35 +245,251 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": round(by / tdom / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = measured_traffic(dom, args.workload)
+    roof["traffic"] = measured_traffic(dom, name)
     roof["kernel"] = dom
     roof["per_launch"] = {"flops": fl, "bytes": by}
 
-    out = {
+    return {
         "metric": "hybrid-layer tokens/s at tau=512 (Mistral-7B-shaped layer) + % of MFMA/HBM roofline",
         "value": round(T / (ms * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": args.workload, "hidden": d.hidden, "n_q_heads": d.n_q_heads,
+        "config": {"workload": name, "hidden": d.hidden, "n_q_heads": d.n_q_heads,
                    "n_kv_heads": d.n_kv_heads, "head_dim": d.head_dim, "ffn_dim": d.ffn_dim,
                    "tokens": T, "chunks": [int(c) for c in b.chunk_len],
                    "chunk_prefix": [int(c) for c in b.chunk_prefix], "decodes": b.n_decodes,
                    "decode_ctx_mean": float(np.mean(b.decode_ctx)) if b.n_decodes else 0.0,
-                   "token_budget": b.token_budget, "page_size": d.page_size, "copies_rotated": args.copies},
+                   "token_budget": b.token_budget, "page_size": d.page_size, "copies_rotated": copies},
         "layer_iters_per_s": round(1e3 / ms, 1),
         "layer_roofline_frac": round(t_roof / (ms * 1e-3), 4),
+        "step_ms_p10_p50_p90": [round(float(np.percentile(step_ms, q)), 5) for q in (10, 50, 90)],
         "wall_s_timed": round(wall, 3),
         "roofline": roof,
         "stages": stages,
     }
+
+
+def sclk_mhz():
+    """Current shader clock as reported by rocm-smi (None if unavailable)."""
+    import subprocess
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                             timeout=20).stdout
+        rec = json.loads(out)
+        for card in rec.values():
+            for k, v in card.items():
+                if "sclk" in k.lower():
+                    return v
+    except Exception:
+        return None
+    return None
+
+
+TAU_SWEEP = (128, 256, 512, 1024, 2048)
+
+
+def sweep_tau(args):
+    """Token-budget sweep on the Mistral-7B-shaped layer: one chunk of tau-64
+    tokens (prefix 1792) + 64 decodes per point.  One line per tau, then a
+    summary with the GEMM stages' time per token against the weight-streaming
+    and MFMA bounds, which locates the compute/bandwidth knee."""
+    from chunked_prefill_hybrid_layer_amd import workloads as W
+    points = []
+    gemm = ("qkv_rope_append", "o_proj_residual", "gate_up_swiglu", "down_residual")
+    for tau in TAU_SWEEP:
+        wl = W.tau_sweep(tau, 0)
+        out = bench_batch(wl, f"tau_sweep_{tau}", args.steps, args.warmup, args.copies)
+        out["metric"] = "hybrid-layer tokens/s, token-budget sweep (Mistral-7B-shaped layer)"
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = cpu_baseline(wl, stride=max(4, tau // 64))
+        print(json.dumps(out), flush=True)
+        d = wl.dims
+        psi = d.hidden * (d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim + d.n_q_heads * d.head_dim * d.hidden + \
+            3 * d.hidden * d.ffn_dim
+        t_gemm = sum(out["stages"][g]["ms"] for g in gemm) * 1e-3
+        points.append({"tau": tau, "tokens_per_s": out["value"], "ms_per_step": out["ms_per_step"],
+                       "gemm_ms": round(t_gemm * 1e3, 4),
+                       "gemm_tflops": round(2 * tau * psi / t_gemm / 1e12, 1),
+                       "gemm_weight_gbs": round(2 * psi / t_gemm / 1e9, 1),
+                       "gemm_bound_ms": round(max(2 * psi / (PEAK_HBM_GBS * 1e9),
+                                                  2 * tau * psi / (PEAK_BF16_TFLOPS * 1e12)) * 1e3, 4)})
+    # algorithmic knee (bf16 weights): n* = bytes_w * FLOPS / (2 BW)
+    knee = 2 * PEAK_BF16_TFLOPS * 1e12 / (2 * PEAK_HBM_GBS * 1e9)
+    print(json.dumps({"metric": "tau sweep summary", "points": points,
+                      "knee_tokens_algorithmic": round(knee, 1)}), flush=True)
+
+
+def kv_append_bench(args, n_tokens=32768):
+    """hb_kv_append of one n_tokens-token prompt (prefix 0) into a shuffled page
+    pool: achieved GB/s over read + write of K and V."""
+    import torch
+    from chunked_prefill_hybrid_layer_amd import hb
+    from chunked_prefill_hybrid_layer_amd import workloads as W
+    from chunked_prefill_hybrid_layer_amd.runtime import DeviceLayer, stream_handle
+    d = W.MISTRAL
+    bt, num_pages = W.deal_block_tables(np.array([n_tokens]), d.page_size, np.random.default_rng(0))
+    hd = hb.make_dims(d)
+    blob, T = hb.pack_metadata(hd, [n_tokens], [0], [], bt, num_pages, n_tokens)
+    meta = torch.from_numpy(blob).cuda()
+    k = torch.randint(-2**15, 2**15, (T, d.n_kv_heads * d.head_dim), dtype=torch.int16, device="cuda")
+    v = torch.randint(-2**15, 2**15, (T, d.n_kv_heads * d.head_dim), dtype=torch.int16, device="cuda")
+    caches = []
+    for _ in range(2):
+        caches.append((torch.empty((num_pages, d.n_kv_heads, d.page_size, d.head_dim), dtype=torch.int16,
+                                   device="cuda"),
+                       torch.empty((num_pages, d.n_kv_heads, d.head_dim, d.page_size), dtype=torch.int16,
+                                   device="cuda")))
+    st = stream_handle()
+
+    def run(i):
+        kc, vc = caches[i & 1]
+        hb.kv_append(hd, blob, meta.data_ptr(), k.data_ptr(), v.data_ptr(), k.stride(0), kc.data_ptr(),
+                     vc.data_ptr(), st)
+
+    for i in range(args.warmup):
+        run(i)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        run(i)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / args.steps * 1e3
+    by = 2 * 2 * T * d.n_kv_heads * d.head_dim * 2       # K and V, read and write, bf16
+    print(json.dumps({"metric": "kv_append GB/s (one 32768-token prompt, Mistral-7B kv shape)",
+                      "value": round(by / us / 1e3, 1), "unit": "GB/s", "us_per_launch": round(us, 2),
+                      "bytes_per_launch": by, "tokens": T, "steps": args.steps, "warmup": args.warmup,
+                      "roofline": {"bound": "hbm", "achieved": round(by / us / 1e3, 1), "peak": PEAK_HBM_GBS,
+                                   "unit": "GB/s", "frac": round(by / us / 1e3 / PEAK_HBM_GBS, 4),
+                                   "traffic": None}}), flush=True)
+
+
+def long_prompt_bench(args):
+    """A 32768-token prompt as 64 chunks of 512 co-batched with 64 decodes,
+    against one unchunked 32768-token prefill: end-to-end time, the
+    attention stages' time (same (query, key) pairs in both), and agreement of
+    the prompt rows."""
+    import torch
+    from chunked_prefill_hybrid_layer_amd import hb
+    from chunked_prefill_hybrid_layer_amd import workloads as W
+    from chunked_prefill_hybrid_layer_amd.runtime import DeviceLayer
+    lp = W.long_prompt(0)
+    d, L, C = lp.dims, lp.prompt_len, lp.chunk
+    max_pos = int(max(L, int(np.max(lp.decode_ctx0)) + lp.n_iter)) + 1
+    nst = hb.NUM_STAGES
+
+    def events(n):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(n)]
+        for row in evs:
+            for e in row:
+                e.record()
+        torch.cuda.synchronize()
+        return evs, [hb.make_events([e.cuda_event for e in row]) for row in evs]
+
+    # chunked: metadata and inputs of all iterations staged on the device first
+    l1 = DeviceLayer(d, lp.weights, lp.num_pages, max_pos)
+    l1.fill_prefixes(lp.block_table, range(1, 1 + lp.n_dec), lp.prefix_k, lp.prefix_v)
+    preps, xs = [], []
+    for i in range(lp.n_iter):
+        b = lp.batch(i)
+        preps.append(l1.prepare(b.chunk_len, b.chunk_prefix, b.decode_ctx, b.block_table, b.token_budget))
+        xs.append(torch.from_numpy(lp.x(i)).cuda())
+    ys = [torch.empty_like(x) for x in xs]
+    ev_c, arr_c = events(lp.n_iter)
+
+    def chunked(ev=None):
+        for i in range(lp.n_iter):
+            l1.forward(preps[i], xs[i], ys[i], None if ev is None else ev[i])
+
+    chunked()                              # warm-up (rewrites the same K/V values)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    chunked(arr_c)
+    torch.cuda.synchronize()
+    wall_c = time.perf_counter() - t0
+    ms_c = ev_c[0][0].elapsed_time(ev_c[-1][nst])
+    st_c = np.array([[ev_c[i][k].elapsed_time(ev_c[i][k + 1]) for k in range(nst)] for i in range(lp.n_iter)])
+    y_chunk = torch.cat([y[:C] for y in ys]).cpu().numpy()
+    del xs, ys
+    torch.cuda.empty_cache()
+
+    l2 = DeviceLayer(d, lp.weights, lp.num_pages, max_pos)
+    ub = lp.unchunked_batch()
+    prep = l2.prepare(ub.chunk_len, ub.chunk_prefix, ub.decode_ctx, ub.block_table, ub.token_budget)
+    x = torch.from_numpy(lp.prompt_x).cuda()
+    y = torch.empty_like(x)
+    ev_u, arr_u = events(1)
+    l2.forward(prep, x, y)
+    torch.cuda.synchronize()
+    l2.forward(prep, x, y, arr_u[0])
+    torch.cuda.synchronize()
+    ms_u = ev_u[0][0].elapsed_time(ev_u[0][nst])
+    st_u = np.array([ev_u[0][k].elapsed_time(ev_u[0][k + 1]) for k in range(nst)])
+    y_full = y.cpu().numpy()
+    rel = float(np.linalg.norm(y_chunk.astype(np.float64) - y_full) / np.linalg.norm(y_full.astype(np.float64)))
+    mx = float(np.max(np.abs(y_chunk - y_full)))
+    names = list(hb.STAGE_NAMES)
+    ia = names.index("attn_chunk")
+    pairs = L * (L + 1) // 2
+    attn_c, attn_u = float(st_c[:, ia].sum()), float(st_u[ia])
+    print(json.dumps({
+        "metric": "long-prompt chunking: 32768-token prompt as 64 chunks of 512 (+64 decodes each) vs unchunked",
+        "chunked_ms_total": round(ms_c, 3), "chunked_ms_per_iteration": round(ms_c / lp.n_iter, 4),
+        "chunked_tokens_per_s": round(lp.n_iter * (C + lp.n_dec) / (ms_c * 1e-3), 1),
+        "chunked_wall_s": round(wall_c, 3),
+        "unchunked_ms": round(ms_u, 3), "unchunked_tokens_per_s": round(L / (ms_u * 1e-3), 1),
+        "prompt_attention_pairs": pairs,
+        "attn_chunk_ms": {"chunked_sum": round(attn_c, 3), "unchunked": round(attn_u, 3),
+                          "recompute_overhead": round(attn_c / attn_u - 1.0, 4),
+                          "chunked_tflops": round(4 * pairs * d.n_q_heads * d.head_dim / (attn_c * 1e-3) / 1e12, 1),
+                          "unchunked_tflops": round(4 * pairs * d.n_q_heads * d.head_dim / (attn_u * 1e-3) / 1e12, 1)},
+        "stage_ms": {n: {"chunked_sum": round(float(st_c[:, k].sum()), 3), "unchunked": round(float(st_u[k]), 3)}
+                     for k, n in enumerate(names)},
+        "prompt_rows_chunked_vs_unchunked": {"rel_l2": rel, "max_abs": mx},
+        "dtype": "bf16", "data": "synthetic", "n_gpus": 1}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mistral_tau512")
+    ap.add_argument("--copies", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the timed steps, copy 256 MiB device-to-device once (counter calibration)")
+    ap.add_argument("--sweep-tau", action="store_true", help="token-budget sweep, one line per tau")
+    ap.add_argument("--kv-append", action="store_true", help="hb_kv_append GB/s on a 32768-token prompt")
+    ap.add_argument("--long-prompt", action="store_true",
+                    help="32768-token prompt: 64 chunks of 512 with 64 decodes vs unchunked")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "the hybrid-batch layer runs on one GPU; --gpus above 1 is not supported "
+                                   "(data-parallel replicas would each run their own batches, weights and "
+                                   "KV pool with no exchange)"}))
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    if args.sweep_tau:
+        return sweep_tau(args)
+    if args.kv_append:
+        return kv_append_bench(args)
+    if args.long_prompt:
+        return long_prompt_bench(args)
+    wl = workload_by_name(args.workload)
+    out = bench_batch(wl, args.workload, args.steps, args.warmup, args.copies, args.calibrate_copy)
+    out["sclk_mhz"] = sclk_mhz()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(out), flush=True)

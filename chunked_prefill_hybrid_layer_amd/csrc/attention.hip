@@ -245,10 +245,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     for (int j = 0; j < NJ; ++j) acc[rb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
 
-  // the item's page ids (at most kChunkKvSplit / 16 = 64), staged once
-  __shared__ int pids[kChunkKvSplit / 16];
+  // The item's page ids, staged in LDS a window of 64 pages (16 key tiles) at
+  // a time, double-buffered: window w sits in pids[w & 1].  Window w + 1 is
+  // staged at the first tile of window w; the buffer it overwrites (window
+  // w - 1) was last read two iterations earlier, and its first reader comes
+  // after at least one barrier.
+  __shared__ int pids[2][64];
   const int npg = (it.key1 - it.key0 + 15) >> 4;
-  if (tid < npg) pids[tid] = bt[(it.key0 >> 4) + tid];
+#define STAGE_PIDS(W)                                                                         \
+  if (tid < 64 && (W) * 64 + tid < npg) pids[(W) & 1][tid] = bt[(it.key0 >> 4) + (W) * 64 + tid];
+  STAGE_PIDS(0);
   __syncthreads();
 
   // thread tid moves 16-byte chunk ci = tid + 256 u of the 4-page tile:
@@ -260,7 +266,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     const int pg = ci / (2 * D), within = ci % (2 * D);                                       \
     const int key_base = (KT) + pg * 16;                                                      \
     if (key_base < it.key1) {                                                                 \
-      const int page = pids[(key_base - it.key0) >> 4];                                       \
+      const int pi = (key_base - it.key0) >> 4;                                               \
+      const int page = pids[(pi >> 6) & 1][pi & 63];                                          \
       const size_t base = ((size_t)page * nkv + kvh) * PAGE + (size_t)within * 8;             \
       kr[u] = *reinterpret_cast<const uint4*>(a.k_cache + base);                              \
       vr[u] = *reinterpret_cast<const uint4*>(a.v_cache + base);                              \
@@ -296,6 +303,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   for (int ti = 0; ti < ntiles; ++ti) {
     const int kt = it.key0 + ti * 64;
     const int cur = ti & 1;
+    if ((ti & 15) == 0) STAGE_PIDS((ti >> 4) + 1);
     if (ti + 1 < ntiles) {
       CHUNK_GLOAD(kt + 64);
     }
@@ -386,6 +394,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   }
 #undef CHUNK_GLOAD
 #undef CHUNK_LSTORE
+#undef STAGE_PIDS
 
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {

@@ -52,46 +52,70 @@ hb_status launch_rmsnorm(const float* x, const uint16_t* gain, uint16_t* out, in
   return HB_OK;
 }
 
-// One thread per (token, kv head, 8-element chunk of d).
+// One wave per (append run, kv head): a run is up to 16 consecutive tokens
+// of one sequence landing in one page at consecutive slots (built by
+// hb_pack_metadata).  K rows go to consecutive slots of the page -- a
+// contiguous copy.  V is stored transposed in the page ([d][16 slots]), so
+// the run's V rows are staged in LDS and written back row by row of d: a
+// full page is one contiguous 4 KB block (two lanes per 32-byte d row), a
+// partial page writes only its own slots.
 template <int D>
 __global__ __launch_bounds__(256) void kv_append_kernel(const uint16_t* __restrict__ k,
                                                         const uint16_t* __restrict__ v, int64_t row_stride,
-                                                        const int32_t* __restrict__ slot, int n_tokens, int nkv,
-                                                        uint16_t* __restrict__ kc, uint16_t* __restrict__ vc) {
-  constexpr int CH = D / 8;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t total = (int64_t)n_tokens * nkv * CH;
-  if (idx >= total) return;
-  const int c = (int)(idx % CH);
-  const int h = (int)((idx / CH) % nkv);
-  const int t = (int)(idx / ((int64_t)CH * nkv));
-  const int sl = slot[t];
-  const int page = sl >> 4, off = sl & 15;
-  const size_t src = (size_t)t * row_stride + (size_t)h * D + c * 8;
-  const uint4 kk = *reinterpret_cast<const uint4*>(k + src);
-  const uint4 vv = *reinterpret_cast<const uint4*>(v + src);
-  const size_t pb = ((size_t)page * nkv + h) * (size_t)(16 * D);
-  *reinterpret_cast<uint4*>(kc + pb + (size_t)off * D + c * 8) = kk;
-  const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
-  uint16_t* vbase = vc + pb + (size_t)(c * 8) * 16 + off;
+                                                        const hb_append_run* __restrict__ runs, int n_runs,
+                                                        int nkv, uint16_t* __restrict__ kc,
+                                                        uint16_t* __restrict__ vc) {
+  constexpr int CPT = D / 8;  // 16-byte chunks per token row
+  __shared__ __align__(16) uint16_t vs[4][16 * D];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * 4 + wave;
+  const bool active = item < (int64_t)n_runs * nkv;
+  int n = 0, s0 = 0, tok0 = 0, h = 0;
+  size_t pb = 0;
+  if (active) {
+    const hb_append_run run = runs[item / nkv];
+    h = (int)(item % nkv);
+    n = run.n_tok;
+    tok0 = run.tok0;
+    s0 = run.slot0 & 15;
+    pb = ((size_t)(run.slot0 >> 4) * nkv + h) * (size_t)(16 * D);
+  }
+  for (int idx = lane; idx < n * CPT; idx += 64) {
+    const int i = idx / CPT, c = idx % CPT;
+    const size_t src = (size_t)(tok0 + i) * row_stride + (size_t)h * D + c * 8;
+    *reinterpret_cast<uint4*>(kc + pb + (size_t)(s0 + i) * D + c * 8) = *reinterpret_cast<const uint4*>(k + src);
+    *reinterpret_cast<uint4*>(&vs[wave][i * D + c * 8]) = *reinterpret_cast<const uint4*>(v + src);
+  }
+  __syncthreads();
+  for (int idx = lane; idx < 2 * D; idx += 64) {
+    const int dd = idx >> 1, hf = idx & 1;          // d row, first or second 8 slots
+    const int lo = max(s0, 8 * hf), hi = min(s0 + n, 8 * hf + 8);
+    if (lo >= hi) continue;
+    uint16_t* dst = vc + pb + (size_t)dd * 16 + 8 * hf;
+    if (lo == 8 * hf && hi == 8 * hf + 8) {
+      uint32_t w[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    vbase[(2 * e) * 16] = (uint16_t)(w[e] & 0xffff);
-    vbase[(2 * e + 1) * 16] = (uint16_t)(w[e] >> 16);
+      for (int j = 0; j < 4; ++j)
+        w[j] = (uint32_t)vs[wave][(8 * hf + 2 * j - s0) * D + dd] |
+               ((uint32_t)vs[wave][(8 * hf + 2 * j + 1 - s0) * D + dd] << 16);
+      *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+      for (int sl = lo; sl < hi; ++sl) dst[sl - 8 * hf] = vs[wave][(sl - s0) * D + dd];
+    }
   }
 }
 
 hb_status launch_kv_append(const hb_dims& d, const DevMeta& m, int n_tokens, const uint16_t* k,
                            const uint16_t* v, int64_t row_stride, uint16_t* kc, uint16_t* vc, stream_t s) {
-  if (n_tokens <= 0) return HB_OK;
-  const int64_t total = (int64_t)n_tokens * d.n_kv_heads * (d.head_dim / 8);
-  const unsigned blocks = (unsigned)((total + 255) / 256);
+  if (n_tokens <= 0 || m.n_append_runs <= 0) return HB_OK;
+  const int64_t items = (int64_t)m.n_append_runs * d.n_kv_heads;
+  const unsigned blocks = (unsigned)((items + 3) / 4);
   if (d.head_dim == 128)
     hipLaunchKernelGGL(kv_append_kernel<128>, dim3(blocks), dim3(256), 0, (hipStream_t)s, k, v, row_stride,
-                       m.slot, n_tokens, d.n_kv_heads, kc, vc);
+                       m.append_runs, m.n_append_runs, d.n_kv_heads, kc, vc);
   else
     hipLaunchKernelGGL(kv_append_kernel<64>, dim3(blocks), dim3(256), 0, (hipStream_t)s, k, v, row_stride,
-                       m.slot, n_tokens, d.n_kv_heads, kc, vc);
+                       m.append_runs, m.n_append_runs, d.n_kv_heads, kc, vc);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(HB_E_HIP, std::string("kv_append launch: ") + hipGetErrorString(e));
   return HB_OK;

@@ -14,10 +14,12 @@ namespace hb {
 // --- attention tiling (fixed by the kernels; recorded in the metadata) -----
 constexpr int kChunkRows = 128;       // (token, head) rows per chunk attention tile
 constexpr int kChunkKeyTile = 64;     // keys staged per step (4 pages of 16)
-constexpr int kChunkKvSplit = 1024;   // keys per chunk attention item (multiple of 64)
+constexpr int kChunkKvSplit = 1024;   // keys per chunk attention item, at least (multiple of 64)
+constexpr int kChunkItemsTarget = 2048;  // chunk items beyond which the key split doubles
 constexpr int kDecodeKeyStep = 32;    // keys per decode step (2 pages)
 constexpr int kDecodeKvSplit = 256;   // keys per decode attention item (multiple of 32)
 constexpr int kPageSize = 16;
+constexpr uint32_t kMetaVersion = 2;
 constexpr int kMaxGroup = 16;         // decode path holds a kv group in one 16-row MFMA tile
 
 // --- GEMM -------------------------------------------------------------------
@@ -60,6 +62,8 @@ struct DevMeta {            // device pointers into the copied metadata blob
   const int32_t* block_table;
   const hb_attn_item* chunk_items;
   const hb_attn_item* decode_items;
+  const hb_append_run* append_runs;
+  int n_append_runs;
 };
 DevMeta dev_meta(const hb_meta_header* h, const void* meta_dev);
 

@@ -27,6 +27,8 @@ DevMeta dev_meta(const hb_meta_header* h, const void* meta_dev) {
   m.block_table = (const int32_t*)(b + h->off_block_table);
   m.chunk_items = (const hb_attn_item*)(b + h->off_chunk_items);
   m.decode_items = (const hb_attn_item*)(b + h->off_decode_items);
+  m.append_runs = (const hb_append_run*)(b + h->off_append_runs);
+  m.n_append_runs = h->n_append_runs;
   return m;
 }
 

@@ -76,7 +76,7 @@ WsLayout ws_layout(const hb_dims& d, int T, int n_partials) {
 hb_status check_meta(const hb_dims* d, const void* meta_host) {
   if (!meta_host) return fail(HB_E_NULL, "meta_host is NULL");
   const hb_meta_header* h = (const hb_meta_header*)meta_host;
-  if (h->magic != HB_META_MAGIC || h->version != 1) return fail(HB_E_META, "bad metadata magic/version");
+  if (h->magic != HB_META_MAGIC || h->version != kMetaVersion) return fail(HB_E_META, "bad metadata magic/version");
   if (h->n_kv_heads != d->n_kv_heads || h->n_q_heads != d->n_q_heads || h->head_dim != d->head_dim ||
       h->page_size != d->page_size || h->group != d->n_q_heads / d->n_kv_heads)
     return fail(HB_E_META, "metadata was built for other dims");
@@ -116,9 +116,10 @@ size_t hb_meta_bytes(const hb_dims* dims, int32_t n_seq, int32_t n_tokens, int32
   size_t csplit = (max_keys + kChunkKvSplit - 1) / kChunkKvSplit;
   size_t dsplit = (max_keys + kDecodeKvSplit - 1) / kDecodeKvSplit;
   size_t items = tiles * csplit + S * dsplit;
+  size_t runs = T + S;                                           // a run per page a sequence touches
   size_t ints = (S + 1) + 3 * S + 5 * T + S * P;
-  return align_up(sizeof(hb_meta_header), 64) + align_up(ints * 4 + 16 * 8, 64) +
-         items * sizeof(hb_attn_item) + 64;
+  return align_up(sizeof(hb_meta_header), 64) + align_up(ints * 4 + 16 * 9, 64) +
+         items * sizeof(hb_attn_item) + runs * sizeof(hb_append_run) + 64;
 }
 
 hb_status hb_pack_metadata(const hb_dims* dims, int32_t n_chunks, const int32_t* chunk_len,
@@ -193,6 +194,15 @@ hb_status hb_pack_metadata(const hb_dims* dims, int32_t n_chunks, const int32_t*
       q_start[s + 1] = q_start[s] + newtok[s];
       kv_len[s] = cached[s] + newtok[s];
     }
+    // Keys per chunk item: kChunkKvSplit, doubled while the chunk tiles' keys
+    // would still make more than kChunkItemsTarget items, so that a long
+    // prompt does not multiply its partial results (and their merge).
+    int64_t chunk_keys = 0;
+    for (int s = 0; s < n_chunks; ++s)
+      for (int t0 = q_start[s]; t0 < q_start[s + 1]; t0 += qt)
+        chunk_keys += cached[s] + (t0 - q_start[s]) + std::min(qt, q_start[s + 1] - t0);
+    int csplit = kChunkKvSplit;
+    while ((int64_t)csplit * kChunkItemsTarget < chunk_keys && csplit < (1 << 20)) csplit *= 2;
     std::vector<int32_t> part_off((size_t)T), part_cnt((size_t)T);
     std::vector<hb_attn_item> citems, ditems;
     int64_t np = 0;
@@ -200,14 +210,14 @@ hb_status hb_pack_metadata(const hb_dims* dims, int32_t n_chunks, const int32_t*
       for (int t0 = q_start[s]; t0 < q_start[s + 1]; t0 += qt) {
         int n = std::min(qt, q_start[s + 1] - t0);
         int key_end = cached[s] + (t0 - q_start[s]) + n;  // last token's position + 1
-        int nsplit = (key_end + kChunkKvSplit - 1) / kChunkKvSplit;
+        int nsplit = (key_end + csplit - 1) / csplit;
         for (int j = 0; j < nsplit; ++j) {
           hb_attn_item it{};
           it.seq = s;
           it.tok0 = t0;
           it.n_tok = n;
-          it.key0 = j * kChunkKvSplit;
-          it.key1 = std::min(key_end, (j + 1) * kChunkKvSplit);
+          it.key0 = j * csplit;
+          it.key1 = std::min(key_end, (j + 1) * csplit);
           it.split = j;
           citems.push_back(it);
         }
@@ -237,6 +247,22 @@ hb_status hb_pack_metadata(const hb_dims* dims, int32_t n_chunks, const int32_t*
     }
     if (np >= ((int64_t)1 << 31)) return fail(HB_E_CAPACITY, "too many attention partials");
 
+    // KV append runs: each sequence's new tokens, cut where a page ends
+    std::vector<hb_append_run> runs;
+    for (int s = 0; s < S; ++s) {
+      const int32_t* row = block_table + (size_t)s * max_pages;
+      for (int t = q_start[s]; t < q_start[s + 1];) {
+        const int pos = cached[s] + (t - q_start[s]);
+        const int n = std::min(p - pos % p, q_start[s + 1] - t);
+        hb_append_run r{};
+        r.tok0 = t;
+        r.n_tok = n;
+        r.slot0 = row[pos / p] * p + pos % p;
+        runs.push_back(r);
+        t += n;
+      }
+    }
+
     // blob layout
     size_t off = align_up(sizeof(hb_meta_header), 64);
     auto take = [&](size_t bytes) {
@@ -246,7 +272,7 @@ hb_status hb_pack_metadata(const hb_dims* dims, int32_t n_chunks, const int32_t*
     };
     hb_meta_header h{};
     h.magic = HB_META_MAGIC;
-    h.version = 1;
+    h.version = kMetaVersion;
     h.n_seq = S;
     h.n_chunks = n_chunks;
     h.n_decodes = n_decodes;
@@ -260,11 +286,12 @@ hb_status hb_pack_metadata(const hb_dims* dims, int32_t n_chunks, const int32_t*
     h.head_dim = dims->head_dim;
     h.n_q_heads = dims->n_q_heads;
     h.chunk_q_tile = qt;
-    h.chunk_kv_split = kChunkKvSplit;
+    h.chunk_kv_split = csplit;
     h.decode_kv_split = kDecodeKvSplit;
     h.n_chunk_items = (int32_t)citems.size();
     h.n_decode_items = (int32_t)ditems.size();
     h.n_partials = (int32_t)np;
+    h.n_append_runs = (int32_t)runs.size();
     h.off_q_start = take((S + 1) * 4);
     h.off_cached = take(S * 4);
     h.off_kv_len = take(S * 4);
@@ -276,6 +303,7 @@ hb_status hb_pack_metadata(const hb_dims* dims, int32_t n_chunks, const int32_t*
     h.off_block_table = take((size_t)S * max_pages * 4);
     h.off_chunk_items = take(citems.size() * sizeof(hb_attn_item));
     h.off_decode_items = take(ditems.size() * sizeof(hb_attn_item));
+    h.off_append_runs = take(runs.size() * sizeof(hb_append_run));
     h.bytes = (int64_t)align_up(off, 64);
     *meta_bytes_out = (size_t)h.bytes;
     if (n_tokens_out) *n_tokens_out = (int32_t)T;
@@ -308,6 +336,7 @@ hb_status hb_pack_metadata(const hb_dims* dims, int32_t n_chunks, const int32_t*
     memcpy(arr(h.off_block_table), block_table, (size_t)S * max_pages * 4);
     if (!citems.empty()) memcpy(base + h.off_chunk_items, citems.data(), citems.size() * sizeof(hb_attn_item));
     if (!ditems.empty()) memcpy(base + h.off_decode_items, ditems.data(), ditems.size() * sizeof(hb_attn_item));
+    memcpy(base + h.off_append_runs, runs.data(), runs.size() * sizeof(hb_append_run));
     return HB_OK;
   } catch (const std::bad_alloc&) {
     return fail(HB_E_CAPACITY, "host allocation failed");

@@ -57,11 +57,13 @@ class MetaHeader(ctypes.Structure):
                 [(n, ctypes.c_int32) for n in
                  ("n_seq", "n_chunks", "n_decodes", "n_tokens", "page_size", "max_pages", "num_pages",
                   "max_kv_len", "n_kv_heads", "group", "head_dim", "n_q_heads", "chunk_q_tile",
-                  "chunk_kv_split", "decode_kv_split", "n_chunk_items", "n_decode_items", "n_partials")] +
+                  "chunk_kv_split", "decode_kv_split", "n_chunk_items", "n_decode_items", "n_partials",
+                  "n_append_runs", "reserved")] +
                 [("bytes", ctypes.c_int64)] +
                 [(n, ctypes.c_int64) for n in
                  ("off_q_start", "off_cached", "off_kv_len", "off_tok_seq", "off_tok_pos", "off_slot",
-                  "off_part_off", "off_part_cnt", "off_block_table", "off_chunk_items", "off_decode_items")])
+                  "off_part_off", "off_part_cnt", "off_block_table", "off_chunk_items", "off_decode_items",
+                  "off_append_runs")])
 
 
 EXPORTS = ["hb_meta_bytes", "hb_pack_metadata", "hb_rope_table", "hb_workspace_bytes", "hb_kv_append",
@@ -171,6 +173,13 @@ def attn_items(blob: np.ndarray, kind: str) -> np.ndarray:
     n = h.n_chunk_items if kind == "chunk" else h.n_decode_items
     off = h.off_chunk_items if kind == "chunk" else h.off_decode_items
     return np.frombuffer(blob, dtype=np.int32, count=8 * n, offset=off).reshape(n, 8).copy()
+
+
+def append_runs(blob: np.ndarray) -> np.ndarray:
+    """KV append runs as an int32 array [n_runs][4] = (tok0, n_tok, slot0, 0)."""
+    h = header(blob)
+    return np.frombuffer(blob, dtype=np.int32, count=4 * h.n_append_runs, offset=h.off_append_runs).reshape(
+        h.n_append_runs, 4).copy()
 
 
 def rope_table(dims: Dims, max_pos: int) -> np.ndarray:

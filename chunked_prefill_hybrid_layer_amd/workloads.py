@@ -313,3 +313,72 @@ def small(seed: int = 0, n_q: int = 8, n_kv: int = 2, head_dim: int = 128,
     d = Dims(hidden=hidden, n_q_heads=n_q, n_kv_heads=n_kv, head_dim=head_dim, ffn_dim=ffn)
     return build_workload(f"small_g{n_q // n_kv}_d{head_dim}", d, list(chunk_len), list(chunk_prefix),
                           list(decode_ctx), seed)
+
+
+@dataclass
+class LongPrompt:
+    """A long prompt run as successive chunks, each co-batched with the same
+    set of decodes (stall-free: every decode advances by one token per
+    iteration), next to the same prompt as one unchunked prefill."""
+    dims: Dims
+    weights: Dict[str, np.ndarray]
+    prompt_x: np.ndarray            # [L][H] float32, bf16-representable
+    chunk: int
+    decode_ctx0: np.ndarray         # [n_dec] contexts at iteration 0
+    decode_x: np.ndarray            # [n_iter][n_dec][H]
+    block_table: np.ndarray         # [1 + n_dec][max_pages]: the prompt, then the decodes
+    num_pages: int
+    prefix_k: list = field(default_factory=list)   # per sequence (the prompt's is empty)
+    prefix_v: list = field(default_factory=list)
+
+    @property
+    def prompt_len(self) -> int:
+        return int(self.prompt_x.shape[0])
+
+    @property
+    def n_iter(self) -> int:
+        return self.prompt_len // self.chunk
+
+    @property
+    def n_dec(self) -> int:
+        return len(self.decode_ctx0)
+
+    def batch(self, i: int) -> Batch:
+        """Iteration i: chunk i of the prompt (prefix i * chunk) + every decode."""
+        return Batch(np.array([self.chunk], np.int32), np.array([i * self.chunk], np.int32),
+                     (self.decode_ctx0 + i).astype(np.int32), self.block_table, self.num_pages,
+                     self.chunk + self.n_dec)
+
+    def x(self, i: int) -> np.ndarray:
+        return np.concatenate([self.prompt_x[i * self.chunk:(i + 1) * self.chunk], self.decode_x[i]])
+
+    def unchunked_batch(self) -> Batch:
+        L = self.prompt_len
+        return Batch(np.array([L], np.int32), np.array([0], np.int32), np.zeros(0, np.int32),
+                     np.ascontiguousarray(self.block_table[:1]), self.num_pages, L)
+
+
+def long_prompt(seed: int = 0, prompt_len: int = 32768, chunk: int = 512, n_dec: int = 64,
+                ctx_lo: int = 1024, ctx_hi: int = 8192, dims: Dims = None) -> LongPrompt:
+    """Long-prompt chunking on the Mistral-7B-shaped layer: a 32768-token
+    prompt as 64 chunks of 512, each co-batched with 64 decodes whose contexts
+    start uniform in [1024, 8192] and grow by one per iteration; x ~ N(0, 1)
+    (fresh decode inputs each iteration); decode prefixes N(0, 1) bf16."""
+    dims = MISTRAL if dims is None else dims
+    assert prompt_len % chunk == 0
+    rw, rx, rl, rb, rc, _ = _streams(seed)
+    n_iter = prompt_len // chunk
+    ctx0 = rl.integers(ctx_lo, ctx_hi + 1, size=n_dec).astype(np.int32)
+    kv_lens = np.concatenate([[prompt_len], ctx0.astype(np.int64) + n_iter])
+    bt, num_pages = deal_block_tables(kv_lens, dims.page_size, rb)
+    w = make_weights(dims, rw)
+    xs = np.random.SeedSequence(int(rx.integers(2**63))).spawn(2)
+    prompt_x = bf16_bits_to_f32(normal_bf16(xs[0], (prompt_len, dims.hidden), 1.0))
+    decode_x = bf16_bits_to_f32(normal_bf16(xs[1], (n_iter, n_dec, dims.hidden), 1.0))
+    lp = LongPrompt(dims, w, prompt_x, chunk, ctx0, decode_x, bt, num_pages)
+    children = np.random.SeedSequence(int(rc.integers(2**63))).spawn(n_dec)
+    kv = list(_pool().map(lambda j: synth_prefix(int(ctx0[j]), dims, children[j]), range(n_dec)))
+    empty = np.zeros((0, dims.n_kv_heads, dims.head_dim), np.uint16)
+    lp.prefix_k = [empty] + [k for k, _ in kv]
+    lp.prefix_v = [empty] + [v for _, v in kv]
+    return lp

@@ -107,6 +107,16 @@ typedef struct {
   int32_t reserved0, reserved1;
 } hb_attn_item;
 
+/* A run of consecutive packed tokens of one sequence whose K/V land in one
+ * page at consecutive slots: tokens [tok0, tok0 + n_tok) go to slots
+ * slot0 .. slot0 + n_tok - 1 (slot0 = page * page_size + first in-page slot). */
+typedef struct {
+  int32_t tok0;
+  int32_t n_tok;    /* 1 .. page_size */
+  int32_t slot0;
+  int32_t reserved;
+} hb_append_run;
+
 typedef struct {
   uint32_t magic;
   uint32_t version;
@@ -120,6 +130,8 @@ typedef struct {
   int32_t decode_kv_split;          /* keys per decode attention item */
   int32_t n_chunk_items, n_decode_items;
   int32_t n_partials;               /* attention partial results (sum of part_cnt) */
+  int32_t n_append_runs;            /* KV append runs (hb_append_run) */
+  int32_t reserved;
   int64_t bytes;                    /* size of the whole blob */
   /* byte offsets from the start of the blob */
   int64_t off_q_start;     /* int32 [n_seq + 1]  first packed token of each sequence */
@@ -133,6 +145,7 @@ typedef struct {
   int64_t off_block_table; /* int32 [n_seq][max_pages] copy of the caller's tables */
   int64_t off_chunk_items; /* hb_attn_item [n_chunk_items] */
   int64_t off_decode_items;/* hb_attn_item [n_decode_items] */
+  int64_t off_append_runs; /* hb_append_run [n_append_runs], in packed-token order */
 } hb_meta_header;
 
 /* Upper bound of the blob size for any batch of n_seq sequences, n_tokens

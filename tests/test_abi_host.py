@@ -94,6 +94,48 @@ def test_attention_work_lists_partition_keys(seed):
             assert a1 == b0
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_append_runs_cover_each_token_once_within_a_page(seed):
+    """The KV append runs list every packed token once, in order; a run stays
+    inside one page and its slots are consecutive and equal the tokens' own
+    slots."""
+    rng = np.random.default_rng(300 + seed)
+    cl, cp, dc, bt, npg = _random_batch(rng, int(rng.integers(0, 4)), int(rng.integers(1, 30)))
+    blob, T = _pack(W.TINY, cl, cp, dc, bt, npg)
+    runs = hb.append_runs(blob)
+    slot = hb.meta_array(blob, "slot")
+    assert runs[:, 0].tolist() == list(np.concatenate([[0], np.cumsum(runs[:, 1])[:-1]]))
+    assert int(runs[:, 1].sum()) == T and np.all(runs[:, 1] >= 1) and np.all(runs[:, 3] == 0)
+    for tok0, n, s0, _ in runs:
+        assert s0 % 16 + n <= 16
+        assert np.array_equal(slot[tok0:tok0 + n], s0 + np.arange(n))
+
+
+def test_long_prompt_widens_the_chunk_key_split():
+    """A 32768-token prompt in one chunk: the keys per chunk item grow past
+    the 1024 minimum (bounding the partial results), the items still cover
+    every token's keys exactly once, and a 512-token chunk keeps 1024."""
+    L = 32768
+    bt, npg = W.deal_block_tables(np.array([L]), 16, np.random.default_rng(1))
+    blob, T = _pack(W.MISTRAL, [L], [0], [], bt, npg)
+    h = hb.header(blob)
+    assert h.chunk_kv_split > 1024 and h.chunk_kv_split % 1024 == 0
+    items = hb.attn_items(blob, "chunk")
+    pcnt = hb.meta_array(blob, "part_cnt")
+    pos = hb.meta_array(blob, "tok_pos")
+    assert np.array_equal(pcnt, (pos + h.chunk_kv_split) // h.chunk_kv_split)
+    assert np.all(items[:, 4] - items[:, 3] <= h.chunk_kv_split)
+    # every (token, key) pair with key <= pos is covered exactly once: per tile, the
+    # split ranges tile [0, key_end) and each token masks keys beyond its position
+    for tok0 in np.unique(items[:, 1]):
+        r = items[items[:, 1] == tok0]
+        r = r[np.argsort(r[:, 5])]
+        assert r[0, 3] == 0 and np.all(r[1:, 3] == r[:-1, 4]) and r[-1, 4] == pos[tok0 + r[0, 2] - 1] + 1
+    bt2, npg2 = W.deal_block_tables(np.array([512 + 3000]), 16, np.random.default_rng(2))
+    blob2, _ = _pack(W.MISTRAL, [512], [3000], [], bt2, npg2)
+    assert hb.header(blob2).chunk_kv_split == 1024
+
+
 def test_worked_example_through_pack():
     g = json.load(open(os.path.join(ROOT, "tests", "golden", "worked_example_yi34b.json")))
     e = g["expected"]

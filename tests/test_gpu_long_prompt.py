@@ -1,0 +1,90 @@
+"""Long-prompt chunking on the GPU at full size (Mistral-7B-shaped layer): a
+32768-token prompt run as 64 chunks of 512, each co-batched with 64 decodes,
+against the same prompt as one unchunked prefill.  Chunked prefill computes
+exactly what the unchunked prefill computes ("Chunked Prefill", mechanism;
+"Sarathi-Serve reading notes" §3.1), so the prompt rows of both runs agree
+with each other and with the oracle, which evaluates sampled rows exactly
+(K/V for all 32768 tokens, then attention and FFN for the sample).  The
+decode rows of these iterations are not checked here (the tau = 512 and Yi
+full-size tests check decode rows against the oracle)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import hybrid_layer as O
+from chunked_prefill_hybrid_layer_amd import workloads as W
+from chunked_prefill_hybrid_layer_amd.runtime import DeviceLayer
+from tests.helpers import TOL_MAX_ABS, TOL_REL_L2, assert_close, errors, log
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_chunked(lp, layer):
+    L, C = lp.prompt_len, lp.chunk
+    y_prompt = np.empty((L, lp.dims.hidden), np.float32)
+    for i in range(lp.n_iter):
+        b = lp.batch(i)
+        prep = layer.prepare(b.chunk_len, b.chunk_prefix, b.decode_ctx, b.block_table, b.token_budget)
+        x = torch.from_numpy(lp.x(i)).cuda()
+        y = torch.empty_like(x)
+        layer.forward(prep, x, y)
+        y_prompt[i * C:(i + 1) * C] = y[:C].cpu().numpy()
+    torch.cuda.synchronize()
+    return y_prompt
+
+
+def test_long_prompt_chunked_matches_unchunked_and_oracle():
+    log("long prompt: generating the 32768-token workload")
+    lp = W.long_prompt(0)
+    d, L = lp.dims, lp.prompt_len
+    max_pos = int(max(L, int(np.max(lp.decode_ctx0)) + lp.n_iter)) + 1
+    log(f"long prompt: chunked run ({lp.n_iter} iterations of {lp.chunk} + {lp.n_dec} decodes)")
+    l1 = DeviceLayer(d, lp.weights, lp.num_pages, max_pos)
+    l1.fill_prefixes(lp.block_table, range(1, 1 + lp.n_dec), lp.prefix_k, lp.prefix_v)
+    y_chunked = _run_chunked(lp, l1)
+    log("long prompt: unchunked run")
+    l2 = DeviceLayer(d, lp.weights, lp.num_pages, max_pos)
+    ub = lp.unchunked_batch()
+    prep = l2.prepare(ub.chunk_len, ub.chunk_prefix, ub.decode_ctx, ub.block_table, ub.token_budget)
+    x = torch.from_numpy(lp.prompt_x).cuda()
+    y = torch.empty_like(x)
+    l2.forward(prep, x, y)
+    y_full = y.cpu().numpy()
+    del x, y
+    # Both runs approximate the same exact result with different summation
+    # groupings (attention key splits of 1024 vs 16384 keys, GEMM plans for
+    # 576 vs 32768 tokens), so they agree to the oracle tolerance.
+    rel, mx = errors(y_chunked, y_full)
+    log(f"long prompt: chunked vs unchunked over all {L} rows: rel_l2={rel:.3e} max_abs={mx:.3e}")
+    for lo, hi in ((0, 1024), (L // 2 - 512, L // 2 + 512), (L - 1024, L)):
+        r_, m_ = errors(y_chunked[lo:hi], y_full[lo:hi])
+        log(f"long prompt:   rows [{lo}, {hi}): rel_l2={r_:.3e} max_abs={m_:.3e}")
+    assert rel <= TOL_REL_L2 and mx <= TOL_MAX_ABS
+
+    # prompt K/V in the two caches: equal up to the bf16 rounding of the projections
+    k1, v1 = l1.cache_logical()
+    k2, v2 = l2.cache_logical()
+    pages = lp.block_table[0][:L // d.page_size]
+    for name, a, b in (("K", k1[pages], k2[pages]), ("V", v1[pages], v2[pages])):
+        diff = a != b
+        frac = float(diff.mean())
+        log(f"long prompt: prompt {name} cache, chunked vs unchunked: {frac * 100:.3f}% not bit-identical")
+        assert frac <= 0.01
+        fa, fb = O.bf16_bits_to_float(a[diff]), O.bf16_bits_to_float(b[diff])
+        assert np.all(np.isfinite(fa)) and np.all(np.isfinite(fb))
+        ulp = np.ldexp(1.0, np.frexp(np.maximum(np.abs(fa), np.abs(fb)))[1] - 8)
+        assert np.all(np.abs(fa - fb) <= ulp + 1e-3 * np.nanmax(np.abs(O.bf16_bits_to_float(a))))
+    del k1, v1, k2, v2, l1, l2
+    torch.cuda.empty_cache()
+
+    rng = np.random.default_rng(4)
+    spread = range(0, lp.n_iter, 9)
+    rows = sorted(set([i * lp.chunk for i in spread] + [i * lp.chunk + lp.chunk - 1 for i in spread] +
+                      [L - 1] + rng.choice(L, 8, replace=False).tolist()))
+    log(f"long prompt: oracle on {len(rows)} sampled rows (K/V for all {L} tokens)")
+    cache = O.PagedCache(lp.num_pages, d.n_kv_heads, d.page_size, d.head_dim)
+    r = O.layer_forward(d, O.weights_to_float(lp.weights), lp.prompt_x.astype(np.float64), [L], [0], [],
+                        np.ascontiguousarray(lp.block_table[:1]), cache, rows=rows)
+    assert r.pairs == sum(p + 1 for p in rows)
+    assert_close(y_full[rows], r.y, "unchunked vs oracle (sampled rows)")
+    assert_close(y_chunked[rows], r.y, "chunked vs oracle (sampled rows)")
