@@ -207,9 +207,12 @@ def bench_batch(wl, name, steps, warmup, copies, calibrate_copy=False):
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
+    host_s = np.zeros(steps)
     t_start.record()
     for i in range(steps):
+        h0 = time.perf_counter()
         step(warmup + i, ev_arrays[i])
+        host_s[i] = time.perf_counter() - h0
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -221,6 +224,7 @@ def bench_batch(wl, name, steps, warmup, copies, calibrate_copy=False):
         dst.copy_(src)
         torch.cuda.synchronize()
     step_ms = np.array([evs[i][0].elapsed_time(evs[i][nst]) for i in range(steps)])
+    gap_ms = np.array([evs[i][nst].elapsed_time(evs[i + 1][0]) for i in range(steps - 1)])
     stage_ms = np.array([[evs[i][k].elapsed_time(evs[i][k + 1]) for k in range(nst)]
                          for i in range(steps)])
     stage_mean = stage_ms.mean(axis=0)
@@ -271,6 +275,8 @@ def bench_batch(wl, name, steps, warmup, copies, calibrate_copy=False):
         "layer_iters_per_s": round(1e3 / ms, 1),
         "layer_roofline_frac": round(t_roof / (ms * 1e-3), 4),
         "step_ms_p10_p50_p90": [round(float(np.percentile(step_ms, q)), 5) for q in (10, 50, 90)],
+        "gap_between_steps_ms_p50": round(float(np.median(gap_ms)), 5) if len(gap_ms) else None,
+        "host_issue_ms_p50": round(float(np.median(host_s)) * 1e3, 4),
         "wall_s_timed": round(wall, 3),
         "roofline": roof,
         "stages": stages,
@@ -304,6 +310,8 @@ def sweep_tau(args):
     from chunked_prefill_hybrid_layer_amd import workloads as W
     points = []
     gemm = ("qkv_rope_append", "o_proj_residual", "gate_up_swiglu", "down_residual")
+    # a discarded first point: clocks settle during the first few hundred steps of a process
+    bench_batch(W.tau_sweep(TAU_SWEEP[0], 0), "warm-up", args.steps, args.warmup, 1)
     for tau in TAU_SWEEP:
         wl = W.tau_sweep(tau, 0)
         out = bench_batch(wl, f"tau_sweep_{tau}", args.steps, args.warmup, args.copies)

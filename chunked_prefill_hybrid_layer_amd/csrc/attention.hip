@@ -65,26 +65,29 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // loop unrolled by two).
 
 // Issue the K (4 x 16 B per page) and V^T (8 x 8 B per page) fragment loads of
-// the step starting at key KB into buffer set SFX.
+// the step starting at key KB into buffer set SFX.  With K stored in 32-dim
+// slices of the page, each K load instruction reads one contiguous 1 KB
+// block (16 keys x 32 dims) and each V^T load 16 dims x 16 keys (512 B); the
+// loads are nontemporal (the KV is read once).
 #define DEC_LOAD(KB, SFX)                                                                     \
   {                                                                                           \
     const int _j = ((KB) - it.key0) >> 4;                                                     \
     const bool _has1 = (KB) + 16 < it.key1;                                                   \
     const int _pg0 = __builtin_amdgcn_readlane(my_pg, _j);                                    \
     const int _pg1 = __builtin_amdgcn_readlane(my_pg, _has1 ? _j + 1 : _j);                   \
-    const uint16_t* _K0 = a.k_cache + ((size_t)_pg0 * nkv + kvh) * hs + r * D + qd * 8;       \
-    const uint16_t* _K1 = a.k_cache + ((size_t)_pg1 * nkv + kvh) * hs + r * D + qd * 8;       \
+    const uint16_t* _K0 = a.k_cache + ((size_t)_pg0 * nkv + kvh) * hs + r * 32 + qd * 8;      \
+    const uint16_t* _K1 = a.k_cache + ((size_t)_pg1 * nkv + kvh) * hs + r * 32 + qd * 8;      \
     const uint16_t* _V0 = a.v_cache + ((size_t)_pg0 * nkv + kvh) * hs + r * 16 + qd * 4;      \
     const uint16_t* _V1 = a.v_cache + ((size_t)_pg1 * nkv + kvh) * hs + r * 16 + qd * 4;      \
     _Pragma("unroll") for (int kk = 0; kk < KK; ++kk)                                         \
-        k0##SFX[kk] = *reinterpret_cast<const uint4*>(_K0 + kk * 32);                        \
+        k0##SFX[kk] = load_stream16(_K0 + kk * 512); \
     _Pragma("unroll") for (int jj = 0; jj < NJ; ++jj)                                         \
-        v0##SFX[jj] = *reinterpret_cast<const uint2*>(_V0 + jj * 256);                        \
+        v0##SFX[jj] = load_stream8(_V0 + jj * 256); \
     if (_has1) {                                                                              \
       _Pragma("unroll") for (int kk = 0; kk < KK; ++kk)                                       \
-          k1##SFX[kk] = *reinterpret_cast<const uint4*>(_K1 + kk * 32);                      \
+          k1##SFX[kk] = load_stream16(_K1 + kk * 512); \
       _Pragma("unroll") for (int jj = 0; jj < NJ; ++jj)                                       \
-          v1##SFX[jj] = *reinterpret_cast<const uint2*>(_V1 + jj * 256);                      \
+          v1##SFX[jj] = load_stream8(_V1 + jj * 256); \
     } else {                                                                                  \
       _Pragma("unroll") for (int kk = 0; kk < KK; ++kk) k1##SFX[kk] = make_uint4(0, 0, 0, 0); \
       _Pragma("unroll") for (int jj = 0; jj < NJ; ++jj) v1##SFX[jj] = make_uint2(0, 0);       \
@@ -284,7 +287,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   _Pragma("unroll") for (int u = 0; u < NLD; ++u) {                                           \
     const int ci = tid + 256 * u;                                                             \
     const int pg = ci / (2 * D), within = ci % (2 * D);                                       \
-    const int key = within / KCH, c = within % KCH;                                           \
+    /* K chunk `within` of the page block [D/32][16][32]: slot key, 8-dim chunk c */          \
+    const int key = (within >> 2) & 15, c = (within >> 6) * 4 + (within & 3);                \
     *reinterpret_cast<uint4*>(&Ks[BUF][(pg * 16 + key) * D + (c ^ (key & (KCH - 1))) * 8]) = kr[u]; \
     const int nvalid = it.key1 - ((KT) + pg * 16 + 8 * (within & 1));                         \
     const uint2 lo = keep_first(make_uint2(vr[u].x, vr[u].y), nvalid);                        \

@@ -5,8 +5,8 @@
 //
 // KV append ("Chunked Prefill", mechanism: each chunk writes its KV into the
 // paged blocks so the next chunk continues from it; "Sarathi-Serve reading
-// notes" §3.1): token t's K row goes to K[page][kvh][slot][:], its V row to
-// V[page][kvh][:][slot], page = slot[t] / 16, slot = slot[t] % 16.
+// notes" §3.1): dim i of token t's K row goes to K[page][kvh][i / 32][slot][i % 32],
+// its V row to V[page][kvh][:][slot], page = slot[t] / 16, slot = slot[t] % 16.
 
 #include "device_common.h"
 
@@ -54,8 +54,8 @@ hb_status launch_rmsnorm(const float* x, const uint16_t* gain, uint16_t* out, in
 
 // One wave per (append run, kv head): a run is up to 16 consecutive tokens
 // of one sequence landing in one page at consecutive slots (built by
-// hb_pack_metadata).  K rows go to consecutive slots of the page -- a
-// contiguous copy.  V is stored transposed in the page ([d][16 slots]), so
+// hb_pack_metadata).  K is stored in 32-dim slices of the page ([d/32][16][32]),
+// so each slice of the run's rows is a contiguous copy.  V is stored transposed in the page ([d][16 slots]), so
 // the run's V rows are staged in LDS and written back row by row of d: a
 // full page is one contiguous 4 KB block (two lanes per 32-byte d row), a
 // partial page writes only its own slots.
@@ -83,7 +83,9 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const uint16_t* __restri
   for (int idx = lane; idx < n * CPT; idx += 64) {
     const int i = idx / CPT, c = idx % CPT;
     const size_t src = (size_t)(tok0 + i) * row_stride + (size_t)h * D + c * 8;
-    *reinterpret_cast<uint4*>(kc + pb + (size_t)(s0 + i) * D + c * 8) = *reinterpret_cast<const uint4*>(k + src);
+    // K page block [D/32][16][32]: dims 8c..8c+7 of slot s0+i
+    *reinterpret_cast<uint4*>(kc + pb + (size_t)(c >> 2) * 512 + (size_t)(s0 + i) * 32 + (c & 3) * 8) =
+        *reinterpret_cast<const uint4*>(k + src);
     *reinterpret_cast<uint4*>(&vs[wave][i * D + c * 8]) = *reinterpret_cast<const uint4*>(v + src);
   }
   __syncthreads();

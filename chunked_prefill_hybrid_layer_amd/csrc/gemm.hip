@@ -114,9 +114,10 @@ __device__ __forceinline__ void qkv_store_pair(const GemmArgs& g, int m, int c, 
     } else {
       const int kvh = (c - qdim) / d;
       const int sl = g.slot[m];
-      uint16_t* kp = g.k_cache + (((size_t)(sl >> 4) * g.n_kv_heads + kvh) * 16 + (sl & 15)) * d + i;
-      kp[0] = y0;
-      kp[half] = y1;
+      // K page block: [d/32][16 slots][32]
+      uint16_t* kb = g.k_cache + ((size_t)(sl >> 4) * g.n_kv_heads + kvh) * 16 * d + (sl & 15) * 32;
+      kb[(i >> 5) * 512 + (i & 31)] = y0;
+      kb[((i + half) >> 5) * 512 + ((i + half) & 31)] = y1;
     }
   } else {
     const int kvh = (c - qdim - kdim) / d;

@@ -50,8 +50,9 @@ class DeviceLayer:
         self.w = {n: to_device_u16(weights[n], device) for n in WEIGHT_NAMES}
         self.hw = hb.Weights(*[self.w[n].data_ptr() for n in WEIGHT_NAMES])
         self.num_pages = int(num_pages)
-        self.k_cache = torch.full((self.num_pages, dims.n_kv_heads, dims.page_size, dims.head_dim), BF16_NAN,
-                                  dtype=torch.int16, device=device)
+        # K page blocks are [head_dim/32][page_size][32]; V page blocks [head_dim][page_size]
+        self.k_cache = torch.full((self.num_pages, dims.n_kv_heads, dims.head_dim // 32, dims.page_size, 32),
+                                  BF16_NAN, dtype=torch.int16, device=device)
         self.v_cache = torch.full((self.num_pages, dims.n_kv_heads, dims.head_dim, dims.page_size), BF16_NAN,
                                   dtype=torch.int16, device=device)
         self.rope_max_pos = int(rope_max_pos)
@@ -102,6 +103,17 @@ class DeviceLayer:
     # -- views for checking ---------------------------------------------------
     def cache_logical(self):
         """(K, V) as uint16 numpy arrays in logical order [page][kv][slot][d]."""
-        k = self.k_cache.cpu().numpy().view(np.uint16)
+        P, nkv, c, p, _ = self.k_cache.shape
+        k = self.k_cache.cpu().numpy().view(np.uint16).transpose(0, 1, 3, 2, 4).reshape(P, nkv, p, c * 32)
         v = self.v_cache.cpu().numpy().view(np.uint16).transpose(0, 1, 3, 2)
-        return k, np.ascontiguousarray(v)
+        return np.ascontiguousarray(k), np.ascontiguousarray(v)
+
+    def gather_kv(self, pages, slots):
+        """K and V rows at (page, slot) pairs as uint16 numpy arrays [n][kv][d]."""
+        pg = torch.as_tensor(np.asarray(pages), device=self.device)
+        sl = torch.as_tensor(np.asarray(slots), device=self.device)
+        k = self.k_cache[pg, :, :, sl, :]                       # [n][kv][d/32][32]
+        v = self.v_cache.permute(0, 1, 3, 2)[pg, :, sl, :]      # [n][kv][d]
+        n, nkv = k.shape[0], k.shape[1]
+        return (k.reshape(n, nkv, -1).cpu().numpy().view(np.uint16),
+                v.cpu().numpy().view(np.uint16))

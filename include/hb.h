@@ -24,7 +24,9 @@
  *     prompt; a decode with context C is one token at position C (C tokens are
  *     already cached; it attends C+1 keys, itself included).
  *   - KV cache (bf16), two separate device arrays, page size p = 16:
- *       K: [num_pages][n_kv_heads][p][head_dim]   (token-major inside a page)
+ *       K: [num_pages][n_kv_heads][head_dim/32][p][32]   (32-dim slices, each
+ *          token-major: dims 32c..32c+31 of a page's 16 tokens are one
+ *          contiguous 1 KB block)
  *       V: [num_pages][n_kv_heads][head_dim][p]   (dim-major inside a page)
  *     Position pos of sequence s lives in page block_table[s][pos / p] at
  *     in-page slot pos % p.  Unused block-table entries are -1 and are never

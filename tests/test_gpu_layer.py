@@ -231,10 +231,7 @@ def _full_size(wl, n_random, calibrate=False):
     assert_close(y[rows], r.y, f"{wl.name} sampled y", max_abs=bound)
     # every new K/V row: the GPU cache at the new slots against the oracle's
     slots = _new_slots(b)
-    pages = torch.tensor([p for p, _ in slots], device="cuda")
-    offs = torch.tensor([s for _, s in slots], device="cuda")
-    gk = layer.k_cache[pages, :, offs, :].cpu().numpy().view(np.uint16)     # [T][kv][d]
-    gv = layer.v_cache.permute(0, 1, 3, 2)[pages, :, offs, :].cpu().numpy().view(np.uint16)  # [T][kv][d]
+    gk, gv = layer.gather_kv([p for p, _ in slots], [s for _, s in slots])   # [T][kv][d] each
     ek = np.stack([cache.pages[p][0, :, sl, :] for p, sl in slots])
     ev = np.stack([cache.pages[p][1, :, sl, :] for p, sl in slots])
     for name, g, e in (("K", gk, ek), ("V", gv, ev)):
