@@ -60,9 +60,9 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 //
 // One step covers 32 keys (2 pages).  The item's page ids (at most 16: a
 // decode item spans at most kDecodeKvSplit = 256 keys) sit one per lane and
-// are broadcast with readlane, so no step waits on a block-table load.  K/V of
-// step j+1 are in flight while step j computes (two register buffers, the
-// loop unrolled by two).
+// are broadcast with readlane, so no step waits on a block-table load.  The
+// K/V of a step sit in one register buffer (138 VGPRs): three waves per SIMD
+// keep more bytes in flight than two double-buffered ones did (measured).
 
 // Issue the K (4 x 16 B per page) and V^T (8 x 8 B per page) fragment loads of
 // the step starting at key KB into buffer set SFX.  With K stored in 32-dim
@@ -146,7 +146,7 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
   }
 
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_decode_kernel(AttnArgs a, float scale_log2) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void attn_decode_kernel(AttnArgs a, float scale_log2) {
   constexpr int KK = D / 32;  // MFMA k-steps over the head dim
   constexpr int NJ = D / 16;  // 16-dim output blocks
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -174,20 +174,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   float m = -INFINITY, l = 0.f;
   const size_t hs = (size_t)16 * D;  // elements of one (page, kv head) block
 
-  uint4 k0A[KK], k1A[KK], k0B[KK], k1B[KK];
-  uint2 v0A[NJ], v1A[NJ], v0B[NJ], v1B[NJ];
-  int kb = it.key0;
-  DEC_LOAD(kb, A);
-  while (true) {
-    const int kbB = kb + 32;
-    if (kbB < it.key1) DEC_LOAD(kbB, B);
+  uint4 k0A[KK], k1A[KK];
+  uint2 v0A[NJ], v1A[NJ];
+  for (int kb = it.key0; kb < it.key1; kb += 32) {
+    DEC_LOAD(kb, A);
     DEC_COMPUTE(kb, A);
-    if (kbB >= it.key1) break;
-    const int kbA = kbB + 32;
-    if (kbA < it.key1) DEC_LOAD(kbA, A);
-    DEC_COMPUTE(kbB, B);
-    if (kbA >= it.key1) break;
-    kb = kbA;
   }
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
@@ -221,8 +212,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   __shared__ __align__(16) uint16_t Vs[2][4 * PAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const hb_attn_item it = a.meta.chunk_items[blockIdx.x];
-  const int kvh = blockIdx.y;
+  // kv head fastest: workgroups go round-robin over the 8 XCDs, so kv head h
+  // runs on XCD h mod 8 and the prefix K/V every query tile of that head
+  // re-reads stays in that XCD's L2
+  const hb_attn_item it = a.meta.chunk_items[blockIdx.x / a.n_kv_heads];
+  const int kvh = blockIdx.x % a.n_kv_heads;
   const int g = a.group, nq = a.n_q_heads, nkv = a.n_kv_heads;
   const int r = lane & 15, qd = lane >> 4;
   const int32_t* bt = a.meta.block_table + (size_t)it.seq * a.max_pages;
@@ -466,7 +460,8 @@ static hb_status launch_attention_d(const AttnArgs& a, stream_t s, void* const* 
   hipStream_t st = (hipStream_t)s;
   if (ev) hipEventRecord((hipEvent_t)ev[0], st);
   if (a.n_chunk_items > 0)
-    hipLaunchKernelGGL(attn_chunk_kernel<D>, dim3(a.n_chunk_items, a.n_kv_heads), dim3(256), 0, st, a, scale_log2);
+    hipLaunchKernelGGL(attn_chunk_kernel<D>, dim3((unsigned)a.n_chunk_items * a.n_kv_heads), dim3(256), 0, st, a,
+                       scale_log2);
   if (ev) hipEventRecord((hipEvent_t)ev[1], st);
   if (a.n_decode_items > 0)
     hipLaunchKernelGGL(attn_decode_kernel<D>, dim3((a.n_decode_items + 3) / 4, a.n_kv_heads), dim3(256), 0, st, a,
