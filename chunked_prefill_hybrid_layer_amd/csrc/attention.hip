@@ -420,7 +420,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 
 // ----------------------------------------------------------------------------
 // merge: o = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p over a token's
-// partials.  D/4 lanes per (token, head), each owning 4 consecutive dims.
+// partials, in one pass with a running maximum (the sums are rescaled when it
+// grows), four partials in flight at a time, in partial order (deterministic).
+// D/4 lanes per (token, head), each owning 4 consecutive dims.  A partial that
+// saw no key of its token has m = -inf and weight 0.
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   constexpr int LPH = D / 4;                 // lanes per (token, head)
@@ -431,22 +434,37 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   if (wid >= (int64_t)a.n_tokens * nq) return;
   const int t = (int)(wid / nq), h = (int)(wid % nq);
   const int p0 = a.meta.part_off[t], pc = a.meta.part_cnt[t];
-  const float* ml = a.part_ml + ((size_t)p0 * nq + h) * 2;
-  float M = -INFINITY;
-  for (int p = 0; p < pc; ++p) M = fmaxf(M, ml[(size_t)p * nq * 2]);
-  float L = 0.f;
-  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  const float2* ml = reinterpret_cast<const float2*>(a.part_ml) + (size_t)p0 * nq + h;
   const float* src = a.part_o + ((size_t)p0 * nq + h) * D + l4 * 4;
-  for (int p = 0; p < pc; ++p) {
-    const float mp = ml[(size_t)p * nq * 2], lp = ml[(size_t)p * nq * 2 + 1];
-    const float w = (mp == -INFINITY) ? 0.f : fast_exp2(mp - M);
-    L += w * lp;
-    const float4 v = *reinterpret_cast<const float4*>(src + (size_t)p * nq * D);
-    o.x += w * v.x;
-    o.y += w * v.y;
-    o.z += w * v.z;
-    o.w += w * v.w;
+  float M = -INFINITY, L = 0.f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#define MERGE_STEP(U)                                                                          \
+  {                                                                                            \
+    float2 mv[U];                                                                              \
+    float4 v[U];                                                                               \
+    _Pragma("unroll") for (int u = 0; u < U; ++u) {                                            \
+      mv[u] = ml[(size_t)(p + u) * nq];                                                        \
+      v[u] = *reinterpret_cast<const float4*>(src + (size_t)(p + u) * nq * D);                 \
+    }                                                                                          \
+    float mb = mv[0].x;                                                                        \
+    _Pragma("unroll") for (int u = 1; u < U; ++u) mb = fmaxf(mb, mv[u].x);                     \
+    const float mn = fmaxf(M, mb);                                                             \
+    if (mn != -INFINITY) {                                                                     \
+      const float sc = (M == -INFINITY) ? 0.f : fast_exp2(M - mn);                             \
+      L *= sc;                                                                                 \
+      o.x *= sc; o.y *= sc; o.z *= sc; o.w *= sc;                                              \
+      _Pragma("unroll") for (int u = 0; u < U; ++u) {                                          \
+        const float w = (mv[u].x == -INFINITY) ? 0.f : fast_exp2(mv[u].x - mn);                \
+        L += w * mv[u].y;                                                                      \
+        o.x += w * v[u].x; o.y += w * v[u].y; o.z += w * v[u].z; o.w += w * v[u].w;            \
+      }                                                                                        \
+      M = mn;                                                                                  \
+    }                                                                                          \
   }
+  int p = 0;
+  for (; p + 4 <= pc; p += 4) MERGE_STEP(4);
+  for (; p < pc; ++p) MERGE_STEP(1);
+#undef MERGE_STEP
   const float inv = 1.0f / L;
   uint2 pk;
   pk.x = pack2bf(o.x * inv, o.y * inv);

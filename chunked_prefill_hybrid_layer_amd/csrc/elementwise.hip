@@ -12,6 +12,10 @@
 
 namespace hb {
 
+// The row stays in registers between the sum of squares and the scaling:
+// up to kNormMaxChunks float4 per thread (hidden <= 256 * 4 * kNormMaxChunks).
+constexpr int kNormMaxChunks = 16;
+
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x,
                                                       const uint16_t* __restrict__ gain,
                                                       uint16_t* __restrict__ out, int hidden, float eps) {
@@ -19,10 +23,15 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
   const int row = blockIdx.x;
   const float4* xr = reinterpret_cast<const float4*>(x + (size_t)row * hidden);
   const int n4 = hidden >> 2;
+  float4 v[kNormMaxChunks];
   float ss = 0.f;
-  for (int i = threadIdx.x; i < n4; i += 256) {
-    float4 v = xr[i];
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+#pragma unroll
+  for (int k = 0; k < kNormMaxChunks; ++k) {
+    const int i = threadIdx.x + 256 * k;
+    if (i < n4) {
+      v[k] = xr[i];
+      ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
+    }
   }
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
@@ -31,21 +40,23 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
   const float r = 1.0f / sqrtf(total / (float)hidden + eps);
   uint2* orow = reinterpret_cast<uint2*>(out + (size_t)row * hidden);
   const uint2* g2 = reinterpret_cast<const uint2*>(gain);
-  for (int i = threadIdx.x; i < n4; i += 256) {
-    float4 v = xr[i];
-    uint2 gg = g2[i];
-    float g0 = bf2f((uint16_t)(gg.x & 0xffff)), g1 = bf2f((uint16_t)(gg.x >> 16));
-    float g2f = bf2f((uint16_t)(gg.y & 0xffff)), g3 = bf2f((uint16_t)(gg.y >> 16));
-    uint2 o;
-    o.x = pack2bf(v.x * r * g0, v.y * r * g1);
-    o.y = pack2bf(v.z * r * g2f, v.w * r * g3);
-    orow[i] = o;
+#pragma unroll
+  for (int k = 0; k < kNormMaxChunks; ++k) {
+    const int i = threadIdx.x + 256 * k;
+    if (i < n4) {
+      const uint2 gg = g2[i];
+      uint2 o;
+      o.x = pack2bf(v[k].x * r * bf2f((uint16_t)(gg.x & 0xffff)), v[k].y * r * bf2f((uint16_t)(gg.x >> 16)));
+      o.y = pack2bf(v[k].z * r * bf2f((uint16_t)(gg.y & 0xffff)), v[k].w * r * bf2f((uint16_t)(gg.y >> 16)));
+      orow[i] = o;
+    }
   }
 }
 
 hb_status launch_rmsnorm(const float* x, const uint16_t* gain, uint16_t* out, int rows, int hidden,
                          float eps, stream_t s) {
   if (rows <= 0) return HB_OK;
+  if (hidden > 256 * 4 * kNormMaxChunks) return fail(HB_E_SHAPE, "rmsnorm: hidden above 16384");
   hipLaunchKernelGGL(rmsnorm_kernel, dim3(rows), dim3(256), 0, (hipStream_t)s, x, gain, out, hidden, eps);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(HB_E_HIP, std::string("rmsnorm launch: ") + hipGetErrorString(e));

@@ -504,7 +504,10 @@ __global__ __launch_bounds__(TL::THREADS) void gemm_sub_kernel(GemmArgs g) {
 }
 
 // y[m][:] = res[m][:] + sum_z part[z][m][:] (z in order); with norm_out, also
-// norm_out[m][:] = bf16(y / sqrt(mean(y^2) + eps) * gain).  One workgroup per row.
+// norm_out[m][:] = bf16(y / sqrt(mean(y^2) + eps) * gain).  One workgroup per
+// row; the row stays in registers (N <= 256 * 4 * kReduceMaxChunks).
+constexpr int kReduceMaxChunks = 16;
+
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int splits,
                                                             const float* __restrict__ res, float* __restrict__ out,
                                                             int M, int N, const uint16_t* __restrict__ gain,
@@ -512,18 +515,23 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   __shared__ float red[4];
   const int m = blockIdx.x;
   const int n4 = N >> 2;
+  float4 v[kReduceMaxChunks];
   float ss = 0.f;
-  for (int i = threadIdx.x; i < n4; i += 256) {
-    float4 v = reinterpret_cast<const float4*>(res + (size_t)m * N)[i];
-    for (int z = 0; z < splits; ++z) {
-      const float4 p = reinterpret_cast<const float4*>(part + ((size_t)z * M + m) * N)[i];
-      v.x += p.x;
-      v.y += p.y;
-      v.z += p.z;
-      v.w += p.w;
+#pragma unroll
+  for (int k = 0; k < kReduceMaxChunks; ++k) {
+    const int i = threadIdx.x + 256 * k;
+    if (i < n4) {
+      v[k] = reinterpret_cast<const float4*>(res + (size_t)m * N)[i];
+      for (int z = 0; z < splits; ++z) {
+        const float4 p = reinterpret_cast<const float4*>(part + ((size_t)z * M + m) * N)[i];
+        v[k].x += p.x;
+        v[k].y += p.y;
+        v[k].z += p.z;
+        v[k].w += p.w;
+      }
+      reinterpret_cast<float4*>(out + (size_t)m * N)[i] = v[k];
+      ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
     }
-    reinterpret_cast<float4*>(out + (size_t)m * N)[i] = v;
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
   }
   if (!norm_out) return;
   ss = wave_sum(ss);
@@ -531,13 +539,16 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   __syncthreads();
   const float total = (red[0] + red[1]) + (red[2] + red[3]);
   const float rs = 1.0f / sqrtf(total / (float)N + eps);
-  for (int i = threadIdx.x; i < n4; i += 256) {
-    const float4 v = reinterpret_cast<const float4*>(out + (size_t)m * N)[i];
-    const uint2 gg = reinterpret_cast<const uint2*>(gain)[i];
-    uint2 o;
-    o.x = pack2bf(v.x * rs * bf2f((uint16_t)(gg.x & 0xffff)), v.y * rs * bf2f((uint16_t)(gg.x >> 16)));
-    o.y = pack2bf(v.z * rs * bf2f((uint16_t)(gg.y & 0xffff)), v.w * rs * bf2f((uint16_t)(gg.y >> 16)));
-    reinterpret_cast<uint2*>(norm_out + (size_t)m * N)[i] = o;
+#pragma unroll
+  for (int k = 0; k < kReduceMaxChunks; ++k) {
+    const int i = threadIdx.x + 256 * k;
+    if (i < n4) {
+      const uint2 gg = reinterpret_cast<const uint2*>(gain)[i];
+      uint2 o;
+      o.x = pack2bf(v[k].x * rs * bf2f((uint16_t)(gg.x & 0xffff)), v[k].y * rs * bf2f((uint16_t)(gg.x >> 16)));
+      o.y = pack2bf(v[k].z * rs * bf2f((uint16_t)(gg.y & 0xffff)), v[k].w * rs * bf2f((uint16_t)(gg.y >> 16)));
+      reinterpret_cast<uint2*>(norm_out + (size_t)m * N)[i] = o;
+    }
   }
 }
 
@@ -650,6 +661,7 @@ hb_status launch_gemm(const GemmArgs& g, stream_t s) {
 hb_status launch_splitk_reduce(const float* part, int splits, const float* res, float* out, int M, int N,
                                const uint16_t* gain, uint16_t* norm_out, float eps, stream_t s) {
   if (M <= 0) return HB_OK;
+  if (N > 256 * 4 * kReduceMaxChunks) return fail(HB_E_SHAPE, "split-K reduce: row above 16384");
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3(M), dim3(256), 0, (hipStream_t)s, part, splits, res, out, M, N, gain,
                      norm_out, eps);
   hipError_t e = hipGetLastError();

@@ -37,6 +37,7 @@ hb_status check_dims(const hb_dims* d) {
   if (d->hidden % 128 || d->ffn_dim % 128 || (d->n_q_heads * d->head_dim) % 128 ||
       (d->n_kv_heads * d->head_dim) % 128)
     return fail(HB_E_SHAPE, "hidden, ffn_dim, n_q*d and n_kv*d must be multiples of 128");
+  if (d->hidden > 16384) return fail(HB_E_SHAPE, "hidden above 16384");
   if (d->page_size != kPageSize) return fail(HB_E_SHAPE, "page_size must be 16");
   if (!(d->rms_eps >= 0.0f) || !(d->rope_theta > 0.0f)) return fail(HB_E_SHAPE, "bad eps or theta");
   return HB_OK;

@@ -70,7 +70,8 @@ typedef enum {
 
 /* Layer shape.  Supported: head_dim 64 or 128; n_q_heads % n_kv_heads == 0
  * with group g = n_q_heads / n_kv_heads <= 16; hidden, ffn_dim, n_q_heads *
- * head_dim and n_kv_heads * head_dim multiples of 128; page_size 16. */
+ * head_dim and n_kv_heads * head_dim multiples of 128; hidden <= 16384;
+ * page_size 16. */
 typedef struct {
   int32_t hidden;
   int32_t n_q_heads;

@@ -181,6 +181,8 @@ def test_pack_rejects_invalid_batches():
     assert _err(lambda: _pack(bad, [4], [0], [], np.array([[0]]), 1)) == "HB_E_SHAPE"
     bad = W.Dims(256, 34, 2, 64, 512)   # group 17
     assert _err(lambda: _pack(bad, [4], [0], [], np.array([[0]]), 1)) == "HB_E_SHAPE"
+    bad = W.Dims(16384 + 128, 4, 4, 64, 512)   # hidden above the row kernels' register budget
+    assert _err(lambda: _pack(bad, [4], [0], [], np.array([[0]]), 1)) == "HB_E_SHAPE"
     # a too-small buffer is reported, and nothing is written
     dims = hb.make_dims(d)
     with pytest.raises(hb.HbError) as ei:
