@@ -15,6 +15,7 @@ Infinity Cache cannot serve a step from the previous step's data.
     python bench.py --sweep-tau      # token budget 128 .. 2048, one line per tau
     python bench.py --kv-append      # hb_kv_append GB/s at T = 32768
     python bench.py --long-prompt    # 32768-token prompt, 64 chunks of 512 vs unchunked
+    python bench.py --chunk-sweep    # the same prompt alone at chunk sizes 128 .. 2048
 """
 import argparse
 import hashlib
@@ -115,26 +116,32 @@ def measured_traffic(stage, workload):
 
 def cpu_baseline(wl, stride=4):
     """The oracle (float64 numpy) on every `stride`-th packed token of the same
-    batch; K/V of all tokens are computed since the cache needs them."""
+    batch; K/V of all tokens are computed since the cache needs them, and the
+    cached prefixes of the sampled rows' sequences are loaded."""
     from oracle import hybrid_layer as O
     b = wl.batch
+    rows = np.arange(0, b.n_tokens, stride)
+    lay = O.token_layout(b.chunk_len, b.chunk_prefix, b.decode_ctx)
+    need = sorted(set(int(s) for s in lay.seq[rows]))
     cache = O.PagedCache(b.num_pages, wl.dims.n_kv_heads, wl.dims.page_size, wl.dims.head_dim)
-    for s in range(b.n_seq):
+    for s in need:
         if wl.prefix_k[s].shape[0]:
             cache.load_prefix(b.block_table, s, O.bf16_bits_to_float(wl.prefix_k[s]),
                               O.bf16_bits_to_float(wl.prefix_v[s]))
     w = O.weights_to_float(wl.weights)
-    rows = np.arange(0, b.n_tokens, stride)
     t0 = time.perf_counter()
     O.layer_forward(wl.dims, w, wl.x.astype(np.float64), b.chunk_len, b.chunk_prefix, b.decode_ctx,
                     b.block_table, cache, rows=rows)
     dt = time.perf_counter() - t0
-    threads = int(os.environ.get("OPENBLAS_NUM_THREADS") or os.environ.get("OMP_NUM_THREADS") or
-                  len(os.sched_getaffinity(0)))
-    threads = min(threads, len(os.sched_getaffinity(0)))
-    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": _oracle_threads(), "kind": "oracle",
             "sample": f"{len(rows)} of the {b.n_tokens} packed tokens (every {stride}th; K/V for all "
                       f"{b.n_tokens}) of the same batch, float64 numpy oracle, {dt:.1f} s"}
+
+
+def _oracle_threads():
+    threads = int(os.environ.get("OPENBLAS_NUM_THREADS") or os.environ.get("OMP_NUM_THREADS") or
+                  len(os.sched_getaffinity(0)))
+    return min(threads, len(os.sched_getaffinity(0)))
 
 
 def bench_batch(wl, name, steps, warmup, copies, calibrate_copy=False):
@@ -381,89 +388,163 @@ def kv_append_bench(args, n_tokens=32768):
                                    "traffic": None}}), flush=True)
 
 
+def _stage_events(n):
+    import torch
+    from chunked_prefill_hybrid_layer_amd import hb
+    nst = hb.NUM_STAGES
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(n)]
+    for row in evs:
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+    return evs, [hb.make_events([e.cuda_event for e in row]) for row in evs]
+
+
+def _run_chunked(lp, with_decodes=True):
+    """All iterations of a LongPrompt on a fresh layer, metadata and inputs
+    staged on the device first; one untimed pass, then a timed one.  Returns
+    (total ms, per-stage ms summed over iterations, prompt rows of y)."""
+    import torch
+    from chunked_prefill_hybrid_layer_amd import hb
+    from chunked_prefill_hybrid_layer_amd.runtime import DeviceLayer
+    d, C = lp.dims, lp.chunk
+    max_pos = int(max(lp.prompt_len, int(np.max(lp.decode_ctx0, initial=0)) + lp.n_iter)) + 1
+    layer = DeviceLayer(d, lp.weights, lp.num_pages, max_pos)
+    if lp.n_dec:
+        layer.fill_prefixes(lp.block_table, range(1, 1 + lp.n_dec), lp.prefix_k, lp.prefix_v)
+    preps, xs = [], []
+    for i in range(lp.n_iter):
+        b = lp.batch(i)
+        preps.append(layer.prepare(b.chunk_len, b.chunk_prefix, b.decode_ctx, b.block_table, b.token_budget))
+        xs.append(torch.from_numpy(lp.x(i)).cuda())
+    ys = [torch.empty_like(x) for x in xs]
+    ev, arr = _stage_events(lp.n_iter)
+    nst = hb.NUM_STAGES
+
+    def go(events=None):
+        for i in range(lp.n_iter):
+            layer.forward(preps[i], xs[i], ys[i], None if events is None else events[i])
+
+    go()                              # warm-up (rewrites the same K/V values)
+    torch.cuda.synchronize()
+    go(arr)
+    torch.cuda.synchronize()
+    ms = ev[0][0].elapsed_time(ev[-1][nst])
+    st = np.array([[ev[i][k].elapsed_time(ev[i][k + 1]) for k in range(nst)] for i in range(lp.n_iter)])
+    y = torch.cat([y[:C] for y in ys]).cpu().numpy()
+    del layer, xs, ys
+    torch.cuda.empty_cache()
+    return ms, st.sum(axis=0), y
+
+
+def _run_unchunked(lp):
+    import torch
+    from chunked_prefill_hybrid_layer_amd import hb
+    from chunked_prefill_hybrid_layer_amd.runtime import DeviceLayer
+    d, L = lp.dims, lp.prompt_len
+    layer = DeviceLayer(d, lp.weights, lp.num_pages, L + 1)
+    ub = lp.unchunked_batch()
+    prep = layer.prepare(ub.chunk_len, ub.chunk_prefix, ub.decode_ctx, ub.block_table, ub.token_budget)
+    x = torch.from_numpy(lp.prompt_x).cuda()
+    y = torch.empty_like(x)
+    ev, arr = _stage_events(1)
+    nst = hb.NUM_STAGES
+    layer.forward(prep, x, y)
+    torch.cuda.synchronize()
+    layer.forward(prep, x, y, arr[0])
+    torch.cuda.synchronize()
+    ms = ev[0][0].elapsed_time(ev[0][nst])
+    st = np.array([ev[0][k].elapsed_time(ev[0][k + 1]) for k in range(nst)])
+    out = y.cpu().numpy()
+    del layer, x, y
+    torch.cuda.empty_cache()
+    return ms, st, out
+
+
+def _long_prompt_cpu_baseline(lp, n_rows=24):
+    """Row-sampled oracle on the unchunked prompt: K/V of all its tokens, then
+    attention and FFN for n_rows rows spread over the prompt."""
+    from oracle import hybrid_layer as O
+    L = lp.prompt_len
+    rows = np.unique(np.linspace(0, L - 1, n_rows).astype(np.int64))
+    cache = O.PagedCache(lp.num_pages, lp.dims.n_kv_heads, lp.dims.page_size, lp.dims.head_dim)
+    w = O.weights_to_float(lp.weights)
+    t0 = time.perf_counter()
+    O.layer_forward(lp.dims, w, lp.prompt_x.astype(np.float64), [L], [0], [],
+                    np.ascontiguousarray(lp.block_table[:1]), cache, rows=rows)
+    dt = time.perf_counter() - t0
+    return {"value": len(rows) / dt, "unit": "tokens/s (row-sampled)", "cores": _oracle_threads(), "kind": "oracle",
+            "sample": f"{len(rows)} rows spread over the {L}-token prompt (K/V for all {L} tokens), float64 numpy "
+                      f"oracle, {dt:.1f} s; a full {L}-row oracle pass would take about "
+                      f"{dt * L / len(rows) / 3600:.1f} h at this rate (an upper bound: K/V are shared)"}
+
+
 def long_prompt_bench(args):
     """A 32768-token prompt as 64 chunks of 512 co-batched with 64 decodes,
     against one unchunked 32768-token prefill: end-to-end time, the
     attention stages' time (same (query, key) pairs in both), and agreement of
     the prompt rows."""
-    import torch
     from chunked_prefill_hybrid_layer_amd import hb
     from chunked_prefill_hybrid_layer_amd import workloads as W
-    from chunked_prefill_hybrid_layer_amd.runtime import DeviceLayer
     lp = W.long_prompt(0)
     d, L, C = lp.dims, lp.prompt_len, lp.chunk
-    max_pos = int(max(L, int(np.max(lp.decode_ctx0)) + lp.n_iter)) + 1
-    nst = hb.NUM_STAGES
-
-    def events(n):
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(n)]
-        for row in evs:
-            for e in row:
-                e.record()
-        torch.cuda.synchronize()
-        return evs, [hb.make_events([e.cuda_event for e in row]) for row in evs]
-
-    # chunked: metadata and inputs of all iterations staged on the device first
-    l1 = DeviceLayer(d, lp.weights, lp.num_pages, max_pos)
-    l1.fill_prefixes(lp.block_table, range(1, 1 + lp.n_dec), lp.prefix_k, lp.prefix_v)
-    preps, xs = [], []
-    for i in range(lp.n_iter):
-        b = lp.batch(i)
-        preps.append(l1.prepare(b.chunk_len, b.chunk_prefix, b.decode_ctx, b.block_table, b.token_budget))
-        xs.append(torch.from_numpy(lp.x(i)).cuda())
-    ys = [torch.empty_like(x) for x in xs]
-    ev_c, arr_c = events(lp.n_iter)
-
-    def chunked(ev=None):
-        for i in range(lp.n_iter):
-            l1.forward(preps[i], xs[i], ys[i], None if ev is None else ev[i])
-
-    chunked()                              # warm-up (rewrites the same K/V values)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    chunked(arr_c)
-    torch.cuda.synchronize()
-    wall_c = time.perf_counter() - t0
-    ms_c = ev_c[0][0].elapsed_time(ev_c[-1][nst])
-    st_c = np.array([[ev_c[i][k].elapsed_time(ev_c[i][k + 1]) for k in range(nst)] for i in range(lp.n_iter)])
-    y_chunk = torch.cat([y[:C] for y in ys]).cpu().numpy()
-    del xs, ys
-    torch.cuda.empty_cache()
-
-    l2 = DeviceLayer(d, lp.weights, lp.num_pages, max_pos)
-    ub = lp.unchunked_batch()
-    prep = l2.prepare(ub.chunk_len, ub.chunk_prefix, ub.decode_ctx, ub.block_table, ub.token_budget)
-    x = torch.from_numpy(lp.prompt_x).cuda()
-    y = torch.empty_like(x)
-    ev_u, arr_u = events(1)
-    l2.forward(prep, x, y)
-    torch.cuda.synchronize()
-    l2.forward(prep, x, y, arr_u[0])
-    torch.cuda.synchronize()
-    ms_u = ev_u[0][0].elapsed_time(ev_u[0][nst])
-    st_u = np.array([ev_u[0][k].elapsed_time(ev_u[0][k + 1]) for k in range(nst)])
-    y_full = y.cpu().numpy()
+    ms_c, st_c, y_chunk = _run_chunked(lp)
+    ms_u, st_u, y_full = _run_unchunked(lp)
     rel = float(np.linalg.norm(y_chunk.astype(np.float64) - y_full) / np.linalg.norm(y_full.astype(np.float64)))
     mx = float(np.max(np.abs(y_chunk - y_full)))
     names = list(hb.STAGE_NAMES)
     ia = names.index("attn_chunk")
     pairs = L * (L + 1) // 2
-    attn_c, attn_u = float(st_c[:, ia].sum()), float(st_u[ia])
-    print(json.dumps({
+    attn_c, attn_u = float(st_c[ia]), float(st_u[ia])
+    out = {
         "metric": "long-prompt chunking: 32768-token prompt as 64 chunks of 512 (+64 decodes each) vs unchunked",
         "chunked_ms_total": round(ms_c, 3), "chunked_ms_per_iteration": round(ms_c / lp.n_iter, 4),
         "chunked_tokens_per_s": round(lp.n_iter * (C + lp.n_dec) / (ms_c * 1e-3), 1),
-        "chunked_wall_s": round(wall_c, 3),
         "unchunked_ms": round(ms_u, 3), "unchunked_tokens_per_s": round(L / (ms_u * 1e-3), 1),
         "prompt_attention_pairs": pairs,
         "attn_chunk_ms": {"chunked_sum": round(attn_c, 3), "unchunked": round(attn_u, 3),
                           "recompute_overhead": round(attn_c / attn_u - 1.0, 4),
                           "chunked_tflops": round(4 * pairs * d.n_q_heads * d.head_dim / (attn_c * 1e-3) / 1e12, 1),
                           "unchunked_tflops": round(4 * pairs * d.n_q_heads * d.head_dim / (attn_u * 1e-3) / 1e12, 1)},
-        "stage_ms": {n: {"chunked_sum": round(float(st_c[:, k].sum()), 3), "unchunked": round(float(st_u[k]), 3)}
+        "stage_ms": {n: {"chunked_sum": round(float(st_c[k]), 3), "unchunked": round(float(st_u[k]), 3)}
                      for k, n in enumerate(names)},
         "prompt_rows_chunked_vs_unchunked": {"rel_l2": rel, "max_abs": mx},
-        "dtype": "bf16", "data": "synthetic", "n_gpus": 1}), flush=True)
+        "dtype": "bf16", "data": "synthetic", "n_gpus": 1}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = _long_prompt_cpu_baseline(lp)
+    print(json.dumps(out), flush=True)
+
+
+CHUNK_SWEEP = (128, 256, 512, 1024, 2048)
+
+
+def chunk_sweep_bench(args):
+    """The 32768-token prompt alone, chunked at C in 128 .. 2048, against the
+    unchunked prefill: the chunk-attention stage summed over the iterations
+    (identical (query, key) pairs at every C) and the whole prompt's time."""
+    from chunked_prefill_hybrid_layer_amd import hb
+    from chunked_prefill_hybrid_layer_amd import workloads as W
+    names = list(hb.STAGE_NAMES)
+    ia = names.index("attn_chunk")
+    base = W.long_prompt(0, n_dec=0)
+    ms_u, st_u, y_full = _run_unchunked(base)
+    attn_u = float(st_u[ia])
+    pts = []
+    for C in CHUNK_SWEEP:
+        lp = W.long_prompt(0, chunk=C, n_dec=0)
+        ms_c, st_c, y = _run_chunked(lp)
+        rel = float(np.linalg.norm(y.astype(np.float64) - y_full) / np.linalg.norm(y_full.astype(np.float64)))
+        pts.append({"chunk": C, "iterations": lp.n_iter, "prompt_ms": round(ms_c, 3),
+                    "attn_chunk_ms": round(float(st_c[ia]), 3),
+                    "recompute_overhead": round(float(st_c[ia]) / attn_u - 1.0, 4),
+                    "gemm_ms": round(float(sum(st_c[names.index(n)] for n in
+                                             ("qkv_rope_append", "o_proj_residual", "gate_up_swiglu",
+                                              "down_residual"))), 3),
+                    "rel_l2_vs_unchunked": rel})
+        print(json.dumps({"metric": "chunk-size sweep, 32768-token prompt", **pts[-1]}), flush=True)
+    print(json.dumps({"metric": "chunk-size sweep summary (32768-token prompt, Mistral-7B-shaped layer)",
+                      "unchunked_ms": round(ms_u, 3), "unchunked_attn_chunk_ms": round(attn_u, 3),
+                      "points": pts}), flush=True)
 
 
 def main():
@@ -480,6 +561,8 @@ def main():
     ap.add_argument("--kv-append", action="store_true", help="hb_kv_append GB/s on a 32768-token prompt")
     ap.add_argument("--long-prompt", action="store_true",
                     help="32768-token prompt: 64 chunks of 512 with 64 decodes vs unchunked")
+    ap.add_argument("--chunk-sweep", action="store_true",
+                    help="32768-token prompt alone at chunk sizes 128 .. 2048 vs unchunked")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "the hybrid-batch layer runs on one GPU; --gpus above 1 is not supported "
@@ -495,11 +578,13 @@ def main():
         return kv_append_bench(args)
     if args.long_prompt:
         return long_prompt_bench(args)
+    if args.chunk_sweep:
+        return chunk_sweep_bench(args)
     wl = workload_by_name(args.workload)
     out = bench_batch(wl, args.workload, args.steps, args.warmup, args.copies, args.calibrate_copy)
     out["sclk_mhz"] = sclk_mhz()
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl)
+        out["cpu_baseline"] = cpu_baseline(wl, stride=4 if b.n_tokens <= 1024 else 32)
     print(json.dumps(out), flush=True)
 
 

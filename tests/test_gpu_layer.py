@@ -184,14 +184,21 @@ def test_chunked_prefill_matches_unchunked_on_gpu():
             assert np.all(np.abs(fa - fb) <= ulp + 1e-3 * scale)
 
 
-@pytest.mark.parametrize("case", ["decodes_only", "one_token_chunk", "ctx0_only", "page_edge_chunks"])
+@pytest.mark.parametrize("case", ["decodes_only", "one_token_chunk", "ctx0_only", "page_edge_chunks",
+                                  "multi_token_decodes"])
 def test_layer_edge_cases(case):
+    """Edge cases of the batch layout.  multi_token_decodes: requests that
+    verify E drafted tokens at once ("Sarathi-Serve reading notes" §7.4,
+    speculative decoding) are chunks of E + 1 tokens whose prefix is the whole
+    context, next to plain decodes."""
     log(f"edge case {case}")
     kw = {
         "decodes_only": dict(chunk_len=(), chunk_prefix=(), decode_ctx=(1, 16, 17, 255, 256, 257, 999)),
         "one_token_chunk": dict(chunk_len=(1, 1), chunk_prefix=(0, 16), decode_ctx=(3,)),
         "ctx0_only": dict(chunk_len=(), chunk_prefix=(), decode_ctx=(0, 0, 0)),
         "page_edge_chunks": dict(chunk_len=(16, 17, 15, 129), chunk_prefix=(16, 15, 1, 1023), decode_ctx=()),
+        "multi_token_decodes": dict(chunk_len=(2, 4, 8, 4), chunk_prefix=(1000, 333, 17, 2045),
+                                    decode_ctx=(5, 1000, 2047)),
     }[case]
     wl = W.small(7, n_q=8, n_kv=2, head_dim=128, **kw)
     b = wl.batch
