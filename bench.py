@@ -584,7 +584,7 @@ def main():
     out = bench_batch(wl, args.workload, args.steps, args.warmup, args.copies, args.calibrate_copy)
     out["sclk_mhz"] = sclk_mhz()
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, stride=4 if b.n_tokens <= 1024 else 32)
+        out["cpu_baseline"] = cpu_baseline(wl, stride=4 if wl.batch.n_tokens <= 1024 else 32)
     print(json.dumps(out), flush=True)
 
 
