@@ -346,6 +346,44 @@ hb_status hb_pack_metadata(const hb_dims* dims, int32_t n_chunks, const int32_t*
   }
 }
 
+hb_status hb_schedule_iteration(int32_t token_budget, int32_t chunk_size, int32_t n_requests,
+                                const hb_request* requests, int32_t* chunk_req, int32_t* chunk_len,
+                                int32_t* chunk_prefix, int32_t* n_chunks_out, int32_t* decode_req,
+                                int32_t* decode_ctx, int32_t* n_decodes_out) {
+  if (!n_chunks_out || !n_decodes_out) return fail(HB_E_NULL, "schedule: NULL count output");
+  if (n_requests < 0 || token_budget < 1 || chunk_size < 1)
+    return fail(HB_E_SHAPE, "schedule: n_requests < 0, token_budget < 1 or chunk_size < 1");
+  if (n_requests > 0 && (!requests || !chunk_req || !chunk_len || !chunk_prefix || !decode_req || !decode_ctx))
+    return fail(HB_E_NULL, "schedule: NULL array");
+  for (int i = 0; i < n_requests; ++i)
+    if (requests[i].prompt_len < 1 || requests[i].cached < 0)
+      return fail(HB_E_LENGTH, "schedule: request " + std::to_string(i) + " has prompt_len < 1 or cached < 0");
+  int64_t n = 0;
+  int nd = 0, nc = 0;
+  // 1. decodes first: every request whose prompt is fully cached, one token each
+  for (int i = 0; i < n_requests && n < token_budget; ++i) {
+    if (requests[i].cached < requests[i].prompt_len) continue;
+    decode_req[nd] = i;
+    decode_ctx[nd] = requests[i].cached;
+    ++nd;
+    ++n;
+  }
+  // 2. then one chunk per prefilling request, in queue order, while budget remains
+  for (int i = 0; i < n_requests && n < token_budget; ++i) {
+    const int64_t remaining = (int64_t)requests[i].prompt_len - requests[i].cached;
+    if (remaining <= 0) continue;
+    const int64_t take = std::min<int64_t>(std::min<int64_t>(chunk_size, remaining), token_budget - n);
+    chunk_req[nc] = i;
+    chunk_len[nc] = (int32_t)take;
+    chunk_prefix[nc] = requests[i].cached;
+    ++nc;
+    n += take;
+  }
+  *n_chunks_out = nc;
+  *n_decodes_out = nd;
+  return HB_OK;
+}
+
 hb_status hb_rope_table(const hb_dims* dims, int32_t max_pos, float* host_out) {
   hb_status st = check_dims(dims);
   if (st != HB_OK) return st;

@@ -66,8 +66,12 @@ class MetaHeader(ctypes.Structure):
                   "off_append_runs")])
 
 
-EXPORTS = ["hb_meta_bytes", "hb_pack_metadata", "hb_rope_table", "hb_workspace_bytes", "hb_kv_append",
-           "hb_layer_forward", "hb_status_str", "hb_last_error_detail"]
+class Request(ctypes.Structure):
+    _fields_ = [("prompt_len", ctypes.c_int32), ("cached", ctypes.c_int32)]
+
+
+EXPORTS = ["hb_meta_bytes", "hb_pack_metadata", "hb_schedule_iteration", "hb_rope_table", "hb_workspace_bytes",
+           "hb_kv_append", "hb_layer_forward", "hb_status_str", "hb_last_error_detail"]
 
 
 def _load() -> ctypes.CDLL:
@@ -82,6 +86,9 @@ def _load() -> ctypes.CDLL:
     lib.hb_pack_metadata.argtypes = [ctypes.POINTER(Dims), I32, I32P, I32P, I32, I32P, I32P, I32, I32, I32,
                                      P, SZ, ctypes.POINTER(SZ), I32P]
     lib.hb_pack_metadata.restype = ctypes.c_int
+    lib.hb_schedule_iteration.argtypes = [I32, I32, I32, ctypes.POINTER(Request), I32P, I32P, I32P, I32P, I32P,
+                                          I32P, I32P]
+    lib.hb_schedule_iteration.restype = ctypes.c_int
     lib.hb_rope_table.argtypes = [ctypes.POINTER(Dims), I32, ctypes.POINTER(ctypes.c_float)]
     lib.hb_rope_table.restype = ctypes.c_int
     lib.hb_workspace_bytes.argtypes = [ctypes.POINTER(Dims), P]
@@ -173,6 +180,20 @@ def attn_items(blob: np.ndarray, kind: str) -> np.ndarray:
     n = h.n_chunk_items if kind == "chunk" else h.n_decode_items
     off = h.off_chunk_items if kind == "chunk" else h.off_decode_items
     return np.frombuffer(blob, dtype=np.int32, count=8 * n, offset=off).reshape(n, 8).copy()
+
+
+def schedule_iteration(token_budget: int, chunk_size: int, prompt_len, cached):
+    """hb_schedule_iteration over requests (prompt_len[i], cached[i]); returns
+    (chunk_req, chunk_len, chunk_prefix, decode_req, decode_ctx) as int32 arrays."""
+    n = len(prompt_len)
+    reqs = (Request * max(n, 1))(*[Request(int(p), int(c)) for p, c in zip(prompt_len, cached)])
+    outs = [np.zeros(max(n, 1), np.int32) for _ in range(5)]
+    nc, nd = ctypes.c_int32(0), ctypes.c_int32(0)
+    ptr = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    _check(lib.hb_schedule_iteration(int(token_budget), int(chunk_size), n, reqs, ptr(outs[0]), ptr(outs[1]),
+                                     ptr(outs[2]), ctypes.byref(nc), ptr(outs[3]), ptr(outs[4]), ctypes.byref(nd)))
+    c, d = nc.value, nd.value
+    return outs[0][:c], outs[1][:c], outs[2][:c], outs[3][:d], outs[4][:d]
 
 
 def append_runs(blob: np.ndarray) -> np.ndarray:

@@ -27,6 +27,17 @@ def stream_handle() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
+def schedule_batch(token_budget: int, chunk_size: int, prompt_len, cached, block_table: np.ndarray,
+                   num_pages: int):
+    """One stall-free iteration (hb_schedule_iteration) over requests with the
+    given prompt lengths and cached token counts, as the arguments of
+    hb_pack_metadata: returns (chunk_len, chunk_prefix, decode_ctx,
+    block-table rows in packed order, request index of each sequence)."""
+    cr, cl, cp, dr, dc = hb.schedule_iteration(token_budget, chunk_size, prompt_len, cached)
+    order = np.concatenate([cr, dr]).astype(np.int64)
+    return cl, cp, dc, np.ascontiguousarray(block_table[order]), order
+
+
 @dataclass
 class Prepared:
     """A hybrid batch's metadata on host and device."""

@@ -183,6 +183,36 @@ hb_status hb_pack_metadata(const hb_dims *dims, int32_t n_chunks, const int32_t 
                            void *meta_host, size_t meta_capacity, size_t *meta_bytes_out,
                            int32_t *n_tokens_out);
 
+/* ---------------------------------------------------------------------------
+ * Stall-free batch composition ("Sarathi-Serve reading notes" §3.4, the
+ * scheduling loop; §7.6, a worked iteration).  Host only, no HIP calls.
+ *
+ * A request is described by its prompt length and the number of its tokens
+ * already in the KV cache.  It is decoding once cached >= prompt_len (its next
+ * token sits at position `cached`), otherwise its prompt is being prefilled.
+ * One iteration takes, in this order:
+ *   1. every decoding request, one token each, in array order, while the
+ *      budget lasts (the pages add all decodes; more decodes than the budget
+ *      is a case they do not cover, and the later ones wait);
+ *   2. then, walking the prefilling requests in array order (the queue
+ *      order), one chunk each of min(chunk_size, prompt_len - cached,
+ *      budget left) tokens, until the budget is spent.
+ * Output, in hb_pack_metadata's sequence order: the chunks (request index,
+ * length, prefix = cached) then the decodes (request index, context =
+ * cached).  Output arrays hold n_requests entries each.  The caller advances
+ * each request's `cached` by what it was given after running the iteration.
+ * Errors: HB_E_NULL, HB_E_SHAPE (n_requests < 0, token_budget < 1,
+ * chunk_size < 1), HB_E_LENGTH (prompt_len < 1 or cached < 0). */
+typedef struct {
+  int32_t prompt_len;
+  int32_t cached;
+} hb_request;
+
+hb_status hb_schedule_iteration(int32_t token_budget, int32_t chunk_size, int32_t n_requests,
+                                const hb_request *requests, int32_t *chunk_req, int32_t *chunk_len,
+                                int32_t *chunk_prefix, int32_t *n_chunks_out, int32_t *decode_req,
+                                int32_t *decode_ctx, int32_t *n_decodes_out);
+
 /* Rotary table for positions 0..max_pos-1 (host only): host_out[pos][i][0..1]
  * = (cos, sin)(pos * theta^(-2i/head_dim)), i < head_dim/2, computed in double
  * and rounded to float.  host_out holds max_pos * head_dim floats. */

@@ -213,3 +213,67 @@ def test_workspace_size_covers_buffers():
     # plus fp32 split-K partials of at most 8 slices of the widest split projection
     split_max = 8 * T * max(d.qkv_dim, d.hidden) * 4
     assert floor <= need <= floor + split_max + 16 * 256
+
+
+def test_schedule_worked_example():
+    """The worked Yi-34B iteration ("Sarathi-Serve reading notes" §7.6): tau
+    2048, chunk 1024, six running decodes, R_A mid-prefill (4500-token prompt,
+    1024 cached), R_B new (800 tokens).  The batch takes the 6 decodes, R_A's
+    next 1024-token chunk and all of R_B: 1830 tokens; afterwards R_A has 2452
+    prompt tokens left and R_B decodes."""
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "worked_example_yi34b.json")))
+    e = g["expected"]
+    ra, rb = g["R_A"], g["R_B"]
+    ctx = [100, 250, 3000, 17, 64, 999]
+    prompt = [ra["prompt_len"], rb["prompt_len"]] + ctx
+    cached = [ra["cached_before"], rb["cached_before"]] + ctx
+    cr, cl, cp, dr, dc = hb.schedule_iteration(g["tau"], g["chunk_size"], prompt, cached)
+    assert list(dr) == [2, 3, 4, 5, 6, 7] and list(dc) == ctx
+    assert list(cr) == [0, 1] and list(cl) == [ra["chunk"], rb["chunk"]] and list(cp) == cached[:2]
+    assert int(cl.sum()) + len(dr) == e["total_tokens"]
+    after = np.array(cached)
+    after[cr] += cl
+    after[dr] += 1
+    assert prompt[0] - after[0] == e["R_A_remaining_prefill_after"] and after[1] == prompt[1]
+    assert prompt[0] - cached[0] == e["R_A_prefill_remaining_before"]
+    # the next iteration: R_B now decodes, R_A takes its next chunk
+    cr2, cl2, _, dr2, _ = hb.schedule_iteration(g["tau"], g["chunk_size"], prompt, after)
+    assert list(dr2) == [1, 2, 3, 4, 5, 6, 7] and list(cr2) == [0] and list(cl2) == [1024]
+
+
+def test_schedule_reproduces_the_long_prompt_iterations():
+    """Driving the 32768-token prompt and its 64 decodes through the
+    scheduler (tau = 512 + 64, chunk 512) gives exactly the hand-built
+    iterations: chunk i at prefix 512 i, every decode advancing by one."""
+    lp = W.long_prompt(0, n_dec=64)
+    prompt = np.concatenate([[lp.prompt_len], lp.decode_ctx0])
+    cached = np.concatenate([[0], lp.decode_ctx0]).astype(np.int64)
+    from chunked_prefill_hybrid_layer_amd.runtime import schedule_batch
+    for i in range(lp.n_iter):
+        cl, cp, dc, bt, order = schedule_batch(lp.chunk + lp.n_dec, lp.chunk, prompt, cached, lp.block_table,
+                                               lp.num_pages)
+        b = lp.batch(i)
+        assert np.array_equal(cl, b.chunk_len) and np.array_equal(cp, b.chunk_prefix)
+        assert np.array_equal(dc, b.decode_ctx) and np.array_equal(bt, b.block_table)
+        cached[order[:len(cl)]] += cl
+        cached[order[len(cl):]] += 1
+    assert cached[0] == lp.prompt_len
+
+
+def test_schedule_budget_edges_and_errors():
+    # more decodes than the budget: the first tau decode in array order, no chunk
+    cr, cl, cp, dr, dc = hb.schedule_iteration(3, 16, [5, 5, 5, 5, 100], [5, 6, 7, 8, 0])
+    assert list(dr) == [0, 1, 2] and len(cr) == 0
+    # the budget runs out inside the queue: the last chunk is cut, later requests wait
+    cr, cl, cp, dr, dc = hb.schedule_iteration(100, 64, [300, 50, 70, 9], [10, 0, 0, 9])
+    assert list(dr) == [3] and list(cr) == [0, 1] and list(cl) == [64, 35] and list(cp) == [10, 0]
+    # a chunk never passes its prompt's end
+    cr, cl, cp, dr, dc = hb.schedule_iteration(1000, 512, [700], [500])
+    assert list(cl) == [200]
+    # nothing to do
+    cr, cl, cp, dr, dc = hb.schedule_iteration(8, 8, [], [])
+    assert len(cr) == 0 and len(dr) == 0
+    assert _err(lambda: hb.schedule_iteration(0, 8, [4], [0])) == "HB_E_SHAPE"
+    assert _err(lambda: hb.schedule_iteration(8, 0, [4], [0])) == "HB_E_SHAPE"
+    assert _err(lambda: hb.schedule_iteration(8, 8, [0], [0])) == "HB_E_LENGTH"
+    assert _err(lambda: hb.schedule_iteration(8, 8, [4], [-1])) == "HB_E_LENGTH"

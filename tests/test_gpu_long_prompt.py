@@ -1,5 +1,6 @@
 """Long-prompt chunking on the GPU at full size (Mistral-7B-shaped layer): a
-32768-token prompt run as 64 chunks of 512, each co-batched with 64 decodes,
+32768-token prompt run as 64 chunks of 512, each co-batched with 64 decodes
+(the batches composed by the stall-free scheduler, hb_schedule_iteration),
 against the same prompt as one unchunked prefill.  Chunked prefill computes
 exactly what the unchunked prefill computes ("Chunked Prefill", mechanism;
 "Sarathi-Serve reading notes" §3.1), so the prompt rows of both runs agree
@@ -13,22 +14,36 @@ import torch
 
 from oracle import hybrid_layer as O
 from chunked_prefill_hybrid_layer_amd import workloads as W
-from chunked_prefill_hybrid_layer_amd.runtime import DeviceLayer
+from chunked_prefill_hybrid_layer_amd.runtime import DeviceLayer, schedule_batch
 from tests.helpers import TOL_MAX_ABS, TOL_REL_L2, assert_close, errors, log
 
 pytestmark = pytest.mark.gpu
 
 
 def _run_chunked(lp, layer):
+    """The iterations come from the stall-free scheduler (hb_schedule_iteration,
+    token budget = chunk + decodes): the prompt is request 0, the decodes
+    requests 1..n; each iteration's batch must be the configuration's."""
     L, C = lp.prompt_len, lp.chunk
+    prompt = np.concatenate([[L], lp.decode_ctx0])
+    cached = np.concatenate([[0], lp.decode_ctx0]).astype(np.int64)
     y_prompt = np.empty((L, lp.dims.hidden), np.float32)
-    for i in range(lp.n_iter):
+    i = 0
+    while cached[0] < L:
+        cl, cp, dc, bt, order = schedule_batch(C + lp.n_dec, C, prompt, cached, lp.block_table, lp.num_pages)
         b = lp.batch(i)
-        prep = layer.prepare(b.chunk_len, b.chunk_prefix, b.decode_ctx, b.block_table, b.token_budget)
-        x = torch.from_numpy(lp.x(i)).cuda()
+        assert np.array_equal(cl, b.chunk_len) and np.array_equal(cp, b.chunk_prefix)
+        assert np.array_equal(dc, b.decode_ctx) and np.array_equal(bt, b.block_table)
+        prep = layer.prepare(cl, cp, dc, bt, C + lp.n_dec)
+        x = torch.from_numpy(np.concatenate([lp.prompt_x[cp[0]:cp[0] + cl[0]],
+                                             lp.decode_x[i][order[len(cl):] - 1]])).cuda()
         y = torch.empty_like(x)
         layer.forward(prep, x, y)
-        y_prompt[i * C:(i + 1) * C] = y[:C].cpu().numpy()
+        y_prompt[cp[0]:cp[0] + cl[0]] = y[:cl[0]].cpu().numpy()
+        cached[order[:len(cl)]] += cl
+        cached[order[len(cl):]] += 1
+        i += 1
+    assert i == lp.n_iter
     torch.cuda.synchronize()
     return y_prompt
 
@@ -38,7 +53,7 @@ def test_long_prompt_chunked_matches_unchunked_and_oracle():
     lp = W.long_prompt(0)
     d, L = lp.dims, lp.prompt_len
     max_pos = int(max(L, int(np.max(lp.decode_ctx0)) + lp.n_iter)) + 1
-    log(f"long prompt: chunked run ({lp.n_iter} iterations of {lp.chunk} + {lp.n_dec} decodes)")
+    log(f"long prompt: chunked run ({lp.n_iter} scheduled iterations of {lp.chunk} + {lp.n_dec} decodes)")
     l1 = DeviceLayer(d, lp.weights, lp.num_pages, max_pos)
     l1.fill_prefixes(lp.block_table, range(1, 1 + lp.n_dec), lp.prefix_k, lp.prefix_v)
     y_chunked = _run_chunked(lp, l1)
