@@ -572,7 +572,7 @@ __global__ __launch_bounds__(256) void qkv_reduce_kernel(GemmArgs g, int splits)
 enum { kTile128 = 0, kTile256 = 1, kTileW256 = 2, kTileW224 = 3 };
 
 // Estimated time of one GEMM under a tile choice: rounds of tiles over the 256
-// CUs times the MFMA time of one tile at that tile's measured efficiency, plus
+// CUs times the MFMA time of one tile (plus its fill) at that tile's measured efficiency, plus
 // the split-K partials (written once, read once by the reduce; up to 128 MB
 // they stay in the 256 MB last-level cache, priced at 10 TB/s, else at 5).  Within 10 % of the
 // measured times on the Mistral-7B- and Yi-34B-shaped projections.
@@ -581,7 +581,8 @@ static double plan_cost(int M, int N, int K, int splits, double eff) {
   const double tiles = (double)((M + TL::BM - 1) / TL::BM) * (N / TL::BN) * splits;
   const double rounds = std::ceil(tiles / kNumCU);
   const double per_cu = 2.5e15 / kNumCU * eff;   // flop/s
-  const double t_tile = 2.0 * TL::BM * TL::BN * ((double)K / splits) / per_cu;
+  // each tile also pays its pipeline fill and epilogue, about 4 K steps of 64
+  const double t_tile = 2.0 * TL::BM * TL::BN * ((double)K / splits + 256.0) / per_cu;
   const double part_bytes = (double)splits * M * N * 4;
   const double t_part = splits > 1 ? 2.0 * part_bytes / (part_bytes <= 128e6 ? 10e12 : 5e12) : 0.0;
   return rounds * t_tile + t_part;
