@@ -201,219 +201,238 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
 
 // ----------------------------------------------------------------------------
 // chunk items
+//
+// One 256-thread workgroup per (item, kv head): up to 128 (token, head) rows,
+// 32 per wave, one 32-column block of v_mfma_f32_32x32x16_bf16.  Keys go in
+// tiles of 64 (4 pages).  Per tile:
+//   S^T = K Q^T   (2 key blocks of 32 x D/16 k-steps; Q stays in registers)
+//   online softmax on the 32 x 64 scores (lane l holds row l % 32 and 32 of
+//   its 64 keys; the other 32 sit in lane l ^ 32)
+//   O^T += V^T P^T (D/32 dim blocks x 4 key steps of 16), P as bf16.
+//
+// K/V reach LDS with direct-to-LDS loads (global_load_lds_dwordx4): wave w
+// moves page w of the tile, D/32 1 KB loads each of K and V, double-buffered
+// over tiles with one barrier per tile.  Each lane's global address is chosen
+// so that the LDS image comes out XOR-swizzled on 16-byte chunks:
+//   K image [page 4][slice D/32][slot 16][32 dims]: the cache's own page layout;
+//     chunk c of slot t's 64-byte row sits at c ^ kswz(t).
+//   V image [page 4][dim D][16 keys]: the cache's own (dim-major) page layout;
+//     half h (keys 8h..8h+7) of dim row d sits at h ^ ((d >> 2) & 1).
+// Both fragment reads are ds_read_b128 without bank conflicts.
+//
+// Key order.  The rows of the QK MFMA are a permutation of the 32 keys of a
+// block: MFMA row i is key kperm(i).  With it, the 16 scores lane l receives
+// for a block are keys 16 (v >> 3) + 8 (l >> 5) + (v & 7), v = 0..15: eight
+// consecutive keys per half.  These are exactly the 8 consecutive keys the PV
+// MFMA wants in lane l, so P goes from the score registers into the PV
+// operand with no data movement, and each V^T fragment is one 16-byte read.
+//
+// Keys at or past the item's end (a partly used last page, pages past the
+// item) are masked to -inf in S; their V entries in LDS are zeroed on the
+// item's last tile, since a stale or poisoned value times a zero weight would
+// still be NaN.  The weight sum l adds the bf16 probabilities the PV product
+// uses, so numerator and denominator carry the same rounding.
+
+__device__ __forceinline__ int kswz(int t) { return ((t >> 1) & 1) | ((t >> 2) & 2); }
+__device__ __forceinline__ int kperm(int i) {
+  return 16 * (i >> 4) + 8 * ((i >> 2) & 1) + 4 * ((i >> 3) & 1) + (i & 3);
+}
+
+__device__ __forceinline__ uint4 keep_first8(uint4 v, int n) {
+  // keep the first n (0..8) bf16 values of an 8-value vector, zero the rest
+  const uint2 lo = keep_first(make_uint2(v.x, v.y), n);
+  const uint2 hi = keep_first(make_uint2(v.z, v.w), n - 4);
+  return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_chunk_kernel(AttnArgs a, float scale_log2) {
-  constexpr int KK = D / 32;
-  constexpr int NJ = D / 16;
-  constexpr int KCH = D / 8;      // 16-byte chunks per K row
+  constexpr int NS = D / 32;      // 32-dim K slices per page = 1 KB V blocks per page = PV dim blocks
+  constexpr int KS = D / 16;      // QK k-steps
   constexpr int PAGE = 16 * D;    // elements per (page, kv head) block
-  constexpr int NLD = D / 32;     // 16-byte chunks each thread moves per operand per tile
-  __shared__ __align__(16) uint16_t Ks[2][4 * PAGE];
-  __shared__ __align__(16) uint16_t Vs[2][4 * PAGE];
+  constexpr int TILE = 4 * PAGE;  // elements of K (or of V) per 64-key tile
+  __shared__ __align__(1024) uint16_t lds[2][2 * TILE];  // [stage][K image | V image]
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // kv head fastest: workgroups go round-robin over the 8 XCDs, so kv head h
   // runs on XCD h mod 8 and the prefix K/V every query tile of that head
   // re-reads stays in that XCD's L2
   const hb_attn_item it = a.meta.chunk_items[blockIdx.x / a.n_kv_heads];
   const int kvh = blockIdx.x % a.n_kv_heads;
   const int g = a.group, nq = a.n_q_heads, nkv = a.n_kv_heads;
-  const int r = lane & 15, qd = lane >> 4;
-  const int32_t* bt = a.meta.block_table + (size_t)it.seq * a.max_pages;
-
-  bf16x8 qf[2][KK];
-  int rpos[2];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int row = wave * 32 + rb * 16 + r;
-    const int tl = row / g, hq = row - tl * g;
-    const bool valid = tl < it.n_tok;
-    const int t = it.tok0 + tl;
-    rpos[rb] = valid ? a.meta.tok_pos[t] : -1;
-    const uint16_t* qrow = a.q + (size_t)t * nq * D + (size_t)(kvh * g + hq) * D + qd * 8;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-      qf[rb][kk] = valid ? as_bf16x8(*reinterpret_cast<const uint4*>(qrow + kk * 32)) : as_bf16x8(make_uint4(0, 0, 0, 0));
-  }
-  f32x4 acc[2][NJ];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) acc[rb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
-
-  // The item's page ids, staged in LDS a window of 64 pages (16 key tiles) at
-  // a time, double-buffered: window w sits in pids[w & 1].  Window w + 1 is
-  // staged at the first tile of window w; the buffer it overwrites (window
-  // w - 1) was last read two iterations earlier, and its first reader comes
-  // after at least one barrier.
-  __shared__ int pids[2][64];
+  const int col = lane & 31, hh = lane >> 5;
+  const int32_t* bt = a.meta.block_table + (size_t)it.seq * a.max_pages + (it.key0 >> 4);
   const int npg = (it.key1 - it.key0 + 15) >> 4;
-#define STAGE_PIDS(W)                                                                         \
-  if (tid < 64 && (W) * 64 + tid < npg) pids[(W) & 1][tid] = bt[(it.key0 >> 4) + (W) * 64 + tid];
-  STAGE_PIDS(0);
-  __syncthreads();
+  const int ntiles = (it.key1 - it.key0 + 63) >> 6;
 
-  // thread tid moves 16-byte chunk ci = tid + 256 u of the 4-page tile:
-  // page ci / (2 D), chunk `within` = ci % (2 D) of that (page, kv head) block
-  uint4 kr[NLD], vr[NLD];
-#define CHUNK_GLOAD(KT)                                                                       \
-  _Pragma("unroll") for (int u = 0; u < NLD; ++u) {                                           \
-    const int ci = tid + 256 * u;                                                             \
-    const int pg = ci / (2 * D), within = ci % (2 * D);                                       \
-    const int key_base = (KT) + pg * 16;                                                      \
-    if (key_base < it.key1) {                                                                 \
-      const int pi = (key_base - it.key0) >> 4;                                               \
-      const int page = pids[(pi >> 6) & 1][pi & 63];                                          \
-      const size_t base = ((size_t)page * nkv + kvh) * PAGE + (size_t)within * 8;             \
-      kr[u] = *reinterpret_cast<const uint4*>(a.k_cache + base);                              \
-      vr[u] = *reinterpret_cast<const uint4*>(a.v_cache + base);                              \
-    } else {                                                                                  \
-      kr[u] = make_uint4(0, 0, 0, 0);                                                         \
-      vr[u] = make_uint4(0, 0, 0, 0);                                                         \
-    }                                                                                         \
-  }
-  // K rows go to Ks swizzled by key; V^T chunk `within` holds dim within / 2,
-  // keys 8 (within & 1) .. +7 of its page: values past the item's last key are
-  // zeroed (the cache may hold poison there), and each 4-key group is placed at
-  // group ^ ((dim >> 2) & 3): the PV fragment reads (ds_read_b64) then have no bank conflicts.
-#define CHUNK_LSTORE(KT, BUF)                                                                 \
-  _Pragma("unroll") for (int u = 0; u < NLD; ++u) {                                           \
-    const int ci = tid + 256 * u;                                                             \
-    const int pg = ci / (2 * D), within = ci % (2 * D);                                       \
-    /* K chunk `within` of the page block [D/32][16][32]: slot key, 8-dim chunk c */          \
-    const int key = (within >> 2) & 15, c = (within >> 6) * 4 + (within & 3);                \
-    *reinterpret_cast<uint4*>(&Ks[BUF][(pg * 16 + key) * D + (c ^ (key & (KCH - 1))) * 8]) = kr[u]; \
-    const int nvalid = it.key1 - ((KT) + pg * 16 + 8 * (within & 1));                         \
-    const uint2 lo = keep_first(make_uint2(vr[u].x, vr[u].y), nvalid);                        \
-    const uint2 hi = keep_first(make_uint2(vr[u].z, vr[u].w), nvalid - 4);                    \
-    const int dd = within >> 1, hf = within & 1, sw = (dd >> 2) & 3;                          \
-    uint16_t* vrow = &Vs[BUF][pg * PAGE + dd * 16];                                           \
-    *reinterpret_cast<uint2*>(vrow + ((2 * hf) ^ sw) * 4) = lo;                               \
-    *reinterpret_cast<uint2*>(vrow + ((2 * hf + 1) ^ sw) * 4) = hi;                           \
+  // this lane's query row and its Q^T fragments (dims 16 ks + 8 hh .. +7)
+  const int row = wave * 32 + col;
+  const int tl = row / g, hq = row - tl * g;
+  const bool valid = tl < it.n_tok;
+  const int t = it.tok0 + tl;
+  const int rpos = valid ? a.meta.tok_pos[t] : -1;
+  bf16x8 qf[KS];
+  {
+    const uint16_t* qrow = a.q + ((size_t)t * nq + kvh * g + hq) * D + hh * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = valid ? as_bf16x8(*reinterpret_cast<const uint4*>(qrow + ks * 16)) : as_bf16x8(make_uint4(0, 0, 0, 0));
   }
 
-  const int ntiles = (it.key1 - it.key0 + 63) / 64;
+  // LDS fragment offsets (elements, stage 0).  K: MFMA row col of key block kb
+  // is key 32 kb + kperm(col): page 2 kb + (col >> 4), slot kperm(col) & 15;
+  // k-step ks reads slice ks >> 1, chunk 2 (ks & 1) + hh.  V: dim row
+  // 32 db + col of page p, half hh.
+  const int kslot = kperm(col) & 15;
+  const int koff = ((col >> 4) * NS * 16 + kslot) * 32;
+  const int kc0 = (hh ^ kswz(kslot)) * 8, kc1 = ((2 + hh) ^ kswz(kslot)) * 8;
+  const int voff = TILE + col * 16 + ((hh ^ ((col >> 2) & 1)) * 8);
+
+  // DMA lane offsets inside a 1 KB load.  K (slot t = lane / 4, LDS chunk
+  // lane % 4) fetches chunk (lane % 4) ^ kswz(t); V (dim lane / 2 of the
+  // block, LDS half lane % 2) fetches half (lane % 2) ^ ((dim >> 2) & 1).
+  const int kdma = (lane >> 2) * 32 + (((lane & 3) ^ kswz(lane >> 2)) * 8);
+  const int vdma = (lane >> 1) * 16 + (((lane & 1) ^ ((lane >> 3) & 1)) * 8);
+
+  // Page ids of this wave's pages (page 4 j + wave of the item for tile j),
+  // one per lane for a window of 64 tiles, double-buffered over windows and
+  // broadcast with readlane.  Window w + 1 is fetched at the first tile of
+  // window w.
+  auto fetch_window = [&](int w) {
+    const int pi = 4 * (64 * w + lane) + wave;
+    return pi < npg ? bt[pi] : 0;
+  };
+  int pw0 = fetch_window(0), pw1 = 0;
+
+  auto issue_tile = [&](int tile, int st) {
+    // wave-uniform: does the tile have this wave's page?
+    if (4 * tile + wave < npg) {
+      const int page = __builtin_amdgcn_readlane(((tile >> 6) & 1) ? pw1 : pw0, tile & 63);
+      const size_t base = ((size_t)page * nkv + kvh) * PAGE;
+      const uint16_t* kg = a.k_cache + base + kdma;
+      const uint16_t* vg = a.v_cache + base + vdma;
+      uint16_t* dst = &lds[st][0];
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        __builtin_amdgcn_global_load_lds((const void*)(kg + s * 512), (lds_ptr_t)(dst + (wave * NS + s) * 512), 16, 0, 0);
+#pragma unroll
+      for (int u = 0; u < NS; ++u)
+        __builtin_amdgcn_global_load_lds((const void*)(vg + u * 512), (lds_ptr_t)(dst + TILE + wave * PAGE + u * 512), 16, 0,
+                                         0);
+    }
+  };
+
+  f32x16 acc[NS];
+#pragma unroll
+  for (int db = 0; db < NS; ++db)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[db][v] = 0.f;
+  float m = -INFINITY, l = 0.f;
   const int first_pos = a.meta.tok_pos[it.tok0];
-  CHUNK_GLOAD(it.key0);
-  CHUNK_LSTORE(it.key0, 0);
-  __syncthreads();
+
+  issue_tile(0, 0);
   for (int ti = 0; ti < ntiles; ++ti) {
     const int kt = it.key0 + ti * 64;
     const int cur = ti & 1;
-    if ((ti & 15) == 0) STAGE_PIDS((ti >> 4) + 1);
-    if (ti + 1 < ntiles) {
-      CHUNK_GLOAD(kt + 64);
+    // tile ti has landed for every wave, and every wave is done with tile ti - 1
+    __syncthreads();
+    if ((ti & 63) == 0) {
+      const int nw = fetch_window((ti >> 6) + 1);
+      if ((ti >> 6) & 1) pw0 = nw; else pw1 = nw;
     }
-    f32x4 s[4][2];
+    if (ti + 1 < ntiles) issue_tile(ti + 1, cur ^ 1);
+    if (kt + 64 > it.key1) {
+      // last tile, partly past the item's end: zero V of keys >= key1
+      uint16_t* vimg = &lds[cur][TILE];
+      for (int c = tid; c < 4 * D * 2; c += 256) {
+        const int p = c / (2 * D), dim = (c >> 1) % D, hs = c & 1;
+        const int nvalid = it.key1 - (kt + 16 * p + 8 * (hs ^ ((dim >> 2) & 1)));
+        if (nvalid < 8) {
+          uint4* ch = reinterpret_cast<uint4*>(vimg + p * PAGE + dim * 16 + hs * 8);
+          *ch = nvalid <= 0 ? make_uint4(0, 0, 0, 0) : keep_first8(*ch, nvalid);
+        }
+      }
+      __syncthreads();
+    }
+    const uint16_t* kimg = &lds[cur][0];
+
+    f32x16 s[2];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      s[kb][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-      s[kb][1] = s[kb][0];
-      const int key = kb * 16 + r;
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const int c = kk * 4 + qd;
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&Ks[cur][key * D + (c ^ (key & (KCH - 1))) * 8]);
-        s[kb][0] = mfma16x16x32(kf, qf[0][kk], s[kb][0]);
-        s[kb][1] = mfma16x16x32(kf, qf[1][kk], s[kb][1]);
+      for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
+            kimg + kb * 2 * NS * 512 + koff + (ks >> 1) * 512 + ((ks & 1) ? kc1 : kc0));
+        s[kb] = mfma32x32x16(kf, qf[ks], s[kb]);
       }
     }
-    bf16x8 pf[2][2], pfl[2][2];
     // causal / end-of-range masks matter only on tiles reaching past the first
     // row's position or past the item's last key (wave-uniform test)
-    const bool need_mask = (kt + 64 > it.key1) || (kt + 63 > first_pos);
+    if ((kt + 64 > it.key1) || (kt + 63 > first_pos)) {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      float sv[16];
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sv[kb * 4 + i] = s[kb][rb][i];
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = kt + kb * 16 + 4 * qd + i;
-            if (!(key <= rpos[rb] && key < it.key1)) sv[kb * 4 + i] = -INFINITY;
-          }
-      }
-      float mb = sv[0];
-#pragma unroll
-      for (int e = 1; e < 16; ++e) mb = fmaxf(mb, sv[e]);
-      mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
-      mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-      const float mn = fmaxf(m[rb], mb * scale_log2);   // log2 units; -inf while a row saw no key
-      const float ms = (mn == -INFINITY) ? 0.f : mn;
-      const float alpha = fast_exp2(m[rb] - ms);
-      float ps[16], lsum = 0.f;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        ps[e] = fast_exp2(fmaf(sv[e], scale_log2, -ms));
-        lsum += ps[e];
-      }
-      l[rb] = l[rb] * alpha + lsum;
-      m[rb] = mn;
-      if (__any(alpha != 1.0f)) {
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) acc[rb][j] *= alpha;
-      }
-      // keys 32c + 4qd + e (e < 4) and 32c + 16 + 4qd + (e - 4) (e >= 4)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        float p8[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          p8[e] = ps[(2 * c) * 4 + e];
-          p8[4 + e] = ps[(2 * c + 1) * 4 + e];
+        for (int v = 0; v < 16; ++v) {
+          const int key = kt + 32 * kb + 16 * (v >> 3) + 8 * hh + (v & 7);
+          if (!(key <= rpos && key < it.key1)) s[kb][v] = -INFINITY;
         }
-        split_p(p8, pf[rb][c], pfl[rb][c]);
+    }
+    float mb = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+    for (int v = 1; v < 16; ++v) mb = fmaxf(mb, fmaxf(s[0][v], s[1][v]));
+    mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+    const float mn = fmaxf(m, mb * scale_log2);   // log2 units; -inf while a row saw no key
+    const float ms = (mn == -INFINITY) ? 0.f : mn;
+    const float alpha = fast_exp2(m - ms);
+    m = mn;
+    // probabilities as bf16 pairs: pk[kb][j] holds keys of score registers 2j, 2j + 1
+    uint32_t pk[2][8];
+    float lsum = 0.f;
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        pk[kb][j] = pack2bf(fast_exp2(fmaf(s[kb][2 * j], scale_log2, -ms)),
+                            fast_exp2(fmaf(s[kb][2 * j + 1], scale_log2, -ms)));
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[kb][j]), ones, lsum, false);
+      }
+    l = l * alpha + lsum;
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+      for (int db = 0; db < NS; ++db) acc[db] *= alpha;
+    }
+    // key step q = 2 kb + h covers the tile's page q: keys 16 q + 8 hh .. +7 in this lane
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bf16x8 pb = as_bf16x8(make_uint4(pk[q >> 1][4 * (q & 1)], pk[q >> 1][4 * (q & 1) + 1],
+                                             pk[q >> 1][4 * (q & 1) + 2], pk[q >> 1][4 * (q & 1) + 3]));
+#pragma unroll
+      for (int db = 0; db < NS; ++db) {
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(kimg + voff + q * PAGE + db * 512);
+        acc[db] = mfma32x32x16(vf, pb, acc[db]);
       }
     }
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int dd = j * 16 + r, sw = (dd >> 2) & 3;
-        const uint2 lo = *reinterpret_cast<const uint2*>(&Vs[cur][(2 * c) * PAGE + dd * 16 + (qd ^ sw) * 4]);
-        const uint2 hi = *reinterpret_cast<const uint2*>(&Vs[cur][(2 * c + 1) * PAGE + dd * 16 + (qd ^ sw) * 4]);
-        const bf16x8 vf = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-        acc[0][j] = mfma16x16x32(vf, pf[0][c], acc[0][j]);
-        acc[1][j] = mfma16x16x32(vf, pf[1][c], acc[1][j]);
-        acc[0][j] = mfma16x16x32(vf, pfl[0][c], acc[0][j]);
-        acc[1][j] = mfma16x16x32(vf, pfl[1][c], acc[1][j]);
-      }
-    }
-    if (ti + 1 < ntiles) {
-      CHUNK_LSTORE(kt + 64, cur ^ 1);
-    }
-    __syncthreads();
   }
-#undef CHUNK_GLOAD
-#undef CHUNK_LSTORE
-#undef STAGE_PIDS
 
+  l += __shfl_xor(l, 32, 64);
+  if (valid) {
+    const int head = kvh * g + hq;
+    const size_t pidx = (size_t)a.meta.part_off[t] + it.split;
+    float* po = a.part_o + (pidx * nq + head) * D + 4 * hh;
+    // acc[db][v] is dim 32 db + 8 (v >> 2) + 4 hh + (v & 3)
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    float lt = l[rb];
-    lt += __shfl_xor(lt, 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
-    const int row = wave * 32 + rb * 16 + r;
-    const int tl = row / g, hq = row - tl * g;
-    if (tl < it.n_tok) {
-      const int t = it.tok0 + tl;
-      const int head = kvh * g + hq;
-      const size_t pidx = (size_t)a.meta.part_off[t] + it.split;
-      float* po = a.part_o + (pidx * nq + head) * D;
+    for (int db = 0; db < NS; ++db)
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        *reinterpret_cast<float4*>(po + j * 16 + qd * 4) =
-            make_float4(acc[rb][j][0], acc[rb][j][1], acc[rb][j][2], acc[rb][j][3]);
-      if (qd == 0) {
-        a.part_ml[(pidx * nq + head) * 2 + 0] = m[rb];
-        a.part_ml[(pidx * nq + head) * 2 + 1] = lt;
-      }
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<float4*>(po + 32 * db + 8 * j) =
+            make_float4(acc[db][4 * j], acc[db][4 * j + 1], acc[db][4 * j + 2], acc[db][4 * j + 3]);
+    if (hh == 0) {
+      a.part_ml[(pidx * nq + head) * 2 + 0] = m;
+      a.part_ml[(pidx * nq + head) * 2 + 1] = l;
     }
   }
 }

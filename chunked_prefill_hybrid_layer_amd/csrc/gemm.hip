@@ -128,8 +128,6 @@ __device__ __forceinline__ void qkv_store_pair(const GemmArgs& g, int m, int c, 
   }
 }
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 #define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
