@@ -58,8 +58,8 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // ----------------------------------------------------------------------------
 // decode items
 //
-// One step covers 32 keys (2 pages).  The item's page ids (at most 16: a
-// decode item spans at most kDecodeKvSplit = 256 keys) sit one per lane and
+// One step covers 32 keys (2 pages).  The item's page ids (at most 64: a
+// decode item spans at most kDecodeKvSplitMax = 1024 keys) sit one per lane and
 // are broadcast with readlane, so no step waits on a block-table load.  The
 // K/V of a step sit in one register buffer (138 VGPRs): three waves per SIMD
 // keep more bytes in flight than two double-buffered ones did (measured).
@@ -233,6 +233,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
 // still be NaN.  The weight sum l adds the bf16 probabilities the PV product
 // uses, so numerator and denominator carry the same rounding.
 
+constexpr float kLazyMax = 8.0f;
+
 __device__ __forceinline__ int kswz(int t) { return ((t >> 1) & 1) | ((t >> 2) & 2); }
 __device__ __forceinline__ int kperm(int i) {
   return 16 * (i >> 4) + 8 * ((i >> 2) & 1) + 4 * ((i >> 3) & 1) + (i & 3);
@@ -380,13 +382,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
           if (!(key <= rpos && key < it.key1)) s[kb][v] = -INFINITY;
         }
     }
-    float mb = fmaxf(s[0][0], s[1][0]);
+    // row maximum (NaN-propagating maximum: v_maximum3_f32 chains, no operand
+    // canonicalisation)
+    float mb = s[0][0];
 #pragma unroll
-    for (int v = 1; v < 16; ++v) mb = fmaxf(mb, fmaxf(s[0][v], s[1][v]));
-    mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-    const float mn = fmaxf(m, mb * scale_log2);   // log2 units; -inf while a row saw no key
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = kb ? 0 : 1; v < 16; ++v) mb = __builtin_elementwise_maximum(mb, s[kb][v]);
+    mb = __builtin_elementwise_maximum(mb, __shfl_xor(mb, 32, 64)) * scale_log2;
+    // The reference maximum m of a row (log2 units; -inf while the row saw no
+    // key) moves only when a tile exceeds it by more than kLazyMax: the
+    // probabilities then stay below 2^kLazyMax, and the accumulator rescale
+    // (a wave-uniform branch) is skipped on most tiles.  o and l are scaled by
+    // the same 2^-m, so the result does not depend on where m sits.
+    const bool grow = mb > m + kLazyMax;
+    const float mn = grow ? mb : m;
     const float ms = (mn == -INFINITY) ? 0.f : mn;
-    const float alpha = fast_exp2(m - ms);
+    const float alpha = grow ? fast_exp2(m - ms) : 1.0f;
     m = mn;
     // probabilities as bf16 pairs: pk[kb][j] holds keys of score registers 2j, 2j + 1
     uint32_t pk[2][8];

@@ -17,7 +17,9 @@ constexpr int kChunkKeyTile = 64;     // keys staged per step (4 pages of 16)
 constexpr int kChunkKvSplit = 1024;   // keys per chunk attention item, at least (multiple of 64)
 constexpr int kChunkItemsTarget = 2048;  // chunk items beyond which the key split doubles
 constexpr int kDecodeKeyStep = 32;    // keys per decode step (2 pages)
-constexpr int kDecodeKvSplit = 256;   // keys per decode attention item (multiple of 32)
+constexpr int kDecodeKvSplit = 256;   // keys per decode attention item, at least (multiple of 32)
+constexpr int kDecodeKvSplitMax = 1024;  // at most: the decode kernel holds an item's page ids one per lane
+constexpr int kDecodeWavesTarget = 16384;  // decode items x kv heads beyond which the decode split doubles
 constexpr int kPageSize = 16;
 constexpr uint32_t kMetaVersion = 2;
 constexpr int kMaxGroup = 16;         // decode path holds a kv group in one 16-row MFMA tile

@@ -229,16 +229,34 @@ hb_status hb_pack_metadata(const hb_dims* dims, int32_t n_chunks, const int32_t*
         }
       }
     }
+    // Longest key ranges first (chunk and decode lists alike): the kernels
+    // take items in list order, so the long ones start early and the short
+    // ones fill in behind them.  The output does not depend on the order
+    // (partials are indexed by split).
+    std::stable_sort(citems.begin(), citems.end(), [](const hb_attn_item& x, const hb_attn_item& y) {
+      return x.key1 - x.key0 > y.key1 - y.key0;
+    });
+    // Keys per decode item: kDecodeKvSplit, doubled (up to kDecodeKvSplitMax)
+    // while a large decode batch would still make more than
+    // kDecodeWavesTarget (item, kv head) waves: past that the split buys no
+    // parallelism, only partial results to write and merge.
+    int dsplit = kDecodeKvSplit;
+    auto decode_items = [&](int split) {
+      int64_t n = 0;
+      for (int s = n_chunks; s < S; ++s) n += (kv_len[s] + split - 1) / split;
+      return n;
+    };
+    while (dsplit < kDecodeKvSplitMax && decode_items(dsplit) * dims->n_kv_heads > kDecodeWavesTarget) dsplit *= 2;
     for (int s = n_chunks; s < S; ++s) {
       int t = q_start[s];
-      int nsplit = (kv_len[s] + kDecodeKvSplit - 1) / kDecodeKvSplit;
+      int nsplit = (kv_len[s] + dsplit - 1) / dsplit;
       for (int j = 0; j < nsplit; ++j) {
         hb_attn_item it{};
         it.seq = s;
         it.tok0 = t;
         it.n_tok = 1;
-        it.key0 = j * kDecodeKvSplit;
-        it.key1 = std::min(kv_len[s], (j + 1) * kDecodeKvSplit);
+        it.key0 = j * dsplit;
+        it.key1 = std::min(kv_len[s], (j + 1) * dsplit);
         it.split = j;
         ditems.push_back(it);
       }
@@ -246,6 +264,9 @@ hb_status hb_pack_metadata(const hb_dims* dims, int32_t n_chunks, const int32_t*
       part_cnt[t] = nsplit;
       np += nsplit;
     }
+    std::stable_sort(ditems.begin(), ditems.end(), [](const hb_attn_item& x, const hb_attn_item& y) {
+      return x.key1 - x.key0 > y.key1 - y.key0;
+    });
     if (np >= ((int64_t)1 << 31)) return fail(HB_E_CAPACITY, "too many attention partials");
 
     // KV append runs: each sequence's new tokens, cut where a page ends
@@ -288,7 +309,7 @@ hb_status hb_pack_metadata(const hb_dims* dims, int32_t n_chunks, const int32_t*
     h.n_q_heads = dims->n_q_heads;
     h.chunk_q_tile = qt;
     h.chunk_kv_split = csplit;
-    h.decode_kv_split = kDecodeKvSplit;
+    h.decode_kv_split = dsplit;
     h.n_chunk_items = (int32_t)citems.size();
     h.n_decode_items = (int32_t)ditems.size();
     h.n_partials = (int32_t)np;

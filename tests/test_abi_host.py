@@ -136,6 +136,38 @@ def test_long_prompt_widens_the_chunk_key_split():
     assert hb.header(blob2).chunk_kv_split == 1024
 
 
+def test_large_decode_batch_widens_the_decode_key_split():
+    """512 decodes of 1000-6000 context keys: the decode split grows past its
+    256-key minimum (at most 1024, the page ids one decode wave can hold), the
+    items still cover every decode's keys exactly once, and both item lists
+    run longest key range first.  32 decodes keep 256."""
+    rng = np.random.default_rng(7)
+    dc = rng.integers(1000, 6000, 512)
+    cl, cp = np.array([64]), np.array([100])
+    kv = np.concatenate([cp + cl, dc + 1])
+    bt, npg = W.deal_block_tables(kv, 16, rng)
+    blob, T = _pack(W.YI, cl, cp, dc, bt, npg)
+    h = hb.header(blob)
+    assert 256 < h.decode_kv_split <= 1024
+    assert h.n_decode_items * W.YI.n_kv_heads <= 16384 or h.decode_kv_split == 1024
+    items = hb.attn_items(blob, "decode")
+    pcnt = hb.meta_array(blob, "part_cnt")
+    assert np.array_equal(pcnt[64:], (dc + 1 + h.decode_kv_split - 1) // h.decode_kv_split)
+    for kind in ("chunk", "decode"):
+        r = hb.attn_items(blob, kind)
+        ln = r[:, 4] - r[:, 3]
+        assert np.all(ln[:-1] >= ln[1:]), kind
+    for t in range(64, T):
+        r = items[items[:, 1] == t]
+        r = r[np.argsort(r[:, 5])]
+        assert r[0, 3] == 0 and np.all(r[1:, 3] == r[:-1, 4]) and r[-1, 4] == dc[t - 64] + 1
+    small = dc[:32]
+    kv2 = np.concatenate([cp + cl, small + 1])
+    bt2, npg2 = W.deal_block_tables(kv2, 16, rng)
+    blob2, _ = _pack(W.YI, cl, cp, small, bt2, npg2)
+    assert hb.header(blob2).decode_kv_split == 256
+
+
 def test_worked_example_through_pack():
     g = json.load(open(os.path.join(ROOT, "tests", "golden", "worked_example_yi34b.json")))
     e = g["expected"]
