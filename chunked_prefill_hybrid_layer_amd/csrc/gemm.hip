@@ -7,13 +7,18 @@
 // 2 n d_in d_out / FLOPS, T_mem = (d_in d_out bytes_w + n d_in bytes_a) / BW;
 // "Chunked Prefill", hybrid-iteration roofline 2(c+b)Psi).
 //
-// Tiles (workgroup BM x BN, K stages of 64, 64 x (BN/2) per wave):
-//   128 x 128, 4 waves   batches under 256 tokens
-//   256 x 128, 8 waves   256+ tokens (residual projections)
-//   256 x 256 / 256 x 224, 8 waves   256+ tokens (QKV, gate/up): half the L2
-//                        and LDS operand traffic per flop of 256 x 128; the
-//                        224-wide tile makes Mistral-size gate/up exactly 256
-//                        tiles for the 256 CUs.
+// Tiles (workgroup BM x BN, K stages of 64):
+//   128 x 128, 4 waves
+//   128 x 128 / 128 x 96, 8 waves (2 per SIMD): more, smaller tiles where the
+//                        256-row ones leave CUs idle or need a K split (the
+//                        128 x 96 one gives a 512-token, 6144-wide QKV exactly
+//                        256 tiles with no split)
+//   256 x 128, 8 waves
+//   256 x 256 / 256 x 224, 8 waves: half the L2 and LDS operand traffic per
+//                        flop of 256 x 128; the 224-wide tile makes
+//                        Mistral-size gate/up exactly 256 tiles for 256 CUs.
+// A planner picks tile and K split per problem from a cost model fitted to
+// measured times.
 // Two waves per SIMD: on gfx950 one wave per SIMD issues back-to-back
 // independent 16x16x32 MFMAs at about two thirds of the rate two waves reach
 // (measured).  Both operands are K-contiguous and reach LDS through
@@ -34,6 +39,9 @@
 // Epilogues (the accumulator tile is staged through LDS as fp32):
 //   QKV:      RoPE (rotate-half, table-driven) on q and k; q -> bf16 buffer;
 //             k and v -> the paged KV cache at the tokens' slots (KV append).
+//             The weight rows are read in an order that interleaves the two
+//             halves of every head, so that each rotated pair is two adjacent
+//             GEMM columns and any tile width holds whole pairs.
 //   residual: out = res + acc (fp32).
 //   SwiGLU:   the first half of the tile's columns are gate rows, the second
 //             half the up rows of the same FFN units; out = silu(gate) * up (bf16).
@@ -67,6 +75,8 @@ struct Tile {
   static_assert(EPI_ROWS % (BM / WM) == 0, "epilogue passes must hold whole waves");
 };
 using Tile128 = Tile<128, 128, 64, 2, 2, 4>;    // ring pipeline (gemm_kernel)
+using Tile128W8 = Tile<128, 128, 64, 4, 2, 4>;  // ring pipeline, 8 waves (two per SIMD)
+using Tile128N96 = Tile<128, 96, 64, 4, 2, 4>;  // ring pipeline, 8 waves
 using Tile256 = Tile<256, 128, 64, 4, 2, 3>;    // ring pipeline (gemm_kernel)
 using TileW256 = Tile<256, 256, 64, 4, 2, 2>;   // sub-step pipeline (gemm_sub_kernel)
 using TileW224 = Tile<256, 224, 64, 4, 2, 2>;   // sub-step pipeline (gemm_sub_kernel)
@@ -85,6 +95,11 @@ __device__ __forceinline__ int swz(int r, int c) {
 template <int MODE, int BN>
 __device__ __forceinline__ const uint16_t* weight_row(const GemmArgs& g, int n, int n0) {
   if (MODE == kGemmQkvRope) {
+    // GEMM columns run over each head with the two halves interleaved:
+    // column 2j of a head is dim j, column 2j + 1 is dim j + d/2, so every
+    // rotated pair sits in two adjacent columns of one tile
+    const int d = g.head_dim, h = n / d, p = n - h * d;
+    n = h * d + (p >> 1) + (p & 1) * (d >> 1);
     if (n < g.n0) return g.w0 + (size_t)n * g.K;
     if (n < g.n0 + g.n1) return g.w1 + (size_t)(n - g.n0) * g.K;
     return g.w2 + (size_t)(n - g.n0 - g.n1) * g.K;
@@ -95,36 +110,52 @@ __device__ __forceinline__ const uint16_t* weight_row(const GemmArgs& g, int n, 
     return g.w0 + (size_t)n * g.K;
   }
 }
-// QKV output of token m, columns c and c + d/2 of one head (c within the first
-// half): q and k are rotated by the token's position, q goes to the q buffer,
-// k and v to the paged cache at the token's slot.
-__device__ __forceinline__ void qkv_store_pair(const GemmArgs& g, int m, int c, float x0, float x1) {
+// QKV output of token m, GEMM columns n .. n + 7 (n a multiple of 8): dims
+// i0 .. i0 + 3 (x0) and i0 + d/2 .. i0 + d/2 + 3 (x1) of one head, where
+// i0 = (n mod d) / 2.  q and k are rotated by the token's position (rotate-
+// half: dim i pairs with dim i + d/2), q goes to the q buffer, k and v to the
+// paged cache at the token's slot.  q and K stores are 8 bytes; V (dim-major
+// in a page) takes one 2-byte store per dim.
+__device__ __forceinline__ void qkv_store4(const GemmArgs& g, int m, int n, const float (&x0)[4],
+                                           const float (&x1)[4]) {
   const int d = g.head_dim, half = d >> 1;
   const int qdim = g.n_q_heads * d, kdim = g.n_kv_heads * d;
-  const int i = c % d;
+  const int hb = n / d, i0 = (n - hb * d) >> 1;
+  const int c = hb * d + i0;  // natural column of dim i0
   if (c < qdim + kdim) {
     const int pos = g.tok_pos[m];
-    const float2 cs = *reinterpret_cast<const float2*>(g.rope + ((size_t)pos * half + i) * 2);
-    const uint16_t y0 = f2bf(x0 * cs.x - x1 * cs.y);
-    const uint16_t y1 = f2bf(x1 * cs.x + x0 * cs.y);
+    const float4* rp = reinterpret_cast<const float4*>(g.rope + ((size_t)pos * half + i0) * 2);
+    const float4 cs01 = rp[0], cs23 = rp[1];
+    const float cs[4] = {cs01.x, cs01.z, cs23.x, cs23.z}, sn[4] = {cs01.y, cs01.w, cs23.y, cs23.w};
+    float y0[4], y1[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      y0[e] = x0[e] * cs[e] - x1[e] * sn[e];
+      y1[e] = x1[e] * cs[e] + x0[e] * sn[e];
+    }
+    const uint2 lo = make_uint2(pack2bf(y0[0], y0[1]), pack2bf(y0[2], y0[3]));
+    const uint2 hi = make_uint2(pack2bf(y1[0], y1[1]), pack2bf(y1[2], y1[3]));
     if (c < qdim) {
       uint16_t* qo = g.out_b + (size_t)m * qdim + c;
-      qo[0] = y0;
-      qo[half] = y1;
+      *reinterpret_cast<uint2*>(qo) = lo;
+      *reinterpret_cast<uint2*>(qo + half) = hi;
     } else {
       const int kvh = (c - qdim) / d;
       const int sl = g.slot[m];
-      // K page block: [d/32][16 slots][32]
+      // K page block: [d/32][16 slots][32]; dims i0 .. i0 + 3 share a 32-dim slice
       uint16_t* kb = g.k_cache + ((size_t)(sl >> 4) * g.n_kv_heads + kvh) * 16 * d + (sl & 15) * 32;
-      kb[(i >> 5) * 512 + (i & 31)] = y0;
-      kb[((i + half) >> 5) * 512 + ((i + half) & 31)] = y1;
+      *reinterpret_cast<uint2*>(kb + (i0 >> 5) * 512 + (i0 & 31)) = lo;
+      *reinterpret_cast<uint2*>(kb + ((i0 + half) >> 5) * 512 + ((i0 + half) & 31)) = hi;
     }
   } else {
     const int kvh = (c - qdim - kdim) / d;
     const int sl = g.slot[m];
-    uint16_t* vp = g.v_cache + (((size_t)(sl >> 4) * g.n_kv_heads + kvh) * d + i) * 16 + (sl & 15);
-    vp[0] = f2bf(x0);
-    vp[half * 16] = f2bf(x1);
+    uint16_t* vp = g.v_cache + (((size_t)(sl >> 4) * g.n_kv_heads + kvh) * d + i0) * 16 + (sl & 15);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      vp[e * 16] = f2bf(x0[e]);
+      vp[(half + e) * 16] = f2bf(x1[e]);
+    }
   }
 }
 
@@ -199,14 +230,15 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x4 (&acc)[TL
         pk.y = pack2bf(o[2], o[3]);
         *reinterpret_cast<uint2*>(g.out_b + (size_t)m * g.ldo + f0 + c4 * 4) = pk;
       }
-    } else {  // QKV + RoPE + KV append: one thread per (token, rotated pair)
-      const int half = g.head_dim >> 1;
-      for (int idx = tid; idx < ER * (BN / 2); idx += NT) {
-        const int r = idx / (BN / 2), pp = idx % (BN / 2);
+    } else {  // QKV + RoPE + KV append: one thread per (token, 4 rotated pairs)
+      for (int idx = tid; idx < ER * (BN / 8); idx += NT) {
+        const int r = idx / (BN / 8), c8 = idx % (BN / 8);
         const int m = mb + r;
         if (m >= g.M) continue;
-        const int c = (pp / half) * g.head_dim + pp % half;  // column within the tile
-        qkv_store_pair(g, m, n0 + c, Cs[r * CS_LD + c], Cs[r * CS_LD + c + half]);
+        const float4 a = *reinterpret_cast<const float4*>(Cs + r * CS_LD + c8 * 8);
+        const float4 b = *reinterpret_cast<const float4*>(Cs + r * CS_LD + c8 * 8 + 4);
+        const float x0[4] = {a.x, a.z, b.x, b.z}, x1[4] = {a.y, a.w, b.y, b.w};
+        qkv_store4(g, m, n0 + c8 * 8, x0, x1);
       }
     }
   }
@@ -217,7 +249,6 @@ __global__ __launch_bounds__(TL::THREADS) void gemm_kernel(GemmArgs g) {
   constexpr int BM = TL::BM, BN = TL::BN, BK = TL::BK, NST = TL::NST, SE = TL::STAGE_ELEMS;
   constexpr int NL = TL::LOADS, NT = TL::THREADS, FM = TL::FM, FN = TL::FN, KS = TL::KS, CPR = TL::CPR;
   constexpr int RPL = TL::RPL, WROWS = BM / TL::WM, WCOLS = BN / TL::WN, CS_LD = TL::CS_LD;
-  static_assert(TL::TOTAL_LOADS % TL::WAVES == 0, "this pipeline counts equal loads per wave");
   __shared__ __align__(16) unsigned char smem[TL::LDS];
   uint16_t* lds = reinterpret_cast<uint16_t*>(smem);
 
@@ -236,11 +267,14 @@ __global__ __launch_bounds__(TL::THREADS) void gemm_kernel(GemmArgs g) {
   // DMA mapping: load q = wave + WAVES * i covers rows [RPL q, RPL q + RPL) of
   // the stage image (A rows first, then B rows); lane l lands at row
   // RPL q + l / CPR, chunk l % CPR, i.e. it loads logical chunk (l % CPR) ^ f(row).
+  // When the loads of a stage do not divide evenly over the waves, the waves
+  // short of one repeat the stage's last load (same bytes to the same LDS
+  // address), so that every wave counts the same number of loads per stage.
   const uint16_t* gsrc[NL];
   int ldst[NL];
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
-    const int q = wave + TL::WAVES * i;
+    const int q = min(wave + TL::WAVES * i, TL::TOTAL_LOADS - 1);
     const int r = RPL * q + lane / CPR;                      // row of the stage image
     const int rr = r < BM ? r : r - BM;                       // row within A or B
     const int c = swz<CPR>(rr, lane % CPR);
@@ -550,40 +584,43 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   }
 }
 
-// QKV after split-K: sum the slices of each rotated column pair, then the QKV
-// epilogue.  One thread per (token, pair).
+// QKV after split-K: sum the slices (in order) of 8 consecutive GEMM columns
+// (4 rotated pairs), then the QKV epilogue.  One thread per (token, 8 columns).
 __global__ __launch_bounds__(256) void qkv_reduce_kernel(GemmArgs g, int splits) {
-  const int half = g.head_dim >> 1, pairs = g.N / 2;
+  const int groups = g.N / 8;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)g.M * pairs) return;
-  const int m = (int)(idx / pairs), p = (int)(idx % pairs);
-  const int c = (p / half) * g.head_dim + p % half;
-  float x0 = 0.f, x1 = 0.f;
+  if (idx >= (int64_t)g.M * groups) return;
+  const int m = (int)(idx / groups), n = (int)(idx % groups) * 8;
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
   for (int z = 0; z < splits; ++z) {
-    const float* row = g.part + ((size_t)z * g.M + m) * g.N;
-    x0 += row[c];
-    x1 += row[c + half];
+    const float4* row = reinterpret_cast<const float4*>(g.part + ((size_t)z * g.M + m) * g.N + n);
+    const float4 u = row[0], v = row[1];
+    a.x += u.x; a.y += u.y; a.z += u.z; a.w += u.w;
+    b.x += v.x; b.y += v.y; b.z += v.z; b.w += v.w;
   }
-  qkv_store_pair(g, m, c, x0, x1);
+  const float x0[4] = {a.x, a.z, b.x, b.z}, x1[4] = {a.y, a.w, b.y, b.w};
+  qkv_store4(g, m, n, x0, x1);
 }
 
-enum { kTile128 = 0, kTile256 = 1, kTileW256 = 2, kTileW224 = 3 };
+enum { kTile128 = 0, kTile256 = 1, kTileW256 = 2, kTileW224 = 3, kTile128W8 = 4, kTile128N96 = 5 };
 
-// Estimated time of one GEMM under a tile choice: rounds of tiles over the 256
-// CUs times the MFMA time of one tile (plus its fill) at that tile's measured efficiency, plus
-// the split-K partials (written once, read once by the reduce; up to 128 MB
-// they stay in the 256 MB last-level cache, priced at 10 TB/s, else at 5).  Within 10 % of the
-// measured times on the Mistral-7B- and Yi-34B-shaped projections.
+// Estimated time of one GEMM under a tile choice, fitted (least squares, 37
+// measured tile/split choices on the Mistral-7B- and Yi-34B-shaped
+// projections, most within 5 %) to
+//   rounds * 2 BM BN (K / splits + 545) / (per-CU peak * eff) * (0.776 + 0.224 f)
+//   + split-K partials written and read once at 6.5 TB/s,
+// where rounds = ceil(tiles / 256 CUs), f = tiles / (rounds * 256) is how full
+// the rounds are (a part-filled machine runs each busy CU faster), and 545
+// K columns stand for a tile's pipeline fill and epilogue.
 template <class TL>
 static double plan_cost(int M, int N, int K, int splits, double eff) {
   const double tiles = (double)((M + TL::BM - 1) / TL::BM) * (N / TL::BN) * splits;
   const double rounds = std::ceil(tiles / kNumCU);
+  const double fill = tiles / (rounds * kNumCU);
   const double per_cu = 2.5e15 / kNumCU * eff;   // flop/s
-  // each tile also pays its pipeline fill and epilogue, about 4 K steps of 64
-  const double t_tile = 2.0 * TL::BM * TL::BN * ((double)K / splits + 256.0) / per_cu;
-  const double part_bytes = (double)splits * M * N * 4;
-  const double t_part = splits > 1 ? 2.0 * part_bytes / (part_bytes <= 128e6 ? 10e12 : 5e12) : 0.0;
-  return rounds * t_tile + t_part;
+  const double t_tile = 2.0 * TL::BM * TL::BN * ((double)K / splits + 545.0) / per_cu;
+  const double t_part = splits > 1 ? 2.0 * splits * (double)M * N * 4 / 6.5e12 : 0.0;
+  return rounds * t_tile * (0.776 + 0.224 * fill) + t_part;
 }
 
 template <class TL>
@@ -601,17 +638,19 @@ static void plan_try(GemmPlan& best, double& best_cost, int tile, int mode, int 
   }
 }
 
-// Efficiencies: fraction of the MFMA peak per busy CU, as measured.
+// Efficiencies: fraction of the MFMA peak per busy CU with every CU busy (fit;
+// 256x224 raised from 0.455 to 0.485 to match the layer, where it beats
+// 256x256 by 3-6 % on gate/up, O and down whenever both apply).
 GemmPlan gemm_plan(int mode, int M, int N, int K) {
   GemmPlan p{kTile128, 1};
   double cost = 1e30;
-  if (M < 256) {
-    plan_try<Tile128>(p, cost, kTile128, mode, M, N, K, 0.30);
-    return p;
-  }
-  plan_try<Tile256>(p, cost, kTile256, mode, M, N, K, 0.45);
-  plan_try<TileW256>(p, cost, kTileW256, mode, M, N, K, 0.52);
-  plan_try<TileW224>(p, cost, kTileW224, mode, M, N, K, 0.52);
+  plan_try<Tile128>(p, cost, kTile128, mode, M, N, K, 0.324);
+  plan_try<Tile128W8>(p, cost, kTile128W8, mode, M, N, K, 0.344);
+  plan_try<Tile128N96>(p, cost, kTile128N96, mode, M, N, K, 0.291);
+  if (M < 256) return p;
+  plan_try<Tile256>(p, cost, kTile256, mode, M, N, K, 0.426);
+  plan_try<TileW256>(p, cost, kTileW256, mode, M, N, K, 0.515);
+  plan_try<TileW224>(p, cost, kTileW224, mode, M, N, K, 0.485);
   return p;
 }
 
@@ -644,11 +683,13 @@ hb_status launch_gemm(const GemmArgs& g, stream_t s) {
   if (p.tile == kTileW224) launch_sub<TileW224>(g, p.splits, (hipStream_t)s);
   else if (p.tile == kTileW256) launch_sub<TileW256>(g, p.splits, (hipStream_t)s);
   else if (p.tile == kTile256) launch_tile<Tile256>(g, p.splits, (hipStream_t)s);
+  else if (p.tile == kTile128W8) launch_tile<Tile128W8>(g, p.splits, (hipStream_t)s);
+  else if (p.tile == kTile128N96) launch_tile<Tile128N96>(g, p.splits, (hipStream_t)s);
   else launch_tile<Tile128>(g, p.splits, (hipStream_t)s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(HB_E_HIP, std::string("gemm launch: ") + hipGetErrorString(e));
   if (p.splits > 1 && g.mode == kGemmQkvRope) {
-    const int64_t n = (int64_t)g.M * (g.N / 2);
+    const int64_t n = (int64_t)g.M * (g.N / 8);
     hipLaunchKernelGGL(qkv_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, (hipStream_t)s, g,
                        p.splits);
     e = hipGetLastError();
