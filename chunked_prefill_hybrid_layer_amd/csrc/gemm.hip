@@ -8,7 +8,6 @@
 // "Chunked Prefill", hybrid-iteration roofline 2(c+b)Psi).
 //
 // Tiles (workgroup BM x BN, K stages of 64):
-//   128 x 128, 4 waves
 //   128 x 128 / 128 x 96, 8 waves (2 per SIMD): more, smaller tiles where the
 //                        256-row ones leave CUs idle or need a K split (the
 //                        128 x 96 one gives a 512-token, 6144-wide QKV exactly
@@ -74,7 +73,6 @@ struct Tile {
   static_assert((BM + BN) % RPL == 0, "stage rows must split into whole wave loads");
   static_assert(EPI_ROWS % (BM / WM) == 0, "epilogue passes must hold whole waves");
 };
-using Tile128 = Tile<128, 128, 64, 2, 2, 4>;    // ring pipeline (gemm_kernel)
 using Tile128W8 = Tile<128, 128, 64, 4, 2, 4>;  // ring pipeline, 8 waves (two per SIMD)
 using Tile128N96 = Tile<128, 96, 64, 4, 2, 4>;  // ring pipeline, 8 waves
 using Tile256 = Tile<256, 128, 64, 4, 2, 3>;    // ring pipeline (gemm_kernel)
@@ -602,7 +600,7 @@ __global__ __launch_bounds__(256) void qkv_reduce_kernel(GemmArgs g, int splits)
   qkv_store4(g, m, n, x0, x1);
 }
 
-enum { kTile128 = 0, kTile256 = 1, kTileW256 = 2, kTileW224 = 3, kTile128W8 = 4, kTile128N96 = 5 };
+enum { kTile256 = 1, kTileW256 = 2, kTileW224 = 3, kTile128W8 = 4, kTile128N96 = 5 };
 
 // Estimated time of one GEMM under a tile choice, fitted (least squares, 37
 // measured tile/split choices on the Mistral-7B- and Yi-34B-shaped
@@ -642,9 +640,8 @@ static void plan_try(GemmPlan& best, double& best_cost, int tile, int mode, int 
 // 256x224 raised from 0.455 to 0.485 to match the layer, where it beats
 // 256x256 by 3-6 % on gate/up, O and down whenever both apply).
 GemmPlan gemm_plan(int mode, int M, int N, int K) {
-  GemmPlan p{kTile128, 1};
+  GemmPlan p{kTile128W8, 1};
   double cost = 1e30;
-  plan_try<Tile128>(p, cost, kTile128, mode, M, N, K, 0.324);
   plan_try<Tile128W8>(p, cost, kTile128W8, mode, M, N, K, 0.344);
   plan_try<Tile128N96>(p, cost, kTile128N96, mode, M, N, K, 0.291);
   if (M < 256) return p;
@@ -685,7 +682,7 @@ hb_status launch_gemm(const GemmArgs& g, stream_t s) {
   else if (p.tile == kTile256) launch_tile<Tile256>(g, p.splits, (hipStream_t)s);
   else if (p.tile == kTile128W8) launch_tile<Tile128W8>(g, p.splits, (hipStream_t)s);
   else if (p.tile == kTile128N96) launch_tile<Tile128N96>(g, p.splits, (hipStream_t)s);
-  else launch_tile<Tile128>(g, p.splits, (hipStream_t)s);
+  else launch_tile<Tile128W8>(g, p.splits, (hipStream_t)s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(HB_E_HIP, std::string("gemm launch: ") + hipGetErrorString(e));
   if (p.splits > 1 && g.mode == kGemmQkvRope) {
