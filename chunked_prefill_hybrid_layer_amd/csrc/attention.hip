@@ -35,11 +35,11 @@ __device__ __forceinline__ uint2 keep_first(uint2 v, int n) {
   return make_uint2(v.x, v.y & 0xffffu);
 }
 
-// Probabilities enter the PV product as two bf16 fragments, p = hi + lo with
-// hi = bf16(p) and lo = bf16(p - hi): about 16 significant bits.  A single bf16
-// P would put a 2^-9 relative error on every weight, and since o is an average
-// of values that largely cancel, that error does not shrink with the number
-// of keys.
+// Decode items: probabilities enter the PV product as two bf16 fragments,
+// p = hi + lo with hi = bf16(p) and lo = bf16(p - hi), about 16 significant
+// bits (a single bf16 P puts a relative error up to 2^-9 on every weight).  The
+// decode kernel is bound by HBM, so the second MFMA per step is free there; the
+// chunk kernel, which is not, uses a single bf16 P (see its comment).
 __device__ __forceinline__ void split_p(const float* p, bf16x8& hi, bf16x8& lo) {
   uint32_t h[4], l[4];
 #pragma unroll
