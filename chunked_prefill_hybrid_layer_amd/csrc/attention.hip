@@ -214,11 +214,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
 // moves page w of the tile, D/32 1 KB loads each of K and V, double-buffered
 // over tiles with one barrier per tile.  Each lane's global address is chosen
 // so that the LDS image comes out XOR-swizzled on 16-byte chunks:
-//   K image [page 4][slice D/32][slot 16][32 dims]: the cache's own page layout;
-//     chunk c of slot t's 64-byte row sits at c ^ kswz(t).
+//   K image [page 4][dim half D/64][slot 16][64 dims]: 128-byte rows, chunk c
+//     of slot t's row at c ^ ((t >> 1) & 7); one 1 KB load fills 8 slots of
+//     one half, gathering from two of the cache's 32-dim slices.
 //   V image [page 4][dim D][16 keys]: the cache's own (dim-major) page layout;
-//     half h (keys 8h..8h+7) of dim row d sits at h ^ ((d >> 2) & 1).
-// Both fragment reads are ds_read_b128 without bank conflicts.
+//     half h (keys 8h..8h+7) of dim row d sits at h ^ ((d >> 3) & 1).
+// Both fragment reads are ds_read_b128 without bank conflicts (measured with
+// SQ_LDS_BANK_CONFLICT on these exact access patterns: the previous swizzles,
+// c ^ f(t) on 64-byte rows and h ^ ((d >> 2) & 1), cost 4 conflict cycles per
+// read and 1.7x the read time).
 //
 // Key order.  The rows of the QK MFMA are a permutation of the 32 keys of a
 // block: MFMA row i is key kperm(i).  With it, the 16 scores lane l receives
@@ -235,7 +239,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
 
 constexpr float kLazyMax = 8.0f;
 
-__device__ __forceinline__ int kswz(int t) { return ((t >> 1) & 1) | ((t >> 2) & 2); }
+__device__ __forceinline__ int kswz(int t) { return (t >> 1) & 7; }
 __device__ __forceinline__ int kperm(int i) {
   return 16 * (i >> 4) + 8 * ((i >> 2) & 1) + 4 * ((i >> 3) & 1) + (i & 3);
 }
@@ -249,7 +253,8 @@ __device__ __forceinline__ uint4 keep_first8(uint4 v, int n) {
 
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_chunk_kernel(AttnArgs a, float scale_log2) {
-  constexpr int NS = D / 32;      // 32-dim K slices per page = 1 KB V blocks per page = PV dim blocks
+  constexpr int NS = D / 32;      // 1 KB K or V loads per page = PV dim blocks
+  constexpr int NH = D / 64;      // 128-byte dim halves of a K row
   constexpr int KS = D / 16;      // QK k-steps
   constexpr int PAGE = 16 * D;    // elements per (page, kv head) block
   constexpr int TILE = 4 * PAGE;  // elements of K (or of V) per 64-key tile
@@ -284,18 +289,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 
   // LDS fragment offsets (elements, stage 0).  K: MFMA row col of key block kb
   // is key 32 kb + kperm(col): page 2 kb + (col >> 4), slot kperm(col) & 15;
-  // k-step ks reads slice ks >> 1, chunk 2 (ks & 1) + hh.  V: dim row
-  // 32 db + col of page p, half hh.
+  // k-step ks reads dim half ks >> 2, chunk (2 ks + hh) & 7 of that half.
+  // V: dim row 32 db + col of page p, half hh.
   const int kslot = kperm(col) & 15;
-  const int koff = ((col >> 4) * NS * 16 + kslot) * 32;
-  const int kc0 = (hh ^ kswz(kslot)) * 8, kc1 = ((2 + hh) ^ kswz(kslot)) * 8;
-  const int voff = TILE + col * 16 + ((hh ^ ((col >> 2) & 1)) * 8);
+  const int koff = ((col >> 4) * NH * 16 + kslot) * 64;
+  int kch[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) kch[j] = (((2 * j + hh) & 7) ^ kswz(kslot)) * 8;
+  const int voff = TILE + col * 16 + ((hh ^ ((col >> 3) & 1)) * 8);
 
-  // DMA lane offsets inside a 1 KB load.  K (slot t = lane / 4, LDS chunk
-  // lane % 4) fetches chunk (lane % 4) ^ kswz(t); V (dim lane / 2 of the
-  // block, LDS half lane % 2) fetches half (lane % 2) ^ ((dim >> 2) & 1).
-  const int kdma = (lane >> 2) * 32 + (((lane & 3) ^ kswz(lane >> 2)) * 8);
-  const int vdma = (lane >> 1) * 16 + (((lane & 1) ^ ((lane >> 3) & 1)) * 8);
+  // DMA lane offsets inside a 1 KB load.  K load (half h, slots 8 b .. 8 b + 7)
+  // of a page: lane -> slot 8 b + lane / 8, LDS chunk lane % 8, which holds
+  // logical chunk c = (lane % 8) ^ kswz(slot): dims 64 h + 8 c .. +7, in the
+  // cache's slice 2 h + c / 4 at chunk c % 4.  V (dim lane / 2 of the block,
+  // LDS half lane % 2) fetches half (lane % 2) ^ ((dim >> 3) & 1).
+  int kdma[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int sl = 8 * b + (lane >> 3), c = (lane & 7) ^ kswz(sl);
+    kdma[b] = ((c >> 2) * 16 + sl) * 32 + (c & 3) * 8;
+  }
+  const int vdma = (lane >> 1) * 16 + (((lane & 1) ^ ((lane >> 4) & 1)) * 8);
 
   // Page ids of this wave's pages (page 4 j + wave of the item for tile j),
   // one per lane for a window of 64 tiles, double-buffered over windows and
@@ -312,12 +326,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     if (4 * tile + wave < npg) {
       const int page = __builtin_amdgcn_readlane(((tile >> 6) & 1) ? pw1 : pw0, tile & 63);
       const size_t base = ((size_t)page * nkv + kvh) * PAGE;
-      const uint16_t* kg = a.k_cache + base + kdma;
+      const uint16_t* kg = a.k_cache + base;
       const uint16_t* vg = a.v_cache + base + vdma;
       uint16_t* dst = &lds[st][0];
+      // K: load s = 2 h + b covers half h, slots 8 b .. 8 b + 7 (page image
+      // [half][slot][64]: element offset 512 s within the page's image)
 #pragma unroll
       for (int s = 0; s < NS; ++s)
-        __builtin_amdgcn_global_load_lds((const void*)(kg + s * 512), (lds_ptr_t)(dst + (wave * NS + s) * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(kg + (s >> 1) * 1024 + kdma[s & 1]),
+                                         (lds_ptr_t)(dst + (wave * NS + s) * 512), 16, 0, 0);
 #pragma unroll
       for (int u = 0; u < NS; ++u)
         __builtin_amdgcn_global_load_lds((const void*)(vg + u * 512), (lds_ptr_t)(dst + TILE + wave * PAGE + u * 512), 16, 0,
@@ -349,7 +366,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
       uint16_t* vimg = &lds[cur][TILE];
       for (int c = tid; c < 4 * D * 2; c += 256) {
         const int p = c / (2 * D), dim = (c >> 1) % D, hs = c & 1;
-        const int nvalid = it.key1 - (kt + 16 * p + 8 * (hs ^ ((dim >> 2) & 1)));
+        const int nvalid = it.key1 - (kt + 16 * p + 8 * (hs ^ ((dim >> 3) & 1)));
         if (nvalid < 8) {
           uint4* ch = reinterpret_cast<uint4*>(vimg + p * PAGE + dim * 16 + hs * 8);
           *ch = nvalid <= 0 ? make_uint4(0, 0, 0, 0) : keep_first8(*ch, nvalid);
@@ -367,7 +384,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
-            kimg + kb * 2 * NS * 512 + koff + (ks >> 1) * 512 + ((ks & 1) ? kc1 : kc0));
+            kimg + kb * 2 * NS * 512 + koff + (ks >> 2) * 1024 + kch[ks & 3]);
         s[kb] = mfma32x32x16(kf, qf[ks], s[kb]);
       }
     }
