@@ -217,28 +217,29 @@ def bench_batch(wl, name, steps, warmup, copies, calibrate_copy=False):
     torch.cuda.synchronize()
     assert all(e.cuda_event for row in evs.values() for e in row)
     ev_arrays = {i: hb.make_events([e.cuda_event for e in row]) for i, row in evs.items()}
-    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    # one timing event pair around the timed steps (a timing event between
+    # steps would itself leave a bubble)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     host_s = np.zeros(steps)
+    t_start.record()
     for i in range(steps):
         h0 = time.perf_counter()
-        step_ev[i].record()
         step(warmup + i, ev_arrays.get(i))
         host_s[i] = time.perf_counter() - h0
-    step_ev[steps].record()
+    t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms = step_ev[0].elapsed_time(step_ev[steps]) / steps
+    ms = t_start.elapsed_time(t_end) / steps
     if calibrate_copy:
         src = torch.empty(64 << 20, dtype=torch.int32, device="cuda").fill_(1)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
-    plain = [i for i in range(steps) if i not in evs]
-    step_ms = np.array([step_ev[i].elapsed_time(step_ev[i + 1]) for i in (plain or range(steps))])
-    inst_ms = np.array([step_ev[i].elapsed_time(step_ev[i + 1]) for i in inst])
+    inst_ms = np.array([evs[i][0].elapsed_time(evs[i][nst]) for i in inst])
     stage_ms = np.array([[evs[i][k].elapsed_time(evs[i][k + 1]) for k in range(nst)] for i in inst])
     stage_mean = stage_ms.mean(axis=0)
 
@@ -287,7 +288,6 @@ def bench_batch(wl, name, steps, warmup, copies, calibrate_copy=False):
                    "token_budget": b.token_budget, "page_size": d.page_size, "copies_rotated": copies},
         "layer_iters_per_s": round(1e3 / ms, 1),
         "layer_roofline_frac": round(t_roof / (ms * 1e-3), 4),
-        "step_ms_p10_p50_p90": [round(float(np.percentile(step_ms, q)), 5) for q in (10, 50, 90)],
         "instrumented_step_ms_p50": round(float(np.median(inst_ms)), 5),
         "instrumented_steps": len(inst),
         "host_issue_ms_p50": round(float(np.median(host_s)) * 1e3, 4),

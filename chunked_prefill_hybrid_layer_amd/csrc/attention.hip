@@ -486,33 +486,37 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   const float* src = a.part_o + ((size_t)p0 * nq + h) * D + l4 * 4;
   float M = -INFINITY, L = 0.f;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-#define MERGE_STEP(U)                                                                          \
-  {                                                                                            \
-    float2 mv[U];                                                                              \
-    float4 v[U];                                                                               \
-    _Pragma("unroll") for (int u = 0; u < U; ++u) {                                            \
-      mv[u] = ml[(size_t)(p + u) * nq];                                                        \
-      v[u] = *reinterpret_cast<const float4*>(src + (size_t)(p + u) * nq * D);                 \
-    }                                                                                          \
-    float mb = mv[0].x;                                                                        \
-    _Pragma("unroll") for (int u = 1; u < U; ++u) mb = fmaxf(mb, mv[u].x);                     \
-    const float mn = fmaxf(M, mb);                                                             \
-    if (mn != -INFINITY) {                                                                     \
-      const float sc = (M == -INFINITY) ? 0.f : fast_exp2(M - mn);                             \
-      L *= sc;                                                                                 \
-      o.x *= sc; o.y *= sc; o.z *= sc; o.w *= sc;                                              \
-      _Pragma("unroll") for (int u = 0; u < U; ++u) {                                          \
-        const float w = (mv[u].x == -INFINITY) ? 0.f : fast_exp2(mv[u].x - mn);                \
-        L += w * mv[u].y;                                                                      \
-        o.x += w * v[u].x; o.y += w * v[u].y; o.z += w * v[u].z; o.w += w * v[u].w;            \
-      }                                                                                        \
-      M = mn;                                                                                  \
-    }                                                                                          \
+  // Steps of four partials, loaded together; slots past the token's last
+  // partial count as empty (m = -inf), so a token with 1..4 partials takes one
+  // round of loads.
+  for (int p = 0; p < pc; p += 4) {
+    float2 mv[4];
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (p + u < pc) {
+        mv[u] = ml[(size_t)(p + u) * nq];
+        v[u] = *reinterpret_cast<const float4*>(src + (size_t)(p + u) * nq * D);
+      } else {
+        mv[u] = make_float2(-INFINITY, 0.f);
+        v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    const float mb = fmaxf(fmaxf(mv[0].x, mv[1].x), fmaxf(mv[2].x, mv[3].x));
+    const float mn = fmaxf(M, mb);
+    if (mn != -INFINITY) {
+      const float sc = (M == -INFINITY) ? 0.f : fast_exp2(M - mn);
+      L *= sc;
+      o.x *= sc; o.y *= sc; o.z *= sc; o.w *= sc;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float w = (mv[u].x == -INFINITY) ? 0.f : fast_exp2(mv[u].x - mn);
+        L += w * mv[u].y;
+        o.x += w * v[u].x; o.y += w * v[u].y; o.z += w * v[u].z; o.w += w * v[u].w;
+      }
+      M = mn;
+    }
   }
-  int p = 0;
-  for (; p + 4 <= pc; p += 4) MERGE_STEP(4);
-  for (; p < pc; ++p) MERGE_STEP(1);
-#undef MERGE_STEP
   const float inv = 1.0f / L;
   uint2 pk;
   pk.x = pack2bf(o.x * inv, o.y * inv);
