@@ -376,18 +376,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     }
     const uint16_t* kimg = &lds[cur][0];
 
+    // QK: the two key blocks' accumulation chains alternate, and the fragment
+    // reads run four ahead of the MFMAs that use them
     f32x16 s[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
+    bf16x8 kf[2 * KS];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
-            kimg + kb * 2 * NS * 512 + koff + (ks >> 2) * 1024 + kch[ks & 3]);
-        s[kb] = mfma32x32x16(kf, qf[ks], s[kb]);
-      }
+    for (int i = 0; i < 2 * KS; ++i)   // i = 2 ks + kb
+      kf[i] = *reinterpret_cast<const bf16x8*>(kimg + (i & 1) * 2 * NS * 512 + koff + ((i >> 1) >> 2) * 1024 +
+                                               kch[(i >> 1) & 3]);
+#pragma unroll
+    for (int i = 0; i < 2 * KS; ++i) s[i & 1] = mfma32x32x16(kf[i], qf[i >> 1], s[i & 1]);
+    // V fragments of the tile, read now so that their latency hides under the
+    // softmax (vf[q * NS + db]: key step q, dim block db)
+    bf16x8 vf[4 * NS];
+#pragma unroll
+    for (int i = 0; i < 4 * NS; ++i)
+      vf[i] = *reinterpret_cast<const bf16x8*>(kimg + voff + (i / NS) * PAGE + (i % NS) * 512);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * KS - 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     // causal / end-of-range masks matter only on tiles reaching past the first
     // row's position or past the item's last key (wave-uniform test)
     if ((kt + 64 > it.key1) || (kt + 63 > first_pos)) {
@@ -440,10 +455,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
       const bf16x8 pb = as_bf16x8(make_uint4(pk[q >> 1][4 * (q & 1)], pk[q >> 1][4 * (q & 1) + 1],
                                              pk[q >> 1][4 * (q & 1) + 2], pk[q >> 1][4 * (q & 1) + 3]));
 #pragma unroll
-      for (int db = 0; db < NS; ++db) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(kimg + voff + q * PAGE + db * 512);
-        acc[db] = mfma32x32x16(vf, pb, acc[db]);
-      }
+      for (int db = 0; db < NS; ++db) acc[db] = mfma32x32x16(vf[q * NS + db], pb, acc[db]);
     }
   }
 
