@@ -43,6 +43,8 @@ def workload_by_name(name):
         return W.tau_sweep(int(name.rsplit("_", 1)[1]), 0)
     if name == "yi_tau2048":
         return W.yi_tau2048(0)
+    if name == "tiny":
+        return W.tiny(0)
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -134,9 +136,43 @@ def cpu_baseline(wl, stride=4):
     O.layer_forward(wl.dims, w, wl.x.astype(np.float64), b.chunk_len, b.chunk_prefix, b.decode_ctx,
                     b.block_table, cache, rows=rows)
     dt = time.perf_counter() - t0
-    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": _oracle_threads(), "kind": "oracle",
+    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": _oracle_threads(), "cpu_model": _cpu_model(),
+            "kind": "oracle",
             "sample": f"{len(rows)} of the {b.n_tokens} packed tokens (every {stride}th; K/V for all "
                       f"{b.n_tokens}) of the same batch, float64 numpy oracle, {dt:.1f} s"}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline_whole(wl, reps=10):
+    """The oracle on the whole batch, median of `reps` calls (small configs)."""
+    from oracle import hybrid_layer as O
+    b = wl.batch
+    w = O.weights_to_float(wl.weights)
+    ts = []
+    for _ in range(reps):
+        cache = O.PagedCache(b.num_pages, wl.dims.n_kv_heads, wl.dims.page_size, wl.dims.head_dim)
+        for s in range(b.n_seq):
+            if wl.prefix_k[s].shape[0]:
+                cache.load_prefix(b.block_table, s, O.bf16_bits_to_float(wl.prefix_k[s]),
+                                  O.bf16_bits_to_float(wl.prefix_v[s]))
+        t0 = time.perf_counter()
+        O.layer_forward(wl.dims, w, wl.x.astype(np.float64), b.chunk_len, b.chunk_prefix, b.decode_ctx,
+                        b.block_table, cache)
+        ts.append(time.perf_counter() - t0)
+    dt = float(np.median(ts))
+    return {"value": b.n_tokens / dt, "unit": "tokens/s", "cores": _oracle_threads(), "cpu_model": _cpu_model(),
+            "kind": "oracle", "sample": f"all {b.n_tokens} packed tokens, median of {reps} calls "
+                                        f"({dt * 1e3:.1f} ms each), float64 numpy oracle"}
 
 
 def _oracle_threads():
@@ -217,29 +253,30 @@ def bench_batch(wl, name, steps, warmup, copies, calibrate_copy=False):
     torch.cuda.synchronize()
     assert all(e.cuda_event for row in evs.values() for e in row)
     ev_arrays = {i: hb.make_events([e.cuda_event for e in row]) for i, row in evs.items()}
-    # one timing event pair around the timed steps (a timing event between
-    # steps would itself leave a bubble)
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    # step-boundary events (the compute stream already waits there for the
+    # step's metadata copy; with and without them the step time measured the same)
+    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     host_s = np.zeros(steps)
-    t_start.record()
     for i in range(steps):
         h0 = time.perf_counter()
+        step_ev[i].record()
         step(warmup + i, ev_arrays.get(i))
         host_s[i] = time.perf_counter() - h0
-    t_end.record()
+    step_ev[steps].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms = t_start.elapsed_time(t_end) / steps
+    ms = step_ev[0].elapsed_time(step_ev[steps]) / steps
     if calibrate_copy:
         src = torch.empty(64 << 20, dtype=torch.int32, device="cuda").fill_(1)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
-    inst_ms = np.array([evs[i][0].elapsed_time(evs[i][nst]) for i in inst])
+    plain = [i for i in range(steps) if i not in evs] or list(range(steps))
+    step_ms = np.array([step_ev[i].elapsed_time(step_ev[i + 1]) for i in plain])
+    inst_ms = np.array([step_ev[i].elapsed_time(step_ev[i + 1]) for i in inst])
     stage_ms = np.array([[evs[i][k].elapsed_time(evs[i][k + 1]) for k in range(nst)] for i in inst])
     stage_mean = stage_ms.mean(axis=0)
 
@@ -288,6 +325,7 @@ def bench_batch(wl, name, steps, warmup, copies, calibrate_copy=False):
                    "token_budget": b.token_budget, "page_size": d.page_size, "copies_rotated": copies},
         "layer_iters_per_s": round(1e3 / ms, 1),
         "layer_roofline_frac": round(t_roof / (ms * 1e-3), 4),
+        "step_ms_p10_p50_p90": [round(float(np.percentile(step_ms, q)), 5) for q in (10, 50, 90)],
         "instrumented_step_ms_p50": round(float(np.median(inst_ms)), 5),
         "instrumented_steps": len(inst),
         "host_issue_ms_p50": round(float(np.median(host_s)) * 1e3, 4),
@@ -492,7 +530,8 @@ def _long_prompt_cpu_baseline(lp, n_rows=24):
     O.layer_forward(lp.dims, w, lp.prompt_x.astype(np.float64), [L], [0], [],
                     np.ascontiguousarray(lp.block_table[:1]), cache, rows=rows)
     dt = time.perf_counter() - t0
-    return {"value": len(rows) / dt, "unit": "tokens/s (row-sampled)", "cores": _oracle_threads(), "kind": "oracle",
+    return {"value": len(rows) / dt, "unit": "tokens/s (row-sampled)", "cores": _oracle_threads(),
+            "cpu_model": _cpu_model(), "kind": "oracle",
             "sample": f"{len(rows)} rows spread over the {L}-token prompt (K/V for all {L} tokens), float64 numpy "
                       f"oracle, {dt:.1f} s; a full {L}-row oracle pass would take about "
                       f"{dt * L / len(rows) / 3600:.1f} h at this rate (an upper bound: K/V are shared)"}
@@ -569,7 +608,7 @@ def chunk_sweep_bench(args):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mistral_tau512")
     ap.add_argument("--copies", type=int, default=4)
@@ -603,7 +642,10 @@ def main():
     out = bench_batch(wl, args.workload, args.steps, args.warmup, args.copies, args.calibrate_copy)
     out["sclk_mhz"] = sclk_mhz()
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, stride=4 if wl.batch.n_tokens <= 1024 else 32)
+        if args.workload == "tiny":
+            out["cpu_baseline"] = cpu_baseline_whole(wl)
+        else:
+            out["cpu_baseline"] = cpu_baseline(wl, stride=4 if wl.batch.n_tokens <= 1024 else 32)
     print(json.dumps(out), flush=True)
 
 
