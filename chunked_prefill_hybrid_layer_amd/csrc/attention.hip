@@ -75,10 +75,10 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
     const bool _has1 = (KB) + 16 < it.key1;                                                   \
     const int _pg0 = __builtin_amdgcn_readlane(my_pg, _j);                                    \
     const int _pg1 = __builtin_amdgcn_readlane(my_pg, _has1 ? _j + 1 : _j);                   \
-    const uint16_t* _K0 = a.k_cache + ((size_t)_pg0 * nkv + kvh) * hs + r * 32 + qd * 8;      \
-    const uint16_t* _K1 = a.k_cache + ((size_t)_pg1 * nkv + kvh) * hs + r * 32 + qd * 8;      \
-    const uint16_t* _V0 = a.v_cache + ((size_t)_pg0 * nkv + kvh) * hs + r * 16 + qd * 4;      \
-    const uint16_t* _V1 = a.v_cache + ((size_t)_pg1 * nkv + kvh) * hs + r * 16 + qd * 4;      \
+    const uint16_t* _K0 = static_cast<const uint16_t*>(a.k_cache) + ((size_t)_pg0 * nkv + kvh) * hs + r * 32 + qd * 8;      \
+    const uint16_t* _K1 = static_cast<const uint16_t*>(a.k_cache) + ((size_t)_pg1 * nkv + kvh) * hs + r * 32 + qd * 8;      \
+    const uint16_t* _V0 = static_cast<const uint16_t*>(a.v_cache) + ((size_t)_pg0 * nkv + kvh) * hs + r * 16 + qd * 4;      \
+    const uint16_t* _V1 = static_cast<const uint16_t*>(a.v_cache) + ((size_t)_pg1 * nkv + kvh) * hs + r * 16 + qd * 4;      \
     _Pragma("unroll") for (int kk = 0; kk < KK; ++kk)                                         \
         k0##SFX[kk] = load_stream16(_K0 + kk * 512); \
     _Pragma("unroll") for (int jj = 0; jj < NJ; ++jj)                                         \
@@ -326,8 +326,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     if (4 * tile + wave < npg) {
       const int page = __builtin_amdgcn_readlane(((tile >> 6) & 1) ? pw1 : pw0, tile & 63);
       const size_t base = ((size_t)page * nkv + kvh) * PAGE;
-      const uint16_t* kg = a.k_cache + base;
-      const uint16_t* vg = a.v_cache + base + vdma;
+      const uint16_t* kg = static_cast<const uint16_t*>(a.k_cache) + base;
+      const uint16_t* vg = static_cast<const uint16_t*>(a.v_cache) + base + vdma;
       uint16_t* dst = &lds[st][0];
       // K: load s = 2 h + b covers half h, slots 8 b .. 8 b + 7 (page image
       // [half][slot][64]: element offset 512 s within the page's image)

@@ -119,7 +119,9 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const uint16_t* __restri
 }
 
 hb_status launch_kv_append(const hb_dims& d, const DevMeta& m, int n_tokens, const uint16_t* k,
-                           const uint16_t* v, int64_t row_stride, uint16_t* kc, uint16_t* vc, stream_t s) {
+                           const uint16_t* v, int64_t row_stride, void* kcv, void* vcv, stream_t s) {
+  uint16_t* kc = static_cast<uint16_t*>(kcv);
+  uint16_t* vc = static_cast<uint16_t*>(vcv);
   if (n_tokens <= 0 || m.n_append_runs <= 0) return HB_OK;
   const int64_t items = (int64_t)m.n_append_runs * d.n_kv_heads;
   const unsigned blocks = (unsigned)((items + 3) / 4);

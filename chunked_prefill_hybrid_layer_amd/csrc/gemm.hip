@@ -141,14 +141,16 @@ __device__ __forceinline__ void qkv_store4(const GemmArgs& g, int m, int n, cons
       const int kvh = (c - qdim) / d;
       const int sl = g.slot[m];
       // K page block: [d/32][16 slots][32]; dims i0 .. i0 + 3 share a 32-dim slice
-      uint16_t* kb = g.k_cache + ((size_t)(sl >> 4) * g.n_kv_heads + kvh) * 16 * d + (sl & 15) * 32;
+      uint16_t* kb = static_cast<uint16_t*>(g.k_cache) + ((size_t)(sl >> 4) * g.n_kv_heads + kvh) * 16 * d +
+                     (sl & 15) * 32;
       *reinterpret_cast<uint2*>(kb + (i0 >> 5) * 512 + (i0 & 31)) = lo;
       *reinterpret_cast<uint2*>(kb + ((i0 + half) >> 5) * 512 + ((i0 + half) & 31)) = hi;
     }
   } else {
     const int kvh = (c - qdim - kdim) / d;
     const int sl = g.slot[m];
-    uint16_t* vp = g.v_cache + (((size_t)(sl >> 4) * g.n_kv_heads + kvh) * d + i0) * 16 + (sl & 15);
+    uint16_t* vp = static_cast<uint16_t*>(g.v_cache) + (((size_t)(sl >> 4) * g.n_kv_heads + kvh) * d + i0) * 16 +
+                   (sl & 15);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       vp[e * 16] = f2bf(x0[e]);

@@ -74,8 +74,7 @@ typedef struct ihipStream_t* stream_t;
 hb_status launch_rmsnorm(const float* x, const uint16_t* gain, uint16_t* out, int rows, int hidden,
                          float eps, stream_t s);
 hb_status launch_kv_append(const hb_dims& d, const DevMeta& m, int n_tokens, const uint16_t* k,
-                           const uint16_t* v, int64_t row_stride, uint16_t* kc, uint16_t* vc,
-                           stream_t s);
+                           const uint16_t* v, int64_t row_stride, void* kc, void* vc, stream_t s);
 
 enum GemmMode { kGemmQkvRope = 0, kGemmResidual = 1, kGemmSwiglu = 2 };
 
@@ -96,12 +95,14 @@ struct GemmArgs {
   int ldo;
   // SwiGLU / QKV bf16 output
   uint16_t* out_b;
-  // QKV epilogue
+  // QKV epilogue; the caches hold bf16, or FP8 e4m3 codes of x * inv_scale
   const float* rope;
   const int32_t* tok_pos;
   const int32_t* slot;
-  uint16_t* k_cache;
-  uint16_t* v_cache;
+  void* k_cache;
+  void* v_cache;
+  int kv_fp8;
+  float k_inv_scale, v_inv_scale;
   int n_q_heads, n_kv_heads, head_dim;
   // split-K partials [splits][M][N] fp32 (used when the plan splits K)
   float* part;
@@ -119,8 +120,10 @@ hb_status launch_splitk_reduce(const float* part, int splits, const float* res, 
 
 struct AttnArgs {
   const uint16_t* q;       // [T][n_q * d]
-  const uint16_t* k_cache;
-  const uint16_t* v_cache;
+  const void* k_cache;     // bf16, or FP8 e4m3 codes (value = code * scale)
+  const void* v_cache;
+  int kv_fp8;
+  float k_scale, v_scale;
   DevMeta meta;
   int max_pages;
   int n_q_heads, n_kv_heads, head_dim, group;

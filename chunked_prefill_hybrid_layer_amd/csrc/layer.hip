@@ -43,9 +43,10 @@ using namespace hb;
   } while (0)
 
 extern "C" hb_status hb_kv_append(const hb_dims* dims, const void* meta_host, const void* meta_dev,
-                                  const uint16_t* k, const uint16_t* v, int64_t row_stride, uint16_t* k_cache,
-                                  uint16_t* v_cache, void* stream) {
+                                  const uint16_t* k, const uint16_t* v, int64_t row_stride, void* k_cache,
+                                  void* v_cache, void* stream) {
   HB_TRY(check_dims(dims));
+  if (dims->kv_fp8) return fail(HB_E_SHAPE, "kv_append: FP8 KV cache not built yet");
   HB_TRY(check_meta(dims, meta_host));
   if (!meta_dev || !k || !v || !k_cache || !v_cache) return fail(HB_E_NULL, "kv_append: NULL pointer");
   if (row_stride < (int64_t)dims->n_kv_heads * dims->head_dim || row_stride % 8)
@@ -59,10 +60,11 @@ extern "C" hb_status hb_kv_append(const hb_dims* dims, const void* meta_host, co
 
 extern "C" hb_status hb_layer_forward(const hb_dims* dims, const hb_weights* w, const void* meta_host,
                                       const void* meta_dev, const float* rope_cs, int32_t rope_max_pos,
-                                      const float* x, float* y, uint16_t* k_cache, uint16_t* v_cache,
+                                      const float* x, float* y, void* k_cache, void* v_cache,
                                       void* workspace, size_t workspace_bytes, void* stream,
                                       void* const* stage_events) {
   HB_TRY(check_dims(dims));
+  if (dims->kv_fp8) return fail(HB_E_SHAPE, "layer_forward: FP8 KV cache not built yet");
   HB_TRY(check_meta(dims, meta_host));
   if (!w || !meta_dev || !rope_cs || !x || !y || !k_cache || !v_cache || !workspace)
     return fail(HB_E_NULL, "layer_forward: NULL pointer");

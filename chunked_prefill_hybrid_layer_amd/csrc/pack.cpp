@@ -11,6 +11,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <new>
 #include <vector>
 
@@ -40,6 +41,10 @@ hb_status check_dims(const hb_dims* d) {
   if (d->hidden > 16384) return fail(HB_E_SHAPE, "hidden above 16384");
   if (d->page_size != kPageSize) return fail(HB_E_SHAPE, "page_size must be 16");
   if (!(d->rms_eps >= 0.0f) || !(d->rope_theta > 0.0f)) return fail(HB_E_SHAPE, "bad eps or theta");
+  if (d->kv_fp8 != 0 && d->kv_fp8 != 1) return fail(HB_E_SHAPE, "kv_fp8 must be 0 or 1");
+  if (d->kv_fp8 && !(std::isfinite(d->k_scale) && d->k_scale > 0.0f && std::isfinite(d->v_scale) &&
+                     d->v_scale > 0.0f))
+    return fail(HB_E_SHAPE, "FP8 KV cache needs finite positive k_scale and v_scale");
   return HB_OK;
 }
 

@@ -39,7 +39,8 @@ class HbError(RuntimeError):
 class Dims(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("ffn_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
-                ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float)]
+                ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float), ("kv_fp8", ctypes.c_int32),
+                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
 
 
 class Weights(ctypes.Structure):
@@ -116,7 +117,8 @@ def _check(status: int):
 def make_dims(d) -> Dims:
     """hb_dims from any object with the layer-shape attributes."""
     return Dims(d.hidden, d.n_q_heads, d.n_kv_heads, d.head_dim, d.ffn_dim, d.page_size,
-                float(d.rms_eps), float(d.rope_theta))
+                float(d.rms_eps), float(d.rope_theta), int(getattr(d, "kv_fp8", 0)),
+                float(getattr(d, "k_scale", 1.0)), float(getattr(d, "v_scale", 1.0)))
 
 
 def _i32(a) -> np.ndarray:

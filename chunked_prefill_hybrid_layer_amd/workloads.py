@@ -100,6 +100,9 @@ class Dims:
     page_size: int = PAGE_SIZE
     rms_eps: float = 1e-5
     rope_theta: float = 10000.0
+    kv_fp8: int = 0            # 1: FP8 e4m3 KV cache with the scales below
+    k_scale: float = 1.0
+    v_scale: float = 1.0
 
     @property
     def group(self) -> int:

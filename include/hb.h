@@ -23,10 +23,11 @@
  *   - A chunk piece of length L with prefix P holds positions [P, P+L) of its
  *     prompt; a decode with context C is one token at position C (C tokens are
  *     already cached; it attends C+1 keys, itself included).
- *   - KV cache (bf16), two separate device arrays, page size p = 16:
+ *   - KV cache (bf16, or FP8 e4m3 with dims->kv_fp8), two separate device
+ *     arrays, page size p = 16:
  *       K: [num_pages][n_kv_heads][head_dim/32][p][32]   (32-dim slices, each
  *          token-major: dims 32c..32c+31 of a page's 16 tokens are one
- *          contiguous 1 KB block)
+ *          contiguous block, 1 KB in bf16, 512 B in FP8)
  *       V: [num_pages][n_kv_heads][head_dim][p]   (dim-major inside a page)
  *     Position pos of sequence s lives in page block_table[s][pos / p] at
  *     in-page slot pos % p.  Unused block-table entries are -1 and are never
@@ -81,6 +82,14 @@ typedef struct {
   int32_t page_size;
   float rms_eps;     /* RMSNorm epsilon, e.g. 1e-5 */
   float rope_theta;  /* rotary base, e.g. 1e4 */
+  /* KV cache element type.  0: bf16.  1: FP8 e4m3 (OCP e4m3fn: exponent bias
+   * 7, largest finite 448, no infinities, NaN 0x7F/0xFF), one byte per
+   * element: the cache holds e4m3(x / scale) rounded to nearest even and
+   * saturated to +-448, and attention reads code value * scale.  The scales
+   * are per layer and come from the caller (ignored for bf16). */
+  int32_t kv_fp8;
+  float k_scale;
+  float v_scale;
 } hb_dims;
 
 /* Device pointers to the layer's parameters (bf16 bits).  Projection
@@ -229,7 +238,7 @@ size_t hb_workspace_bytes(const hb_dims *dims, const void *meta_host);
  * from hb_pack_metadata and its byte-identical device copy. */
 hb_status hb_kv_append(const hb_dims *dims, const void *meta_host, const void *meta_dev,
                        const uint16_t *k, const uint16_t *v, int64_t row_stride,
-                       uint16_t *k_cache, uint16_t *v_cache, void *stream);
+                       void *k_cache, void *v_cache, void *stream);
 
 /* One decoder-layer forward over the hybrid batch (device):
  *   xn  = RMSNorm(x) * g_attn                                  (bf16)
@@ -256,7 +265,7 @@ hb_status hb_kv_append(const hb_dims *dims, const void *meta_host, const void *m
     "o_proj_residual", "rmsnorm_ffn", "gate_up_swiglu", "down_residual" }
 hb_status hb_layer_forward(const hb_dims *dims, const hb_weights *w, const void *meta_host,
                            const void *meta_dev, const float *rope_cs, int32_t rope_max_pos,
-                           const float *x, float *y, uint16_t *k_cache, uint16_t *v_cache,
+                           const float *x, float *y, void *k_cache, void *v_cache,
                            void *workspace, size_t workspace_bytes, void *stream,
                            void *const *stage_events);
 

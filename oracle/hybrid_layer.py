@@ -179,6 +179,50 @@ def hybrid_batch_budget(n_decodes: int, chunk_takes: Sequence[int], tau: int):
 # the oracle's paged KV cache
 
 
+# ----------------------------------------------------------------------------
+# FP8 e4m3 KV cache (optional storage type)
+#
+# OCP 8-bit floating point, E4M3 ("e4m3fn"): sign bit, 4 exponent bits with
+# bias 7, 3 mantissa bits.  Exponent field 0 holds subnormals (m/8) * 2^-6;
+# other fields (1 + m/8) * 2^(e - 7).  No infinities; code 0x7F (and 0xFF) is
+# NaN, so the largest finite magnitude is 1.75 * 2^8 = 448 (code 0x7E).
+# Reading for the cache: a value x is stored as e4m3(x / scale), rounded to
+# the nearest code value with ties to the even code, magnitudes past 448
+# saturating to 448; it is read back as value(code) * scale.
+
+
+def _e4m3_magnitude(code: int) -> float:
+    e, m = code >> 3, code & 7
+    if e == 0:
+        return (m / 8.0) * 2.0 ** -6
+    return (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+_E4M3_MAG = np.array([_e4m3_magnitude(c) for c in range(127)])   # codes 0x00..0x7E, increasing
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """float array -> uint8 e4m3 codes (round to nearest, ties to even code,
+    saturating at +-448, NaN -> 0x7F with the input's sign)."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), _E4M3_MAG[-1])
+    hi = np.clip(np.searchsorted(_E4M3_MAG, a, side="left"), 0, 126)   # first code >= a
+    lo = np.maximum(hi - 1, 0)
+    d_hi = _E4M3_MAG[hi] - a
+    d_lo = a - _E4M3_MAG[lo]
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    code = np.where(np.isnan(x), np.uint8(0x7F), code)
+    return (code | (np.signbit(x).astype(np.uint8) << 7)).astype(np.uint8)
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """uint8 e4m3 codes -> float64 values (NaN for 0x7F / 0xFF)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    mag = np.concatenate([_E4M3_MAG, [np.nan]])[c & 0x7F]
+    return np.where(c & 0x80, -mag, mag)
+
+
 class PagedCache:
     """K and V pages in logical order [kv_head][slot][d], float64.
 
@@ -186,12 +230,18 @@ class PagedCache:
     first time something is written to it, so a cache over a large pool costs
     only the pages actually used.  Reading a slot nobody wrote returns NaN."""
 
-    def __init__(self, num_pages: int, n_kv: int, page_size: int, head_dim: int):
+    def __init__(self, num_pages: int, n_kv: int, page_size: int, head_dim: int, kv_fp8: int = 0,
+                 k_scale: float = 1.0, v_scale: float = 1.0):
         self.num_pages = num_pages
         self.n_kv = n_kv
         self.page_size = page_size
         self.head_dim = head_dim
         self.pages: Dict[int, np.ndarray] = {}   # page -> [2 (K, V)][n_kv][slot][d]
+        # FP8 storage: written values are quantised (e4m3(x / scale)); pages
+        # hold the values read back, codes the stored bytes (0x7F where unwritten)
+        self.kv_fp8 = int(kv_fp8)
+        self.scales = (float(k_scale), float(v_scale))
+        self.codes: Dict[int, np.ndarray] = {}
 
     def _page(self, page: int) -> np.ndarray:
         if not 0 <= page < self.num_pages:
@@ -205,6 +255,12 @@ class PagedCache:
     def write(self, block_table, seq: int, pos: int, k_row: np.ndarray, v_row: np.ndarray):
         page, slot = page_of(block_table, seq, pos, self.page_size)
         pg = self._page(page)
+        if self.kv_fp8:
+            cd = self.codes.setdefault(page, np.full(pg.shape, 0x7F, dtype=np.uint8))
+            for i, (row, sc) in enumerate(((k_row, self.scales[0]), (v_row, self.scales[1]))):
+                cd[i, :, slot, :] = e4m3_encode(np.asarray(row, dtype=np.float64) / sc)
+                pg[i, :, slot, :] = e4m3_decode(cd[i, :, slot, :]) * sc
+            return
         pg[0, :, slot, :] = k_row
         pg[1, :, slot, :] = v_row
 
@@ -378,9 +434,15 @@ def layer_forward(dims, w: Dict[str, np.ndarray], x: np.ndarray, chunk_len, chun
     k, f = linear(xn, w["w_k"]); flops += f
     v, f = linear(xn, w["w_v"]); flops += f
     q, f = linear(xn[rows], w["w_q"]); flops += f
-    k = act(rope(k.reshape(T, nkv, d), lay.pos, dims.rope_theta))
-    v = act(v.reshape(T, nkv, d))
+    k = rope(k.reshape(T, nkv, d), lay.pos, dims.rope_theta)
+    v = v.reshape(T, nkv, d)
     q = act(rope(q.reshape(len(rows), nq, d), lay.pos[rows], dims.rope_theta))
+    # a bf16 cache stores bf16(k), bf16(v); an FP8 cache quantises the unrounded
+    # values itself (e4m3(x / scale))
+    if getattr(dims, "kv_fp8", 0) != cache.kv_fp8:
+        raise ValueError("cache storage type does not match dims.kv_fp8")
+    if not cache.kv_fp8:
+        k, v = act(k), act(v)
 
     # a4: new K/V go into the paged cache at their sequence positions
     for t in range(T):

@@ -437,3 +437,62 @@ def test_row_block_evaluation_is_bit_identical():
     assert np.array_equal(a, b, equal_nan=True)
     g = rng.standard_normal(1024)
     assert np.array_equal(O.rmsnorm(x[6:], g, 1e-5), O._rmsnorm(x[6:], g, 1e-5))
+
+
+# ---------------------------------------------------------------- FP8 e4m3 KV storage
+
+def test_e4m3_code_points_from_the_format_definition():
+    """OCP 8-bit floating point E4M3: sign, 4 exponent bits (bias 7), 3
+    mantissa bits, subnormals below 2^-6, NaN at 0x7F, largest finite 448."""
+    cases = {0.0: 0x00, 1.0: 0x38, -2.0: 0xC0, 448.0: 0x7E, 2.0 ** -6: 0x08, 2.0 ** -9: 0x01,
+             0.5: 0x30, 1.125: 0x39, 240.0: 0x77, 256.0: 0x78, 3.25: 0x45, -0.875: 0xB6}
+    for x, code in cases.items():
+        assert int(O.e4m3_encode(x)) == code, (x, hex(int(O.e4m3_encode(x))))
+        assert float(O.e4m3_decode(np.uint8(code))) == x
+    assert int(O.e4m3_encode(-0.0)) == 0x80
+    assert np.isnan(O.e4m3_decode(np.uint8(0x7F))) and np.isnan(O.e4m3_decode(np.uint8(0xFF)))
+
+
+def test_e4m3_rounds_to_nearest_even_and_saturates():
+    # midpoints go to the even code (the code's last bit is the mantissa's)
+    ties = {1.0625: 0x38, 1.1875: 0x3A, 2.0 ** -10: 0x00, 3 * 2.0 ** -10: 0x02,
+            7.5 * 2.0 ** -9: 0x08, 464.0: 0x7E, 2.5 * 2.0 ** -9: 0x02}
+    for x, code in ties.items():
+        assert int(O.e4m3_encode(x)) == code, (x, hex(int(O.e4m3_encode(x))))
+    # just off a midpoint goes to the nearer code
+    assert int(O.e4m3_encode(1.0625 + 1e-9)) == 0x39
+    assert int(O.e4m3_encode(1.1875 - 1e-9)) == 0x39
+    # beyond the largest finite magnitude: saturation, not NaN
+    for x in (449.0, 480.0, 1e6, np.inf):
+        assert int(O.e4m3_encode(x)) == 0x7E and int(O.e4m3_encode(-x)) == 0xFE
+
+
+def test_e4m3_round_trip_and_monotonicity():
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
+    vals = O.e4m3_decode(codes)
+    assert np.all(O.e4m3_encode(vals) == np.where(vals == 0, codes, codes))   # -0 keeps its sign bit
+    pos = O.e4m3_decode(np.arange(127, dtype=np.uint8))
+    assert np.all(np.diff(pos) > 0)
+    # every value maps to a code whose value is within half a step of it
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal(20000) * 2.0 ** rng.integers(-12, 9, 20000)
+    x = x[np.abs(x) <= 448]
+    y = O.e4m3_decode(O.e4m3_encode(x))
+    mag = np.abs(x)
+    idx = np.clip(np.searchsorted(pos, mag), 1, 126)
+    step = pos[idx] - pos[idx - 1]
+    assert np.all(np.abs(y - x) <= step / 2 + 1e-300)
+
+
+def test_fp8_cache_stores_quantised_values():
+    c = O.PagedCache(4, 2, 16, 64, kv_fp8=1, k_scale=0.0625, v_scale=0.25)
+    bt = np.array([[2, 0]], dtype=np.int32)
+    k = np.linspace(-3, 3, 128).reshape(2, 64)
+    v = np.linspace(-100, 100, 128).reshape(2, 64)
+    c.write(bt, 0, 5, k, v)
+    kk, vv = c.gather(bt, 0, 6)
+    assert np.array_equal(kk[5], O.e4m3_decode(O.e4m3_encode(k / 0.0625)) * 0.0625)
+    assert np.array_equal(vv[5], O.e4m3_decode(O.e4m3_encode(v / 0.25)) * 0.25)
+    assert np.all(np.isnan(kk[:5])) and np.all(c.codes[2][:, :, :5, :] == 0x7F)
+    # half an e4m3 step: |x / scale| <= 48 lies in binades up to [32, 64), step 4
+    assert np.max(np.abs(kk[5] - k)) <= 0.0625 * 4 / 2
