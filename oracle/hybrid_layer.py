@@ -42,6 +42,14 @@ pages are silent:
     output once to that storage type (round to nearest even).  With
     ``storage="exact"`` nothing is rounded.
 
+FP8 KV storage (kv_fp8 = 1; not on the pages, which keep K/V in the layer's
+own precision): each K or V element is stored as the OCP e4m3fn code of
+x / scale, with the per-layer K and V scales the caller passes (float32).
+Codes round to nearest with ties to the even code and saturate at +-448 (the
+format's largest finite value; 0x7F / 0xFF are NaN and mark unwritten slots).
+The quotient x / scale is taken in single precision (see ``fp8_quotient``), and
+attention reads code * scale.
+
 Page layout of the oracle's own cache: ``k[page][kv_head][slot][d]`` (logical
 order, float64); a sequence's position p lives in page
 ``block_table[s][p // page_size]`` at slot ``p % page_size`` ([notes] §3.5,
@@ -223,6 +231,16 @@ def e4m3_decode(codes) -> np.ndarray:
     return np.where(c & 0x80, -mag, mag)
 
 
+def fp8_quotient(x, scale) -> np.ndarray:
+    """x / scale as the FP8 code is taken from it: in single precision, x
+    rounded to float32 times the float32 reciprocal of the float32 scale.  The
+    pages fix no precision for this step; where x / scale lies at (or within
+    float32 rounding of) the midpoint of two codes, the precision decides the
+    code, so the kernels' single-precision product is the definition here."""
+    inv = np.float32(1.0) / np.float32(scale)
+    return (np.asarray(x, dtype=np.float64).astype(np.float32) * inv).astype(np.float64)
+
+
 class PagedCache:
     """K and V pages in logical order [kv_head][slot][d], float64.
 
@@ -238,9 +256,10 @@ class PagedCache:
         self.head_dim = head_dim
         self.pages: Dict[int, np.ndarray] = {}   # page -> [2 (K, V)][n_kv][slot][d]
         # FP8 storage: written values are quantised (e4m3(x / scale)); pages
-        # hold the values read back, codes the stored bytes (0x7F where unwritten)
+        # hold the values read back, codes the stored bytes (0x7F where unwritten).
+        # The scales are single-precision numbers (as a caller hands them over)
         self.kv_fp8 = int(kv_fp8)
-        self.scales = (float(k_scale), float(v_scale))
+        self.scales = (np.float32(k_scale), np.float32(v_scale))
         self.codes: Dict[int, np.ndarray] = {}
 
     def _page(self, page: int) -> np.ndarray:
@@ -258,8 +277,8 @@ class PagedCache:
         if self.kv_fp8:
             cd = self.codes.setdefault(page, np.full(pg.shape, 0x7F, dtype=np.uint8))
             for i, (row, sc) in enumerate(((k_row, self.scales[0]), (v_row, self.scales[1]))):
-                cd[i, :, slot, :] = e4m3_encode(np.asarray(row, dtype=np.float64) / sc)
-                pg[i, :, slot, :] = e4m3_decode(cd[i, :, slot, :]) * sc
+                cd[i, :, slot, :] = e4m3_encode(fp8_quotient(row, sc))
+                pg[i, :, slot, :] = e4m3_decode(cd[i, :, slot, :]) * np.float64(sc)
             return
         pg[0, :, slot, :] = k_row
         pg[1, :, slot, :] = v_row

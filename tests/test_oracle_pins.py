@@ -496,3 +496,23 @@ def test_fp8_cache_stores_quantised_values():
     assert np.all(np.isnan(kk[:5])) and np.all(c.codes[2][:, :, :5, :] == 0x7F)
     # half an e4m3 step: |x / scale| <= 48 lies in binades up to [32, 64), step 4
     assert np.max(np.abs(kk[5] - k)) <= 0.0625 * 4 / 2
+
+
+def test_fp8_quotient_is_single_precision():
+    """Worked by hand.  Scale 0.03 as float32 is 0.029999999329447746; its
+    reciprocal 33.33333407839... rounds to the float32 33.333335876464844
+    (neighbours 33.333332061767578 and 33.333335876464844, 2^-18 apart).
+    0.75 times that is 25 + 2^-19 exactly, a float32, just above the midpoint
+    25 of the codes 24 (0x5C) and 26 (0x5D): code 0x5D.  The float64 quotient
+    0.75 / 0.03 is exactly 25, which would tie to the even code 0x5C."""
+    q = O.fp8_quotient(np.array([0.75, -0.75]), 0.03)
+    assert q[0] == 25 + 2.0 ** -19 and q[1] == -q[0]
+    assert list(O.e4m3_encode(q)) == [0x5D, 0xDD]
+    assert int(O.e4m3_encode(0.75 / 0.03)) == 0x5C
+    # a power-of-two scale divides exactly
+    x = np.array([1.0625, -3.0, 2.0 ** -10, 1000.0])
+    assert np.array_equal(O.fp8_quotient(x, 2.0 ** -4), x * 16)
+    c = O.PagedCache(1, 1, 16, 32, kv_fp8=1, k_scale=0.03, v_scale=0.03)
+    c.write(np.array([[0]], dtype=np.int32), 0, 0, np.full((1, 32), 0.75), np.full((1, 32), -0.75))
+    assert np.all(c.codes[0][0] == np.where(np.arange(16)[:, None] == 0, 0x5D, 0x7F))
+    assert np.all(c.pages[0][1, 0, 0] == -26 * np.float64(np.float32(0.03)))
