@@ -61,7 +61,8 @@ def stage_model(wl):
     for c, n in zip(b.chunk_prefix, b.chunk_len):
         chunk_pairs += int(n) * int(c) + int(n) * (int(n) + 1) // 2
     dec_pairs = int(np.sum(b.decode_ctx.astype(np.int64) + 1))
-    kv_bytes_per_key = nkv * D * 2 * 2                      # K and V, bf16
+    kv_elem = 1 if getattr(d, "kv_fp8", 0) else 2            # bytes per cached K/V element
+    kv_bytes_per_key = nkv * D * 2 * kv_elem                # K and V
     chunk_kv_keys = int(np.sum(cached[:b.n_chunks] + new[:b.n_chunks]))
     blob, _ = hb.pack_metadata(hb.make_dims(d), b.chunk_len, b.chunk_prefix, b.decode_ctx, b.block_table,
                                b.num_pages, b.token_budget)
@@ -70,7 +71,8 @@ def stage_model(wl):
     m = {
         "rmsnorm_attn": (0, T * H * 4 + T * H * 2 + H * 2, "hbm"),
         "qkv_rope_append": (2 * T * H * (nq + 2 * nkv) * D,
-                            (nq + 2 * nkv) * D * H * 2 + T * H * 2 + T * (nq + 2 * nkv) * D * 2, "mfma"),
+                            (nq + 2 * nkv) * D * H * 2 + T * H * 2 + T * nq * D * 2 + T * 2 * nkv * D * kv_elem,
+                            "mfma"),
         "attn_chunk": (4 * chunk_pairs * nq * D, chunk_kv_keys * kv_bytes_per_key, "mfma"),
         "attn_decode": (4 * dec_pairs * nq * D, dec_pairs * kv_bytes_per_key, "hbm"),
         "attn_merge": (0, part_bytes + T * nq * D * 2, "hbm"),
@@ -126,7 +128,7 @@ def cpu_baseline(wl, stride=4):
     rows = np.arange(0, b.n_tokens, stride)
     lay = O.token_layout(b.chunk_len, b.chunk_prefix, b.decode_ctx)
     need = sorted(set(int(s) for s in lay.seq[rows]))
-    cache = O.PagedCache(b.num_pages, wl.dims.n_kv_heads, wl.dims.page_size, wl.dims.head_dim)
+    cache = _oracle_cache(O, wl)
     for s in need:
         if wl.prefix_k[s].shape[0]:
             cache.load_prefix(b.block_table, s, O.bf16_bits_to_float(wl.prefix_k[s]),
@@ -140,6 +142,12 @@ def cpu_baseline(wl, stride=4):
             "kind": "oracle",
             "sample": f"{len(rows)} of the {b.n_tokens} packed tokens (every {stride}th; K/V for all "
                       f"{b.n_tokens}) of the same batch, float64 numpy oracle, {dt:.1f} s"}
+
+
+def _oracle_cache(O, wl):
+    d = wl.dims
+    return O.PagedCache(wl.batch.num_pages, d.n_kv_heads, d.page_size, d.head_dim, kv_fp8=d.kv_fp8,
+                        k_scale=d.k_scale, v_scale=d.v_scale)
 
 
 def _cpu_model():
@@ -160,7 +168,7 @@ def cpu_baseline_whole(wl, reps=10):
     w = O.weights_to_float(wl.weights)
     ts = []
     for _ in range(reps):
-        cache = O.PagedCache(b.num_pages, wl.dims.n_kv_heads, wl.dims.page_size, wl.dims.head_dim)
+        cache = _oracle_cache(O, wl)
         for s in range(b.n_seq):
             if wl.prefix_k[s].shape[0]:
                 cache.load_prefix(b.block_table, s, O.bf16_bits_to_float(wl.prefix_k[s]),
@@ -322,7 +330,9 @@ def bench_batch(wl, name, steps, warmup, copies, calibrate_copy=False):
                    "tokens": T, "chunks": [int(c) for c in b.chunk_len],
                    "chunk_prefix": [int(c) for c in b.chunk_prefix], "decodes": b.n_decodes,
                    "decode_ctx_mean": float(np.mean(b.decode_ctx)) if b.n_decodes else 0.0,
-                   "token_budget": b.token_budget, "page_size": d.page_size, "copies_rotated": copies},
+                   "token_budget": b.token_budget, "page_size": d.page_size, "copies_rotated": copies,
+                   "kv_cache": ("fp8_e4m3 (k_scale %g, v_scale %g)" % (d.k_scale, d.v_scale)) if d.kv_fp8
+                   else "bf16"},
         "layer_iters_per_s": round(1e3 / ms, 1),
         "layer_roofline_frac": round(t_roof / (ms * 1e-3), 4),
         "step_ms_p10_p50_p90": [round(float(np.percentile(step_ms, q)), 5) for q in (10, 50, 90)],
@@ -613,6 +623,8 @@ def main():
     ap.add_argument("--workload", default="mistral_tau512")
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kv-fp8", action="store_true",
+                    help="FP8 e4m3 KV cache (k_scale 2^-4, v_scale 2^-3) instead of bf16")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, copy 256 MiB device-to-device once (counter calibration)")
     ap.add_argument("--sweep-tau", action="store_true", help="token-budget sweep, one line per tau")
@@ -639,7 +651,12 @@ def main():
     if args.chunk_sweep:
         return chunk_sweep_bench(args)
     wl = workload_by_name(args.workload)
-    out = bench_batch(wl, args.workload, args.steps, args.warmup, args.copies, args.calibrate_copy)
+    name = args.workload
+    if args.kv_fp8:
+        from chunked_prefill_hybrid_layer_amd import workloads as W
+        wl = W.with_kv_fp8(wl)
+        name += "_kvfp8"
+    out = bench_batch(wl, name, args.steps, args.warmup, args.copies, args.calibrate_copy)
     out["sclk_mhz"] = sclk_mhz()
     if not args.no_cpu_baseline:
         if args.workload == "tiny":

@@ -75,19 +75,29 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
     const bool _has1 = (KB) + 16 < it.key1;                                                   \
     const int _pg0 = __builtin_amdgcn_readlane(my_pg, _j);                                    \
     const int _pg1 = __builtin_amdgcn_readlane(my_pg, _has1 ? _j + 1 : _j);                   \
-    const uint16_t* _K0 = static_cast<const uint16_t*>(a.k_cache) + ((size_t)_pg0 * nkv + kvh) * hs + r * 32 + qd * 8;      \
-    const uint16_t* _K1 = static_cast<const uint16_t*>(a.k_cache) + ((size_t)_pg1 * nkv + kvh) * hs + r * 32 + qd * 8;      \
-    const uint16_t* _V0 = static_cast<const uint16_t*>(a.v_cache) + ((size_t)_pg0 * nkv + kvh) * hs + r * 16 + qd * 4;      \
-    const uint16_t* _V1 = static_cast<const uint16_t*>(a.v_cache) + ((size_t)_pg1 * nkv + kvh) * hs + r * 16 + qd * 4;      \
+    /* element offsets of this lane's fragments (bytes in FP8, where each K   \
+       and V^T fragment is half as many bytes and is widened to bf16 exactly) */ \
+    const size_t _k0 = ((size_t)_pg0 * nkv + kvh) * hs + r * 32 + qd * 8;                    \
+    const size_t _k1 = ((size_t)_pg1 * nkv + kvh) * hs + r * 32 + qd * 8;                    \
+    const size_t _v0 = ((size_t)_pg0 * nkv + kvh) * hs + r * 16 + qd * 4;                    \
+    const size_t _v1 = ((size_t)_pg1 * nkv + kvh) * hs + r * 16 + qd * 4;                    \
+    const uint16_t* _Kb = static_cast<const uint16_t*>(a.k_cache);                           \
+    const uint16_t* _Vb = static_cast<const uint16_t*>(a.v_cache);                           \
+    const uint8_t* _K8 = static_cast<const uint8_t*>(a.k_cache);                             \
+    const uint8_t* _V8 = static_cast<const uint8_t*>(a.v_cache);                             \
     _Pragma("unroll") for (int kk = 0; kk < KK; ++kk)                                         \
-        k0##SFX[kk] = load_stream16(_K0 + kk * 512); \
+        k0##SFX[kk] = F8 ? fp8x8_bf16x8(load_stream8(_K8 + _k0 + kk * 512))                   \
+                         : load_stream16(_Kb + _k0 + kk * 512);                               \
     _Pragma("unroll") for (int jj = 0; jj < NJ; ++jj)                                         \
-        v0##SFX[jj] = load_stream8(_V0 + jj * 256); \
+        v0##SFX[jj] = F8 ? fp8x4_bf16x4(load_stream4(_V8 + _v0 + jj * 256))                   \
+                         : load_stream8(_Vb + _v0 + jj * 256);                                \
     if (_has1) {                                                                              \
       _Pragma("unroll") for (int kk = 0; kk < KK; ++kk)                                       \
-          k1##SFX[kk] = load_stream16(_K1 + kk * 512); \
+          k1##SFX[kk] = F8 ? fp8x8_bf16x8(load_stream8(_K8 + _k1 + kk * 512))                 \
+                           : load_stream16(_Kb + _k1 + kk * 512);                             \
       _Pragma("unroll") for (int jj = 0; jj < NJ; ++jj)                                       \
-          v1##SFX[jj] = load_stream8(_V1 + jj * 256); \
+          v1##SFX[jj] = F8 ? fp8x4_bf16x4(load_stream4(_V8 + _v1 + jj * 256))                 \
+                           : load_stream8(_Vb + _v1 + jj * 256);                              \
     } else {                                                                                  \
       _Pragma("unroll") for (int kk = 0; kk < KK; ++kk) k1##SFX[kk] = make_uint4(0, 0, 0, 0); \
       _Pragma("unroll") for (int jj = 0; jj < NJ; ++jj) v1##SFX[jj] = make_uint2(0, 0);       \
@@ -145,7 +155,9 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
     }                                                                                         \
   }
 
-template <int D>
+// F8: the cache holds FP8 e4m3 codes; scale_log2 carries k_scale and the
+// partials are scaled by v_scale.
+template <int D, bool F8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void attn_decode_kernel(AttnArgs a, float scale_log2) {
   constexpr int KK = D / 32;  // MFMA k-steps over the head dim
   constexpr int NJ = D / 16;  // 16-dim output blocks
@@ -186,9 +198,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
     const int head = kvh * g + r;
     const size_t pidx = (size_t)a.meta.part_off[t] + it.split;
     float* po = a.part_o + (pidx * nq + head) * D;
+    const float vsc = F8 ? a.v_scale : 1.0f;
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
-      *reinterpret_cast<float4*>(po + j * 16 + qd * 4) = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+      *reinterpret_cast<float4*>(po + j * 16 + qd * 4) =
+          make_float4(acc[j][0] * vsc, acc[j][1] * vsc, acc[j][2] * vsc, acc[j][3] * vsc);
     if (qd == 0) {
       a.part_ml[(pidx * nq + head) * 2 + 0] = m;
       a.part_ml[(pidx * nq + head) * 2 + 1] = l;
@@ -251,7 +265,11 @@ __device__ __forceinline__ uint4 keep_first8(uint4 v, int n) {
   return make_uint4(lo.x, lo.y, hi.x, hi.y);
 }
 
-template <int D>
+// F8: the cache holds FP8 e4m3 codes.  Pages then come through registers
+// (each wave loads its page's codes, widens them exactly to bf16 and writes the
+// same LDS images the direct-to-LDS loads produce); scale_log2 carries
+// k_scale and the partials are scaled by v_scale.
+template <int D, bool F8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_chunk_kernel(AttnArgs a, float scale_log2) {
   constexpr int NS = D / 32;      // 1 KB K or V loads per page = PV dim blocks
   constexpr int NH = D / 64;      // 128-byte dim halves of a K row
@@ -342,6 +360,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     }
   };
 
+  // FP8 pages: a page block is D * 16 bytes, loaded as D / 64 units of 1 KB
+  // (16 bytes per lane).  Unit L of K holds slice L / 32, slot (L / 2) % 16,
+  // dims 16 (L % 2) .. +15 of that slice; unit L of V is dim row L.
+  constexpr int NL8 = D / 64;
+  uint4 kr8[NL8], vr8[NL8];
+  auto load_tile8 = [&](int tile) {
+    if (4 * tile + wave < npg) {
+      const int page = __builtin_amdgcn_readlane(((tile >> 6) & 1) ? pw1 : pw0, tile & 63);
+      const size_t base = ((size_t)page * nkv + kvh) * PAGE + lane * 16;
+#pragma unroll
+      for (int u = 0; u < NL8; ++u) {
+        kr8[u] = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.k_cache) + base + u * 1024);
+        vr8[u] = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.v_cache) + base + u * 1024);
+      }
+    }
+  };
+  auto store_tile8 = [&](int tile, int st) {
+    if (4 * tile + wave < npg) {
+      uint16_t* kimg = &lds[st][0] + wave * PAGE;      // [dim half][slot][64]
+      uint16_t* vimg = &lds[st][TILE] + wave * PAGE;   // [dim][16 keys]
+#pragma unroll
+      for (int u = 0; u < NL8; ++u) {
+        const int L = u * 64 + lane;
+        const int sl = (L >> 1) & 15, c0 = ((L >> 5) & 1) * 4 + 2 * (L & 1);
+        uint16_t* krow = kimg + ((L >> 6) * 16 + sl) * 64;
+        *reinterpret_cast<uint4*>(krow + ((c0 ^ kswz(sl)) * 8)) = fp8x8_bf16x8(make_uint2(kr8[u].x, kr8[u].y));
+        *reinterpret_cast<uint4*>(krow + (((c0 + 1) ^ kswz(sl)) * 8)) = fp8x8_bf16x8(make_uint2(kr8[u].z, kr8[u].w));
+        uint16_t* vrow = vimg + L * 16;
+        const int sw = (L >> 3) & 1;
+        *reinterpret_cast<uint4*>(vrow + sw * 8) = fp8x8_bf16x8(make_uint2(vr8[u].x, vr8[u].y));
+        *reinterpret_cast<uint4*>(vrow + (sw ^ 1) * 8) = fp8x8_bf16x8(make_uint2(vr8[u].z, vr8[u].w));
+      }
+    }
+  };
+
   f32x16 acc[NS];
 #pragma unroll
   for (int db = 0; db < NS; ++db)
@@ -350,7 +403,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   float m = -INFINITY, l = 0.f;
   const int first_pos = a.meta.tok_pos[it.tok0];
 
-  issue_tile(0, 0);
+  if (F8) {
+    load_tile8(0);
+    store_tile8(0, 0);
+  } else {
+    issue_tile(0, 0);
+  }
   for (int ti = 0; ti < ntiles; ++ti) {
     const int kt = it.key0 + ti * 64;
     const int cur = ti & 1;
@@ -360,7 +418,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
       const int nw = fetch_window((ti >> 6) + 1);
       if ((ti >> 6) & 1) pw0 = nw; else pw1 = nw;
     }
-    if (ti + 1 < ntiles) issue_tile(ti + 1, cur ^ 1);
+    if (ti + 1 < ntiles) {
+      if (F8) load_tile8(ti + 1);
+      else issue_tile(ti + 1, cur ^ 1);
+    }
     if (kt + 64 > it.key1) {
       // last tile, partly past the item's end: zero V of keys >= key1
       uint16_t* vimg = &lds[cur][TILE];
@@ -457,6 +518,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 #pragma unroll
       for (int db = 0; db < NS; ++db) acc[db] = mfma32x32x16(vf[q * NS + db], pb, acc[db]);
     }
+    // FP8: the next tile's codes, loaded before this tile's compute, go into
+    // the other LDS images (every wave finished reading them before this
+    // iteration's barrier)
+    if (F8 && ti + 1 < ntiles) store_tile8(ti + 1, cur ^ 1);
   }
 
   l += __shfl_xor(l, 32, 64);
@@ -464,13 +529,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     const int head = kvh * g + hq;
     const size_t pidx = (size_t)a.meta.part_off[t] + it.split;
     float* po = a.part_o + (pidx * nq + head) * D + 4 * hh;
+    const float vsc = F8 ? a.v_scale : 1.0f;
     // acc[db][v] is dim 32 db + 8 (v >> 2) + 4 hh + (v & 3)
 #pragma unroll
     for (int db = 0; db < NS; ++db)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         *reinterpret_cast<float4*>(po + 32 * db + 8 * j) =
-            make_float4(acc[db][4 * j], acc[db][4 * j + 1], acc[db][4 * j + 2], acc[db][4 * j + 3]);
+            make_float4(acc[db][4 * j] * vsc, acc[db][4 * j + 1] * vsc, acc[db][4 * j + 2] * vsc,
+                        acc[db][4 * j + 3] * vsc);
     if (hh == 0) {
       a.part_ml[(pidx * nq + head) * 2 + 0] = m;
       a.part_ml[(pidx * nq + head) * 2 + 1] = l;
@@ -536,17 +603,18 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   *reinterpret_cast<uint2*>(a.out + (size_t)t * nq * D + (size_t)h * D + l4 * 4) = pk;
 }
 
-template <int D>
+template <int D, bool F8>
 static hb_status launch_attention_d(const AttnArgs& a, stream_t s, void* const* ev) {
-  const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
+  // FP8: keys are code * k_scale, so k_scale joins the score scale
+  const float scale_log2 = 1.4426950408889634f / sqrtf((float)D) * (F8 ? a.k_scale : 1.0f);
   hipStream_t st = (hipStream_t)s;
   if (ev) hipEventRecord((hipEvent_t)ev[0], st);
   if (a.n_chunk_items > 0)
-    hipLaunchKernelGGL(attn_chunk_kernel<D>, dim3((unsigned)a.n_chunk_items * a.n_kv_heads), dim3(256), 0, st, a,
+    hipLaunchKernelGGL((attn_chunk_kernel<D, F8>), dim3((unsigned)a.n_chunk_items * a.n_kv_heads), dim3(256), 0, st, a,
                        scale_log2);
   if (ev) hipEventRecord((hipEvent_t)ev[1], st);
   if (a.n_decode_items > 0)
-    hipLaunchKernelGGL(attn_decode_kernel<D>, dim3((a.n_decode_items + 3) / 4, a.n_kv_heads), dim3(256), 0, st, a,
+    hipLaunchKernelGGL((attn_decode_kernel<D, F8>), dim3((a.n_decode_items + 3) / 4, a.n_kv_heads), dim3(256), 0, st, a,
                        scale_log2);
   if (ev) hipEventRecord((hipEvent_t)ev[2], st);
   const int64_t pairs = (int64_t)a.n_tokens * a.n_q_heads, per_block = 256 / (D / 4);
@@ -559,7 +627,9 @@ static hb_status launch_attention_d(const AttnArgs& a, stream_t s, void* const* 
 
 hb_status launch_attention(const AttnArgs& a, stream_t s, void* const* ev) {
   if (a.n_tokens <= 0) return HB_OK;
-  return a.head_dim == 128 ? launch_attention_d<128>(a, s, ev) : launch_attention_d<64>(a, s, ev);
+  if (a.kv_fp8)
+    return a.head_dim == 128 ? launch_attention_d<128, true>(a, s, ev) : launch_attention_d<64, true>(a, s, ev);
+  return a.head_dim == 128 ? launch_attention_d<128, false>(a, s, ev) : launch_attention_d<64, false>(a, s, ev);
 }
 
 }  // namespace hb

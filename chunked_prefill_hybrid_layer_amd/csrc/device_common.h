@@ -28,6 +28,35 @@ __device__ __forceinline__ uint2 load_stream8(const void* p) {
   const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
   return make_uint2(v.x, v.y);
 }
+__device__ __forceinline__ uint32_t load_stream4(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
+
+// FP8 e4m3 (OCP e4m3fn) KV storage.  The conversion instruction rounds to
+// nearest even but turns magnitudes past 448's rounding range into NaN, so
+// values are clamped to +-448 first (saturating codes).
+__device__ __forceinline__ float clamp448(float x) { return fminf(fmaxf(x, -448.0f), 448.0f); }
+// four floats -> four codes, byte i holding value i
+__device__ __forceinline__ uint32_t pack4fp8(float a, float b, float c, float d) {
+  const uint32_t lo = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(c), clamp448(d), lo, true);
+}
+__device__ __forceinline__ uint8_t fp8_code(float a) {
+  return (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), 0.0f, 0, false) & 0xffu);
+}
+// two codes (the low or high half of w) -> two bf16 in one word, exactly
+// (every e4m3 value is a bf16 value)
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+__device__ __forceinline__ uint2 fp8x4_bf16x4(uint32_t w) {
+  return make_uint2(fp8x2_bf16x2<false>(w), fp8x2_bf16x2<true>(w));
+}
+__device__ __forceinline__ uint4 fp8x8_bf16x8(uint2 w) {
+  return make_uint4(fp8x2_bf16x2<false>(w.x), fp8x2_bf16x2<true>(w.x), fp8x2_bf16x2<false>(w.y),
+                    fp8x2_bf16x2<true>(w.y));
+}
 
 // float -> bf16, round to nearest even, NaN kept (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }

@@ -68,21 +68,22 @@ hb_status launch_rmsnorm(const float* x, const uint16_t* gain, uint16_t* out, in
 // hb_pack_metadata).  K is stored in 32-dim slices of the page ([d/32][16][32]),
 // so each slice of the run's rows is a contiguous copy.  V is stored transposed in the page ([d][16 slots]), so
 // the run's V rows are staged in LDS and written back row by row of d: a
-// full page is one contiguous 4 KB block (two lanes per 32-byte d row), a
-// partial page writes only its own slots.
-template <int D>
+// full page is one contiguous block (two lanes per d row), a partial page
+// writes only its own slots.  F8: the cache holds FP8 e4m3 codes of x / scale
+// (kinv, vinv are 1 / scale), one byte per element, same layout.
+template <int D, bool F8>
 __global__ __launch_bounds__(256) void kv_append_kernel(const uint16_t* __restrict__ k,
                                                         const uint16_t* __restrict__ v, int64_t row_stride,
                                                         const hb_append_run* __restrict__ runs, int n_runs,
-                                                        int nkv, uint16_t* __restrict__ kc,
-                                                        uint16_t* __restrict__ vc) {
+                                                        int nkv, void* __restrict__ kcv, void* __restrict__ vcv,
+                                                        float kinv, float vinv) {
   constexpr int CPT = D / 8;  // 16-byte chunks per token row
   __shared__ __align__(16) uint16_t vs[4][16 * D];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t item = (int64_t)blockIdx.x * 4 + wave;
   const bool active = item < (int64_t)n_runs * nkv;
   int n = 0, s0 = 0, tok0 = 0, h = 0;
-  size_t pb = 0;
+  size_t pb = 0;   // elements (= bytes in F8) from the cache start to the (page, kv head) block
   if (active) {
     const hb_append_run run = runs[item / nkv];
     h = (int)(item % nkv);
@@ -95,8 +96,21 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const uint16_t* __restri
     const int i = idx / CPT, c = idx % CPT;
     const size_t src = (size_t)(tok0 + i) * row_stride + (size_t)h * D + c * 8;
     // K page block [D/32][16][32]: dims 8c..8c+7 of slot s0+i
-    *reinterpret_cast<uint4*>(kc + pb + (size_t)(c >> 2) * 512 + (size_t)(s0 + i) * 32 + (c & 3) * 8) =
-        *reinterpret_cast<const uint4*>(k + src);
+    const size_t kd = pb + (size_t)(c >> 2) * 512 + (size_t)(s0 + i) * 32 + (c & 3) * 8;
+    const uint4 kr = *reinterpret_cast<const uint4*>(k + src);
+    if (F8) {
+      const uint32_t w[4] = {kr.x, kr.y, kr.z, kr.w};
+      float f[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f[2 * j] = bf2f((uint16_t)(w[j] & 0xffff)) * kinv;
+        f[2 * j + 1] = bf2f((uint16_t)(w[j] >> 16)) * kinv;
+      }
+      *reinterpret_cast<uint2*>(static_cast<uint8_t*>(kcv) + kd) =
+          make_uint2(pack4fp8(f[0], f[1], f[2], f[3]), pack4fp8(f[4], f[5], f[6], f[7]));
+    } else {
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(kcv) + kd) = kr;
+    }
     *reinterpret_cast<uint4*>(&vs[wave][i * D + c * 8]) = *reinterpret_cast<const uint4*>(v + src);
   }
   __syncthreads();
@@ -104,33 +118,48 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const uint16_t* __restri
     const int dd = idx >> 1, hf = idx & 1;          // d row, first or second 8 slots
     const int lo = max(s0, 8 * hf), hi = min(s0 + n, 8 * hf + 8);
     if (lo >= hi) continue;
-    uint16_t* dst = vc + pb + (size_t)dd * 16 + 8 * hf;
-    if (lo == 8 * hf && hi == 8 * hf + 8) {
-      uint32_t w[4];
+    const size_t vd = pb + (size_t)dd * 16 + 8 * hf;
+    if (F8) {
+      uint8_t* dst = static_cast<uint8_t*>(vcv) + vd;
+      if (lo == 8 * hf && hi == 8 * hf + 8) {
+        float f[8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        w[j] = (uint32_t)vs[wave][(8 * hf + 2 * j - s0) * D + dd] |
-               ((uint32_t)vs[wave][(8 * hf + 2 * j + 1 - s0) * D + dd] << 16);
-      *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+        for (int j = 0; j < 8; ++j) f[j] = bf2f(vs[wave][(8 * hf + j - s0) * D + dd]) * vinv;
+        *reinterpret_cast<uint2*>(dst) = make_uint2(pack4fp8(f[0], f[1], f[2], f[3]), pack4fp8(f[4], f[5], f[6], f[7]));
+      } else {
+        for (int sl = lo; sl < hi; ++sl) dst[sl - 8 * hf] = fp8_code(bf2f(vs[wave][(sl - s0) * D + dd]) * vinv);
+      }
     } else {
-      for (int sl = lo; sl < hi; ++sl) dst[sl - 8 * hf] = vs[wave][(sl - s0) * D + dd];
+      uint16_t* dst = static_cast<uint16_t*>(vcv) + vd;
+      if (lo == 8 * hf && hi == 8 * hf + 8) {
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          w[j] = (uint32_t)vs[wave][(8 * hf + 2 * j - s0) * D + dd] |
+                 ((uint32_t)vs[wave][(8 * hf + 2 * j + 1 - s0) * D + dd] << 16);
+        *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+      } else {
+        for (int sl = lo; sl < hi; ++sl) dst[sl - 8 * hf] = vs[wave][(sl - s0) * D + dd];
+      }
     }
   }
 }
 
 hb_status launch_kv_append(const hb_dims& d, const DevMeta& m, int n_tokens, const uint16_t* k,
-                           const uint16_t* v, int64_t row_stride, void* kcv, void* vcv, stream_t s) {
-  uint16_t* kc = static_cast<uint16_t*>(kcv);
-  uint16_t* vc = static_cast<uint16_t*>(vcv);
+                           const uint16_t* v, int64_t row_stride, void* kc, void* vc, stream_t s) {
   if (n_tokens <= 0 || m.n_append_runs <= 0) return HB_OK;
   const int64_t items = (int64_t)m.n_append_runs * d.n_kv_heads;
   const unsigned blocks = (unsigned)((items + 3) / 4);
-  if (d.head_dim == 128)
-    hipLaunchKernelGGL(kv_append_kernel<128>, dim3(blocks), dim3(256), 0, (hipStream_t)s, k, v, row_stride,
-                       m.append_runs, m.n_append_runs, d.n_kv_heads, kc, vc);
-  else
-    hipLaunchKernelGGL(kv_append_kernel<64>, dim3(blocks), dim3(256), 0, (hipStream_t)s, k, v, row_stride,
-                       m.append_runs, m.n_append_runs, d.n_kv_heads, kc, vc);
+  const float kinv = d.kv_fp8 ? 1.0f / d.k_scale : 1.0f, vinv = d.kv_fp8 ? 1.0f / d.v_scale : 1.0f;
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(blocks), dim3(256), 0, (hipStream_t)s, k, v, row_stride, m.append_runs,
+                       m.n_append_runs, d.n_kv_heads, kc, vc, kinv, vinv);
+  };
+  if (d.head_dim == 128) {
+    if (d.kv_fp8) go(kv_append_kernel<128, true>); else go(kv_append_kernel<128, false>);
+  } else {
+    if (d.kv_fp8) go(kv_append_kernel<64, true>); else go(kv_append_kernel<64, false>);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(HB_E_HIP, std::string("kv_append launch: ") + hipGetErrorString(e));
   return HB_OK;

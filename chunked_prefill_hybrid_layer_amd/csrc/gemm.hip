@@ -112,8 +112,8 @@ __device__ __forceinline__ const uint16_t* weight_row(const GemmArgs& g, int n, 
 // i0 .. i0 + 3 (x0) and i0 + d/2 .. i0 + d/2 + 3 (x1) of one head, where
 // i0 = (n mod d) / 2.  q and k are rotated by the token's position (rotate-
 // half: dim i pairs with dim i + d/2), q goes to the q buffer, k and v to the
-// paged cache at the token's slot.  q and K stores are 8 bytes; V (dim-major
-// in a page) takes one 2-byte store per dim.
+// paged cache at the token's slot (bf16, or FP8 codes of x / scale).  q and K
+// stores are 8 bytes (4 in FP8); V (dim-major in a page) takes one store per dim.
 __device__ __forceinline__ void qkv_store4(const GemmArgs& g, int m, int n, const float (&x0)[4],
                                            const float (&x1)[4]) {
   const int d = g.head_dim, half = d >> 1;
@@ -137,6 +137,17 @@ __device__ __forceinline__ void qkv_store4(const GemmArgs& g, int m, int n, cons
       uint16_t* qo = g.out_b + (size_t)m * qdim + c;
       *reinterpret_cast<uint2*>(qo) = lo;
       *reinterpret_cast<uint2*>(qo + half) = hi;
+    } else if (g.kv_fp8) {
+      // FP8 K page block: [d/32][16 slots][32] codes of k / k_scale
+      const int kvh = (c - qdim) / d;
+      const int sl = g.slot[m];
+      uint8_t* kb = static_cast<uint8_t*>(g.k_cache) + ((size_t)(sl >> 4) * g.n_kv_heads + kvh) * 16 * d +
+                    (sl & 15) * 32;
+      const float s = g.k_inv_scale;
+      *reinterpret_cast<uint32_t*>(kb + (i0 >> 5) * 512 + (i0 & 31)) =
+          pack4fp8(y0[0] * s, y0[1] * s, y0[2] * s, y0[3] * s);
+      *reinterpret_cast<uint32_t*>(kb + ((i0 + half) >> 5) * 512 + ((i0 + half) & 31)) =
+          pack4fp8(y1[0] * s, y1[1] * s, y1[2] * s, y1[3] * s);
     } else {
       const int kvh = (c - qdim) / d;
       const int sl = g.slot[m];
@@ -149,12 +160,21 @@ __device__ __forceinline__ void qkv_store4(const GemmArgs& g, int m, int n, cons
   } else {
     const int kvh = (c - qdim - kdim) / d;
     const int sl = g.slot[m];
-    uint16_t* vp = static_cast<uint16_t*>(g.v_cache) + (((size_t)(sl >> 4) * g.n_kv_heads + kvh) * d + i0) * 16 +
-                   (sl & 15);
+    const size_t vo = (((size_t)(sl >> 4) * g.n_kv_heads + kvh) * d + i0) * 16 + (sl & 15);
+    if (g.kv_fp8) {
+      uint8_t* vp = static_cast<uint8_t*>(g.v_cache) + vo;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      vp[e * 16] = f2bf(x0[e]);
-      vp[(half + e) * 16] = f2bf(x1[e]);
+      for (int e = 0; e < 4; ++e) {
+        vp[e * 16] = fp8_code(x0[e] * g.v_inv_scale);
+        vp[(half + e) * 16] = fp8_code(x1[e] * g.v_inv_scale);
+      }
+    } else {
+      uint16_t* vp = static_cast<uint16_t*>(g.v_cache) + vo;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vp[e * 16] = f2bf(x0[e]);
+        vp[(half + e) * 16] = f2bf(x1[e]);
+      }
     }
   }
 }

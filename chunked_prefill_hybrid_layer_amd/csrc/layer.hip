@@ -46,7 +46,6 @@ extern "C" hb_status hb_kv_append(const hb_dims* dims, const void* meta_host, co
                                   const uint16_t* k, const uint16_t* v, int64_t row_stride, void* k_cache,
                                   void* v_cache, void* stream) {
   HB_TRY(check_dims(dims));
-  if (dims->kv_fp8) return fail(HB_E_SHAPE, "kv_append: FP8 KV cache not built yet");
   HB_TRY(check_meta(dims, meta_host));
   if (!meta_dev || !k || !v || !k_cache || !v_cache) return fail(HB_E_NULL, "kv_append: NULL pointer");
   if (row_stride < (int64_t)dims->n_kv_heads * dims->head_dim || row_stride % 8)
@@ -64,7 +63,6 @@ extern "C" hb_status hb_layer_forward(const hb_dims* dims, const hb_weights* w, 
                                       void* workspace, size_t workspace_bytes, void* stream,
                                       void* const* stage_events) {
   HB_TRY(check_dims(dims));
-  if (dims->kv_fp8) return fail(HB_E_SHAPE, "layer_forward: FP8 KV cache not built yet");
   HB_TRY(check_meta(dims, meta_host));
   if (!w || !meta_dev || !rope_cs || !x || !y || !k_cache || !v_cache || !workspace)
     return fail(HB_E_NULL, "layer_forward: NULL pointer");
@@ -124,6 +122,9 @@ extern "C" hb_status hb_layer_forward(const hb_dims* dims, const hb_weights* w, 
   g.slot = m.slot;
   g.k_cache = k_cache;
   g.v_cache = v_cache;
+  g.kv_fp8 = dims->kv_fp8;
+  g.k_inv_scale = dims->kv_fp8 ? 1.0f / dims->k_scale : 1.0f;
+  g.v_inv_scale = dims->kv_fp8 ? 1.0f / dims->v_scale : 1.0f;
   g.n_q_heads = nq;
   g.n_kv_heads = nkv;
   g.head_dim = d;
@@ -136,6 +137,9 @@ extern "C" hb_status hb_layer_forward(const hb_dims* dims, const hb_weights* w, 
   at.q = qb;
   at.k_cache = k_cache;
   at.v_cache = v_cache;
+  at.kv_fp8 = dims->kv_fp8;
+  at.k_scale = dims->kv_fp8 ? dims->k_scale : 1.0f;
+  at.v_scale = dims->kv_fp8 ? dims->v_scale : 1.0f;
   at.meta = m;
   at.max_pages = h->max_pages;
   at.n_q_heads = nq;

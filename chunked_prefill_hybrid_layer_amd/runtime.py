@@ -15,6 +15,7 @@ import torch
 from . import hb
 
 BF16_NAN = 0x7FC0
+E4M3_NAN = 0x7F
 WEIGHT_NAMES = ("w_q", "w_k", "w_v", "w_o", "w_g", "w_u", "w_d", "g_attn", "g_ffn")
 
 
@@ -52,7 +53,8 @@ class Prepared:
 
 class DeviceLayer:
     """Weights, paged KV cache (NaN-filled: unwritten slots are poison), rotary
-    table and workspace of one decoder layer on one GPU."""
+    table and workspace of one decoder layer on one GPU.  With dims.kv_fp8 the
+    cache holds one-byte FP8 e4m3 codes (NaN code 0x7F as poison), else bf16."""
 
     def __init__(self, dims, weights: dict, num_pages: int, rope_max_pos: int, device: str = "cuda"):
         self.dims = dims
@@ -62,10 +64,13 @@ class DeviceLayer:
         self.hw = hb.Weights(*[self.w[n].data_ptr() for n in WEIGHT_NAMES])
         self.num_pages = int(num_pages)
         # K page blocks are [head_dim/32][page_size][32]; V page blocks [head_dim][page_size]
+        self.kv_fp8 = bool(getattr(dims, "kv_fp8", 0))
+        fill, dt = (E4M3_NAN, torch.uint8) if self.kv_fp8 else (BF16_NAN, torch.int16)
         self.k_cache = torch.full((self.num_pages, dims.n_kv_heads, dims.head_dim // 32, dims.page_size, 32),
-                                  BF16_NAN, dtype=torch.int16, device=device)
-        self.v_cache = torch.full((self.num_pages, dims.n_kv_heads, dims.head_dim, dims.page_size), BF16_NAN,
-                                  dtype=torch.int16, device=device)
+                                  fill, dtype=dt, device=device)
+        self.v_cache = torch.full((self.num_pages, dims.n_kv_heads, dims.head_dim, dims.page_size), fill,
+                                  dtype=dt, device=device)
+        self._np_cache = np.uint8 if self.kv_fp8 else np.uint16
         self.rope_max_pos = int(rope_max_pos)
         self.rope = torch.from_numpy(hb.rope_table(self.hd, self.rope_max_pos)).to(device)
         self.ws: Optional[torch.Tensor] = None
@@ -113,18 +118,20 @@ class DeviceLayer:
 
     # -- views for checking ---------------------------------------------------
     def cache_logical(self):
-        """(K, V) as uint16 numpy arrays in logical order [page][kv][slot][d]."""
+        """(K, V) in logical order [page][kv][slot][d]: bf16 bits as uint16, or
+        FP8 e4m3 codes as uint8."""
         P, nkv, c, p, _ = self.k_cache.shape
-        k = self.k_cache.cpu().numpy().view(np.uint16).transpose(0, 1, 3, 2, 4).reshape(P, nkv, p, c * 32)
-        v = self.v_cache.cpu().numpy().view(np.uint16).transpose(0, 1, 3, 2)
+        k = self.k_cache.cpu().numpy().view(self._np_cache).transpose(0, 1, 3, 2, 4).reshape(P, nkv, p, c * 32)
+        v = self.v_cache.cpu().numpy().view(self._np_cache).transpose(0, 1, 3, 2)
         return np.ascontiguousarray(k), np.ascontiguousarray(v)
 
     def gather_kv(self, pages, slots):
-        """K and V rows at (page, slot) pairs as uint16 numpy arrays [n][kv][d]."""
+        """K and V rows at (page, slot) pairs [n][kv][d]: bf16 bits as uint16, or
+        FP8 e4m3 codes as uint8."""
         pg = torch.as_tensor(np.asarray(pages), device=self.device)
         sl = torch.as_tensor(np.asarray(slots), device=self.device)
         k = self.k_cache[pg, :, :, sl, :]                       # [n][kv][d/32][32]
         v = self.v_cache.permute(0, 1, 3, 2)[pg, :, sl, :]      # [n][kv][d]
         n, nkv = k.shape[0], k.shape[1]
-        return (k.reshape(n, nkv, -1).cpu().numpy().view(np.uint16),
-                v.cpu().numpy().view(np.uint16))
+        return (k.reshape(n, nkv, -1).cpu().numpy().view(self._np_cache),
+                v.cpu().numpy().view(self._np_cache))

@@ -24,6 +24,7 @@ Value recipe (the pages give none; these are readings):
 """
 from __future__ import annotations
 
+import dataclasses
 from dataclasses import dataclass, field
 import os
 from typing import Dict, List, Optional
@@ -306,6 +307,21 @@ def yi_tau2048(seed: int = 0) -> Workload:
     _, _, rl, _, _, _ = _streams(seed)
     ctx = _lognormal_ctx(rl, 512, 2048, 16384)
     return build_workload("yi_tau2048", YI, [768, 768], [0, 6144], ctx, seed, token_budget=2048)
+
+
+# FP8 KV cache scales of the synthetic workloads (powers of two, K and V
+# different): N(0, 1)-sized K/V over the scale stay far inside e4m3's +-448
+# and far above its subnormals (2^-6)
+FP8_K_SCALE = 2.0 ** -4
+FP8_V_SCALE = 2.0 ** -3
+
+
+def with_kv_fp8(wl: Workload, k_scale: float = FP8_K_SCALE, v_scale: float = FP8_V_SCALE) -> Workload:
+    """The same workload with an FP8 e4m3 KV cache (prefixes are quantised
+    when they are written)."""
+    wl.dims = dataclasses.replace(wl.dims, kv_fp8=1, k_scale=float(k_scale), v_scale=float(v_scale))
+    wl.name += "_kvfp8"
+    return wl
 
 
 def small(seed: int = 0, n_q: int = 8, n_kv: int = 2, head_dim: int = 128,

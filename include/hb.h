@@ -85,8 +85,12 @@ typedef struct {
   /* KV cache element type.  0: bf16.  1: FP8 e4m3 (OCP e4m3fn: exponent bias
    * 7, largest finite 448, no infinities, NaN 0x7F/0xFF), one byte per
    * element: the cache holds e4m3(x / scale) rounded to nearest even and
-   * saturated to +-448, and attention reads code value * scale.  The scales
-   * are per layer and come from the caller (ignored for bf16). */
+   * saturated to +-448, and attention reads code value * scale.  x / scale is
+   * evaluated in single precision as x times the float reciprocal of scale
+   * (the precision decides codes at midpoints).  K/V inputs must be finite
+   * (NaN inputs are outside the contract).  The scales are per layer, come from
+   * the caller, must be finite and > 0 (HB_E_SHAPE otherwise) and are ignored
+   * for bf16. */
   int32_t kv_fp8;
   float k_scale;
   float v_scale;
@@ -234,7 +238,8 @@ size_t hb_workspace_bytes(const hb_dims *dims, const void *meta_host);
 /* KV append ("Chunked Prefill", mechanism: each chunk writes its KV into the
  * paged blocks): for every packed token t, k[t] and v[t] ([n_kv][head_dim]
  * bf16, consecutive tokens `row_stride` elements apart) go to slot[t] of the
- * K and V caches.  Only those slots change.  meta_host / meta_dev: the blob
+ * K and V caches (as FP8 codes of k / k_scale, v / v_scale with
+ * dims->kv_fp8).  Only those slots change.  meta_host / meta_dev: the blob
  * from hb_pack_metadata and its byte-identical device copy. */
 hb_status hb_kv_append(const hb_dims *dims, const void *meta_host, const void *meta_dev,
                        const uint16_t *k, const uint16_t *v, int64_t row_stride,

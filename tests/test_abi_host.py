@@ -215,6 +215,12 @@ def test_pack_rejects_invalid_batches():
     assert _err(lambda: _pack(bad, [4], [0], [], np.array([[0]]), 1)) == "HB_E_SHAPE"
     bad = W.Dims(16384 + 128, 4, 4, 64, 512)   # hidden above the row kernels' register budget
     assert _err(lambda: _pack(bad, [4], [0], [], np.array([[0]]), 1)) == "HB_E_SHAPE"
+    # FP8 cache settings: kv_fp8 is 0 or 1, its scales finite and positive
+    _pack(W.Dims(256, 4, 4, 64, 512, kv_fp8=1, k_scale=0.0625, v_scale=3.0), [4], [0], [], np.array([[0]]), 1)
+    for kw in (dict(kv_fp8=2), dict(kv_fp8=1, k_scale=0.0), dict(kv_fp8=1, v_scale=-1.0),
+               dict(kv_fp8=1, k_scale=float("nan")), dict(kv_fp8=1, v_scale=float("inf"))):
+        bad = W.Dims(256, 4, 4, 64, 512, **kw)
+        assert _err(lambda: _pack(bad, [4], [0], [], np.array([[0]]), 1)) == "HB_E_SHAPE", kw
     # a too-small buffer is reported, and nothing is written
     dims = hb.make_dims(d)
     with pytest.raises(hb.HbError) as ei:

@@ -7,7 +7,7 @@ import pytest
 from oracle import hybrid_layer as O
 from chunked_prefill_hybrid_layer_amd import workloads as W
 from tests.helpers import (TOL_MAX_ABS, assert_close, compare_cache, conditioning_floor, errors, log,
-                           new_values_close, oracle_cache, oracle_forward, sample_rows)
+                           new_codes_close, new_values_close, oracle_cache, oracle_forward, sample_rows)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -239,10 +239,16 @@ def _full_size(wl, n_random, calibrate=False):
     # every new K/V row: the GPU cache at the new slots against the oracle's
     slots = _new_slots(b)
     gk, gv = layer.gather_kv([p for p, _ in slots], [s for _, s in slots])   # [T][kv][d] each
-    ek = np.stack([cache.pages[p][0, :, sl, :] for p, sl in slots])
-    ev = np.stack([cache.pages[p][1, :, sl, :] for p, sl in slots])
+    if wl.dims.kv_fp8:
+        ek = np.stack([cache.codes[p][0, :, sl, :] for p, sl in slots])
+        ev = np.stack([cache.codes[p][1, :, sl, :] for p, sl in slots])
+        close = new_codes_close
+    else:
+        ek = np.stack([cache.pages[p][0, :, sl, :] for p, sl in slots])
+        ev = np.stack([cache.pages[p][1, :, sl, :] for p, sl in slots])
+        close = new_values_close
     for name, g, e in (("K", gk, ek), ("V", gv, ev)):
-        new_values_close(g, e, f"{wl.name} new {name}")
+        close(g, e, f"{wl.name} new {name}")
 
 
 def test_full_size_mistral_tau512():
@@ -271,3 +277,105 @@ def test_full_size_other_gemm_plans(case):
 
 def test_full_size_yi_tau2048():
     _full_size(W.yi_tau2048(0), 24, calibrate=True)
+
+
+# ---------------------------------------------------------------- FP8 e4m3 KV cache
+
+@pytest.mark.parametrize("head_dim,n_kv", [(128, 2), (64, 4)])
+def test_kv_append_fp8_codes_bit_exact(head_dim, n_kv):
+    """hb_kv_append into an FP8 cache: every byte equals the oracle's e4m3
+    code of value / scale (the scales are powers of two, so both sides divide
+    exactly), including planted ties (to the even code), values past +-448
+    (saturated) and values below the subnormal range."""
+    from chunked_prefill_hybrid_layer_amd.runtime import DeviceLayer, to_device_u16
+    from chunked_prefill_hybrid_layer_amd import hb
+    log(f"kv_append fp8 head_dim={head_dim} n_kv={n_kv}")
+    wl = W.with_kv_fp8(W.small(1, n_q=n_kv * 2, n_kv=n_kv, head_dim=head_dim, chunk_len=(37, 200, 1),
+                               chunk_prefix=(15, 0, 31), decode_ctx=(0, 15, 16, 47, 300)))
+    b, d = wl.batch, wl.dims
+    layer = DeviceLayer(d, wl.weights, b.num_pages, 2048)
+    layer.fill_prefixes(b.block_table, range(b.n_seq), wl.prefix_k, wl.prefix_v)
+    T = b.n_tokens
+    rng = np.random.default_rng(5)
+    stride = n_kv * head_dim + 64
+    kf = rng.standard_normal((T, stride))
+    vf = rng.standard_normal((T, stride))
+    # planted values, in units of the scale: ties between adjacent codes
+    # (1 + 1/16 -> 1, 1 + 3/16 -> 1.25, 2^-7 + 2^-10 between subnormals,
+    # 448 + 16 and 480 past the top), saturation and underflow
+    special = np.array([1.0625, 1.1875, -1.0625, 2.0 ** -7 + 2.0 ** -10, 2.0 ** -10, -2.0 ** -11,
+                        464.0, -464.0, 480.0, 1e4, -1e4, 0.0, -0.0, 240.0, 248.0, 0.75 * 2.0 ** -9])
+    for t in range(0, T, 7):
+        cols = rng.choice(n_kv * head_dim, size=len(special), replace=False)
+        kf[t, cols] = special * d.k_scale
+        vf[t, cols] = special[::-1] * d.v_scale
+    kb = W.f32_to_bf16_bits(kf.astype(np.float32))
+    vb = W.f32_to_bf16_bits(vf.astype(np.float32))
+    prep = layer.prepare(b.chunk_len, b.chunk_prefix, b.decode_ctx, b.block_table)
+    kd, vd = to_device_u16(kb, "cuda"), to_device_u16(vb, "cuda")
+    hb.kv_append(layer.hd, prep.blob, prep.meta_dev.data_ptr(), kd.data_ptr(), vd.data_ptr(), stride,
+                 layer.k_cache.data_ptr(), layer.v_cache.data_ptr(), 0)
+    torch.cuda.synchronize()
+    cache = oracle_cache(wl)
+    lay = O.token_layout(b.chunk_len, b.chunk_prefix, b.decode_ctx)
+    for t in range(T):
+        krow = O.bf16_bits_to_float(kb[t, :n_kv * head_dim]).reshape(n_kv, head_dim)
+        vrow = O.bf16_bits_to_float(vb[t, :n_kv * head_dim]).reshape(n_kv, head_dim)
+        cache.write(b.block_table, int(lay.seq[t]), int(lay.pos[t]), krow, vrow)
+    compare_cache(layer.cache_logical(), cache, b.num_pages, None, "kv_append fp8")
+
+
+FP8_SMALL = {k: SMALL[k] for k in ("g4_d128", "g1_d64", "g16_d128")}
+
+
+@pytest.mark.parametrize("name", list(FP8_SMALL))
+def test_layer_parity_small_kv_fp8(name):
+    """Whole layer over an FP8 cache: y within the floating-point bar of the
+    oracle's (which reads the same quantised K/V), the cache's untouched bytes
+    bit-exact and the new codes within one e4m3 step."""
+    log(f"layer parity small kv fp8 {name}")
+    wl = W.with_kv_fp8(W.small(2, **FP8_SMALL[name]))
+    b = wl.batch
+    layer = _layer_for(wl)
+    layer.fill_prefixes(b.block_table, range(b.n_seq), wl.prefix_k, wl.prefix_v)
+    y, _ = _run(layer, wl)
+    r, cache = oracle_forward(wl)
+    assert_close(y, r.y, f"small {name} kv fp8 y")
+    compare_cache(layer.cache_logical(), cache, b.num_pages, _new_slots(b), f"small {name} kv fp8")
+
+
+def test_layer_parity_kv_fp8_other_scales():
+    """Scales that are not powers of two (k 0.05, v 0.03): the k scale folds
+    into the score scale and the v scale into the output."""
+    log("layer parity kv fp8, scales 0.05 / 0.03")
+    wl = W.with_kv_fp8(W.small(9, n_q=8, n_kv=2, head_dim=128), k_scale=0.05, v_scale=0.03)
+    b = wl.batch
+    layer = _layer_for(wl)
+    layer.fill_prefixes(b.block_table, range(b.n_seq), wl.prefix_k, wl.prefix_v)
+    y, _ = _run(layer, wl)
+    r, cache = oracle_forward(wl)
+    assert_close(y, r.y, "kv fp8 scales 0.05/0.03 y")
+    compare_cache(layer.cache_logical(), cache, b.num_pages, _new_slots(b), "kv fp8 scales 0.05/0.03")
+
+
+@pytest.mark.parametrize("case", ["decodes_only", "page_edge_chunks", "multi_token_decodes"])
+def test_layer_edge_cases_kv_fp8(case):
+    log(f"edge case kv fp8 {case}")
+    kw = {
+        "decodes_only": dict(chunk_len=(), chunk_prefix=(), decode_ctx=(1, 16, 17, 255, 256, 257, 999)),
+        "page_edge_chunks": dict(chunk_len=(16, 17, 15, 129), chunk_prefix=(16, 15, 1, 1023), decode_ctx=()),
+        "multi_token_decodes": dict(chunk_len=(2, 4, 8, 4), chunk_prefix=(1000, 333, 17, 2045),
+                                    decode_ctx=(5, 1000, 2047)),
+    }[case]
+    wl = W.with_kv_fp8(W.small(7, n_q=8, n_kv=2, head_dim=128, **kw))
+    b = wl.batch
+    layer = _layer_for(wl)
+    layer.fill_prefixes(b.block_table, range(b.n_seq), wl.prefix_k, wl.prefix_v)
+    y, _ = _run(layer, wl)
+    r, cache = oracle_forward(wl)
+    assert_close(y, r.y, f"{case} kv fp8")
+    compare_cache(layer.cache_logical(), cache, b.num_pages, _new_slots(b), f"{case} kv fp8")
+
+
+def test_full_size_mistral_tau512_kv_fp8():
+    _full_size(W.with_kv_fp8(W.mistral_tau512(0)), 48)
