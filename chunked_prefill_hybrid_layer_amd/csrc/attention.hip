@@ -75,32 +75,59 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
     const bool _has1 = (KB) + 16 < it.key1;                                                   \
     const int _pg0 = __builtin_amdgcn_readlane(my_pg, _j);                                    \
     const int _pg1 = __builtin_amdgcn_readlane(my_pg, _has1 ? _j + 1 : _j);                   \
-    /* element offsets of this lane's fragments (bytes in FP8, where each K   \
-       and V^T fragment is half as many bytes and is widened to bf16 exactly) */ \
-    const size_t _k0 = ((size_t)_pg0 * nkv + kvh) * hs + r * 32 + qd * 8;                    \
-    const size_t _k1 = ((size_t)_pg1 * nkv + kvh) * hs + r * 32 + qd * 8;                    \
-    const size_t _v0 = ((size_t)_pg0 * nkv + kvh) * hs + r * 16 + qd * 4;                    \
-    const size_t _v1 = ((size_t)_pg1 * nkv + kvh) * hs + r * 16 + qd * 4;                    \
-    const uint16_t* _Kb = static_cast<const uint16_t*>(a.k_cache);                           \
-    const uint16_t* _Vb = static_cast<const uint16_t*>(a.v_cache);                           \
-    const uint8_t* _K8 = static_cast<const uint8_t*>(a.k_cache);                             \
-    const uint8_t* _V8 = static_cast<const uint8_t*>(a.v_cache);                             \
+    const uint16_t* _K0 = static_cast<const uint16_t*>(a.k_cache) + ((size_t)_pg0 * nkv + kvh) * hs + r * 32 + qd * 8; \
+    const uint16_t* _K1 = static_cast<const uint16_t*>(a.k_cache) + ((size_t)_pg1 * nkv + kvh) * hs + r * 32 + qd * 8; \
+    const uint16_t* _V0 = static_cast<const uint16_t*>(a.v_cache) + ((size_t)_pg0 * nkv + kvh) * hs + r * 16 + qd * 4; \
+    const uint16_t* _V1 = static_cast<const uint16_t*>(a.v_cache) + ((size_t)_pg1 * nkv + kvh) * hs + r * 16 + qd * 4; \
     _Pragma("unroll") for (int kk = 0; kk < KK; ++kk)                                         \
-        k0##SFX[kk] = F8 ? fp8x8_bf16x8(load_stream8(_K8 + _k0 + kk * 512))                   \
-                         : load_stream16(_Kb + _k0 + kk * 512);                               \
+        k0##SFX[kk] = load_stream16(_K0 + kk * 512);                                          \
     _Pragma("unroll") for (int jj = 0; jj < NJ; ++jj)                                         \
-        v0##SFX[jj] = F8 ? fp8x4_bf16x4(load_stream4(_V8 + _v0 + jj * 256))                   \
-                         : load_stream8(_Vb + _v0 + jj * 256);                                \
+        v0##SFX[jj] = load_stream8(_V0 + jj * 256);                                           \
     if (_has1) {                                                                              \
       _Pragma("unroll") for (int kk = 0; kk < KK; ++kk)                                       \
-          k1##SFX[kk] = F8 ? fp8x8_bf16x8(load_stream8(_K8 + _k1 + kk * 512))                 \
-                           : load_stream16(_Kb + _k1 + kk * 512);                             \
+          k1##SFX[kk] = load_stream16(_K1 + kk * 512);                                        \
       _Pragma("unroll") for (int jj = 0; jj < NJ; ++jj)                                       \
-          v1##SFX[jj] = F8 ? fp8x4_bf16x4(load_stream4(_V8 + _v1 + jj * 256))                 \
-                           : load_stream8(_Vb + _v1 + jj * 256);                              \
+          v1##SFX[jj] = load_stream8(_V1 + jj * 256);                                         \
     } else {                                                                                  \
       _Pragma("unroll") for (int kk = 0; kk < KK; ++kk) k1##SFX[kk] = make_uint4(0, 0, 0, 0); \
       _Pragma("unroll") for (int jj = 0; jj < NJ; ++jj) v1##SFX[jj] = make_uint2(0, 0);       \
+    }                                                                                         \
+  }
+
+// FP8 cache: the same fragments as codes (8 bytes of K, 4 of V^T per lane and
+// page: byte offsets equal the bf16 element offsets) into raw buffer I; a
+// missing second page reads as zero codes.
+#define DEC_LOAD8(KB, I)                                                                      \
+  {                                                                                           \
+    const int _j = ((KB) - it.key0) >> 4;                                                     \
+    const bool _has1 = (KB) + 16 < it.key1;                                                   \
+    const int _pg0 = __builtin_amdgcn_readlane(my_pg, _j);                                    \
+    const int _pg1 = __builtin_amdgcn_readlane(my_pg, _has1 ? _j + 1 : _j);                   \
+    const uint8_t* _K0 = static_cast<const uint8_t*>(a.k_cache) + ((size_t)_pg0 * nkv + kvh) * hs + r * 32 + qd * 8; \
+    const uint8_t* _K1 = static_cast<const uint8_t*>(a.k_cache) + ((size_t)_pg1 * nkv + kvh) * hs + r * 32 + qd * 8; \
+    const uint8_t* _V0 = static_cast<const uint8_t*>(a.v_cache) + ((size_t)_pg0 * nkv + kvh) * hs + r * 16 + qd * 4; \
+    const uint8_t* _V1 = static_cast<const uint8_t*>(a.v_cache) + ((size_t)_pg1 * nkv + kvh) * hs + r * 16 + qd * 4; \
+    _Pragma("unroll") for (int kk = 0; kk < KK; ++kk) k0r[I][kk] = load_stream8(_K0 + kk * 512); \
+    _Pragma("unroll") for (int jj = 0; jj < NJ; ++jj) v0r[I][jj] = load_stream4(_V0 + jj * 256); \
+    if (_has1) {                                                                              \
+      _Pragma("unroll") for (int kk = 0; kk < KK; ++kk) k1r[I][kk] = load_stream8(_K1 + kk * 512); \
+      _Pragma("unroll") for (int jj = 0; jj < NJ; ++jj) v1r[I][jj] = load_stream4(_V1 + jj * 256); \
+    } else {                                                                                  \
+      _Pragma("unroll") for (int kk = 0; kk < KK; ++kk) k1r[I][kk] = make_uint2(0, 0);        \
+      _Pragma("unroll") for (int jj = 0; jj < NJ; ++jj) v1r[I][jj] = 0u;                      \
+    }                                                                                         \
+  }
+
+// Raw buffer I widened (exactly) into the bf16 buffer set SFX.
+#define DEC_WIDEN(I, SFX)                                                                     \
+  {                                                                                           \
+    _Pragma("unroll") for (int kk = 0; kk < KK; ++kk) {                                       \
+      k0##SFX[kk] = fp8x8_bf16x8(k0r[I][kk]);                                                 \
+      k1##SFX[kk] = fp8x8_bf16x8(k1r[I][kk]);                                                 \
+    }                                                                                         \
+    _Pragma("unroll") for (int jj = 0; jj < NJ; ++jj) {                                       \
+      v0##SFX[jj] = fp8x4_bf16x4(v0r[I][jj]);                                                 \
+      v1##SFX[jj] = fp8x4_bf16x4(v1r[I][jj]);                                                 \
     }                                                                                         \
   }
 
@@ -188,9 +215,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
 
   uint4 k0A[KK], k1A[KK];
   uint2 v0A[NJ], v1A[NJ];
-  for (int kb = it.key0; kb < it.key1; kb += 32) {
-    DEC_LOAD(kb, A);
-    DEC_COMPUTE(kb, A);
+  if constexpr (F8) {
+    // two steps' codes in flight (the bytes of one bf16 step), each widened
+    // just before its MFMAs
+    uint2 k0r[2][KK], k1r[2][KK];
+    uint32_t v0r[2][NJ], v1r[2][NJ];
+    for (int kb = it.key0; kb < it.key1; kb += 64) {
+      const bool second = kb + 32 < it.key1;
+      DEC_LOAD8(kb, 0);
+      if (second) DEC_LOAD8(kb + 32, 1);
+      DEC_WIDEN(0, A);
+      DEC_COMPUTE(kb, A);
+      if (second) {
+        DEC_WIDEN(1, A);
+        DEC_COMPUTE(kb + 32, A);
+      }
+    }
+  } else {
+    for (int kb = it.key0; kb < it.key1; kb += 32) {
+      DEC_LOAD(kb, A);
+      DEC_COMPUTE(kb, A);
+    }
   }
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
@@ -211,6 +256,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
 }
 
 #undef DEC_LOAD
+#undef DEC_LOAD8
+#undef DEC_WIDEN
 #undef DEC_COMPUTE
 
 // ----------------------------------------------------------------------------
