@@ -35,6 +35,13 @@ __device__ __forceinline__ uint2 keep_first(uint2 v, int n) {
   return make_uint2(v.x, v.y & 0xffffu);
 }
 
+__device__ __forceinline__ uint4 keep_first8(uint4 v, int n) {
+  // keep the first n (0..8) bf16 values of an 8-value vector, zero the rest
+  const uint2 lo = keep_first(make_uint2(v.x, v.y), n);
+  const uint2 hi = keep_first(make_uint2(v.z, v.w), n - 4);
+  return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
 // Decode items: probabilities enter the PV product as two bf16 fragments,
 // p = hi + lo with hi = bf16(p) and lo = bf16(p - hi), about 16 significant
 // bits (a single bf16 P puts a relative error up to 2^-9 on every weight).  The
@@ -63,92 +70,82 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // are broadcast with readlane, so no step waits on a block-table load.  The
 // K/V of a step sit in one register buffer (138 VGPRs): three waves per SIMD
 // keep more bytes in flight than two double-buffered ones did (measured).
+//
+// Key order.  Lane l = (qd = l / 16, r = l % 16).  The two QK MFMAs of a step
+// take their A rows from permuted keys: row i of MFMA h is key
+// 8 (i / 4) + 4 h + i % 4 of the step, so the 4 scores lane l receives from
+// MFMA h are keys 8 qd + 4 h .. + 3, and the lane ends up with the 8
+// consecutive keys 8 qd .. 8 qd + 7.  Those are exactly the keys of the PV
+// MFMA's B operand (P^T) in that lane, and its A operand (V^T: dim r, the
+// same 8 keys) is one 16-byte run of the dim-major V page (page qd / 2,
+// slots 8 (qd % 2) .. + 7).  So P stays in its lanes, and each V^T load moves
+// 1 KB (16 dims x 32 keys) like each K load does.  The K row of MFMA h in lane
+// l is key 8 (r / 4) + 4 h + r % 4: page r / 8, slot 8 ((r / 4) % 2) + 4 h +
+// r % 4.
 
-// Issue the K (4 x 16 B per page) and V^T (8 x 8 B per page) fragment loads of
-// the step starting at key KB into buffer set SFX.  With K stored in 32-dim
-// slices of the page, each K load instruction reads one contiguous 1 KB
-// block (16 keys x 32 dims) and each V^T load 16 dims x 16 keys (512 B); the
-// loads are nontemporal (the KV is read once).
-#define DEC_LOAD(KB, SFX)                                                                     \
+// Issue the K (2 x D/32 loads of 16 B) and V^T (D/16 loads of 16 B) fragment
+// loads of the step starting at key KB.  Each K load instruction reads 16 keys
+// x 32 dims (1 KB) in 64-byte runs, each V^T load 16 dims x 32 keys (1 KB) in
+// 16-byte runs; the loads are nontemporal (the KV is read once).  Without a
+// second page, its lanes read the first page again (the keys are masked).
+#define DEC_ADDR(KB)                                                                          \
+  const int _j = ((KB) - it.key0) >> 4;                                                       \
+  const bool _has1 = (KB) + 16 < it.key1;                                                     \
+  const int _pg0 = __builtin_amdgcn_readlane(my_pg, _j);                                      \
+  const int _pg1 = __builtin_amdgcn_readlane(my_pg, _has1 ? _j + 1 : _j);                     \
+  const size_t _kb = ((size_t)((r >> 3) ? _pg1 : _pg0) * nkv + kvh) * hs + kslot * 32 + qd * 8; \
+  const size_t _vb = ((size_t)((qd >> 1) ? _pg1 : _pg0) * nkv + kvh) * hs + r * 16 + (qd & 1) * 8;
+
+#define DEC_LOAD(KB)                                                                          \
   {                                                                                           \
-    const int _j = ((KB) - it.key0) >> 4;                                                     \
-    const bool _has1 = (KB) + 16 < it.key1;                                                   \
-    const int _pg0 = __builtin_amdgcn_readlane(my_pg, _j);                                    \
-    const int _pg1 = __builtin_amdgcn_readlane(my_pg, _has1 ? _j + 1 : _j);                   \
-    const uint16_t* _K0 = static_cast<const uint16_t*>(a.k_cache) + ((size_t)_pg0 * nkv + kvh) * hs + r * 32 + qd * 8; \
-    const uint16_t* _K1 = static_cast<const uint16_t*>(a.k_cache) + ((size_t)_pg1 * nkv + kvh) * hs + r * 32 + qd * 8; \
-    const uint16_t* _V0 = static_cast<const uint16_t*>(a.v_cache) + ((size_t)_pg0 * nkv + kvh) * hs + r * 16 + qd * 4; \
-    const uint16_t* _V1 = static_cast<const uint16_t*>(a.v_cache) + ((size_t)_pg1 * nkv + kvh) * hs + r * 16 + qd * 4; \
-    _Pragma("unroll") for (int kk = 0; kk < KK; ++kk)                                         \
-        k0##SFX[kk] = load_stream16(_K0 + kk * 512);                                          \
-    _Pragma("unroll") for (int jj = 0; jj < NJ; ++jj)                                         \
-        v0##SFX[jj] = load_stream8(_V0 + jj * 256);                                           \
-    if (_has1) {                                                                              \
-      _Pragma("unroll") for (int kk = 0; kk < KK; ++kk)                                       \
-          k1##SFX[kk] = load_stream16(_K1 + kk * 512);                                        \
-      _Pragma("unroll") for (int jj = 0; jj < NJ; ++jj)                                       \
-          v1##SFX[jj] = load_stream8(_V1 + jj * 256);                                         \
-    } else {                                                                                  \
-      _Pragma("unroll") for (int kk = 0; kk < KK; ++kk) k1##SFX[kk] = make_uint4(0, 0, 0, 0); \
-      _Pragma("unroll") for (int jj = 0; jj < NJ; ++jj) v1##SFX[jj] = make_uint2(0, 0);       \
+    DEC_ADDR(KB)                                                                              \
+    const uint16_t* _K = static_cast<const uint16_t*>(a.k_cache) + _kb;                       \
+    const uint16_t* _V = static_cast<const uint16_t*>(a.v_cache) + _vb;                       \
+    _Pragma("unroll") for (int kk = 0; kk < KK; ++kk) {                                       \
+      k0[kk] = load_stream16(_K + kk * 512);                                                  \
+      k1[kk] = load_stream16(_K + kk * 512 + 4 * 32);                                         \
     }                                                                                         \
+    _Pragma("unroll") for (int jj = 0; jj < NJ; ++jj) vv[jj] = load_stream16(_V + jj * 256);  \
   }
 
-// FP8 cache: the same fragments as codes (8 bytes of K, 4 of V^T per lane and
-// page: byte offsets equal the bf16 element offsets) into raw buffer I; a
-// missing second page reads as zero codes.
+// FP8 cache: the same fragments as codes (byte offsets equal the bf16 element
+// offsets) into raw buffer I.
 #define DEC_LOAD8(KB, I)                                                                      \
   {                                                                                           \
-    const int _j = ((KB) - it.key0) >> 4;                                                     \
-    const bool _has1 = (KB) + 16 < it.key1;                                                   \
-    const int _pg0 = __builtin_amdgcn_readlane(my_pg, _j);                                    \
-    const int _pg1 = __builtin_amdgcn_readlane(my_pg, _has1 ? _j + 1 : _j);                   \
-    const uint8_t* _K0 = static_cast<const uint8_t*>(a.k_cache) + ((size_t)_pg0 * nkv + kvh) * hs + r * 32 + qd * 8; \
-    const uint8_t* _K1 = static_cast<const uint8_t*>(a.k_cache) + ((size_t)_pg1 * nkv + kvh) * hs + r * 32 + qd * 8; \
-    const uint8_t* _V0 = static_cast<const uint8_t*>(a.v_cache) + ((size_t)_pg0 * nkv + kvh) * hs + r * 16 + qd * 4; \
-    const uint8_t* _V1 = static_cast<const uint8_t*>(a.v_cache) + ((size_t)_pg1 * nkv + kvh) * hs + r * 16 + qd * 4; \
-    _Pragma("unroll") for (int kk = 0; kk < KK; ++kk) k0r[I][kk] = load_stream8(_K0 + kk * 512); \
-    _Pragma("unroll") for (int jj = 0; jj < NJ; ++jj) v0r[I][jj] = load_stream4(_V0 + jj * 256); \
-    if (_has1) {                                                                              \
-      _Pragma("unroll") for (int kk = 0; kk < KK; ++kk) k1r[I][kk] = load_stream8(_K1 + kk * 512); \
-      _Pragma("unroll") for (int jj = 0; jj < NJ; ++jj) v1r[I][jj] = load_stream4(_V1 + jj * 256); \
-    } else {                                                                                  \
-      _Pragma("unroll") for (int kk = 0; kk < KK; ++kk) k1r[I][kk] = make_uint2(0, 0);        \
-      _Pragma("unroll") for (int jj = 0; jj < NJ; ++jj) v1r[I][jj] = 0u;                      \
+    DEC_ADDR(KB)                                                                              \
+    const uint8_t* _K = static_cast<const uint8_t*>(a.k_cache) + _kb;                         \
+    const uint8_t* _V = static_cast<const uint8_t*>(a.v_cache) + _vb;                         \
+    _Pragma("unroll") for (int kk = 0; kk < KK; ++kk) {                                       \
+      k0r[I][kk] = load_stream8(_K + kk * 512);                                               \
+      k1r[I][kk] = load_stream8(_K + kk * 512 + 4 * 32);                                      \
     }                                                                                         \
+    _Pragma("unroll") for (int jj = 0; jj < NJ; ++jj) vr[I][jj] = load_stream8(_V + jj * 256); \
   }
 
-// Raw buffer I widened (exactly) into the bf16 buffer set SFX.
-#define DEC_WIDEN(I, SFX)                                                                     \
+// Raw buffer I widened (exactly) into the bf16 buffers.
+#define DEC_WIDEN(I)                                                                          \
   {                                                                                           \
     _Pragma("unroll") for (int kk = 0; kk < KK; ++kk) {                                       \
-      k0##SFX[kk] = fp8x8_bf16x8(k0r[I][kk]);                                                 \
-      k1##SFX[kk] = fp8x8_bf16x8(k1r[I][kk]);                                                 \
+      k0[kk] = fp8x8_bf16x8(k0r[I][kk]);                                                      \
+      k1[kk] = fp8x8_bf16x8(k1r[I][kk]);                                                      \
     }                                                                                         \
-    _Pragma("unroll") for (int jj = 0; jj < NJ; ++jj) {                                       \
-      v0##SFX[jj] = fp8x4_bf16x4(v0r[I][jj]);                                                 \
-      v1##SFX[jj] = fp8x4_bf16x4(v1r[I][jj]);                                                 \
-    }                                                                                         \
+    _Pragma("unroll") for (int jj = 0; jj < NJ; ++jj) vv[jj] = fp8x8_bf16x8(vr[I][jj]);       \
   }
 
-// Scores, online softmax and PV for the step starting at key KB from buffer SFX.
-#define DEC_COMPUTE(KB, SFX)                                                                  \
+// Scores, online softmax and PV for the step starting at key KB.
+#define DEC_COMPUTE(KB)                                                                       \
   {                                                                                           \
-    const bool _has1 = (KB) + 16 < it.key1;                                                   \
     f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;                                            \
-    _Pragma("unroll") for (int kk = 0; kk < KK; ++kk)                                         \
-        s0 = mfma16x16x32(as_bf16x8(k0##SFX[kk]), qf[kk], s0);                               \
-    if (_has1) {                                                                              \
-      _Pragma("unroll") for (int kk = 0; kk < KK; ++kk)                                       \
-          s1 = mfma16x16x32(as_bf16x8(k1##SFX[kk]), qf[kk], s1);                             \
+    _Pragma("unroll") for (int kk = 0; kk < KK; ++kk) {                                       \
+      s0 = mfma16x16x32(as_bf16x8(k0[kk]), qf[kk], s0);                                       \
+      s1 = mfma16x16x32(as_bf16x8(k1[kk]), qf[kk], s1);                                       \
     }                                                                                         \
-    /* raw scores; keys past the item's end are masked (tail step only) */                   \
+    /* raw scores of keys KB + 8 qd + e; keys past the item's end are masked */               \
     float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};                   \
+    const int _nv = it.key1 - ((KB) + 8 * qd); /* valid keys among this lane's 8 */           \
     if ((KB) + 32 > it.key1) {                                                                \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                         \
-        if ((KB) + 4 * qd + i >= it.key1) sv[i] = -INFINITY;                                  \
-        if ((KB) + 16 + 4 * qd + i >= it.key1) sv[4 + i] = -INFINITY;                         \
-      }                                                                                       \
+      _Pragma("unroll") for (int e = 0; e < 8; ++e)                                           \
+        if (e >= _nv) sv[e] = -INFINITY;                                                      \
     }                                                                                         \
     float mb = sv[0];                                                                         \
     _Pragma("unroll") for (int e = 1; e < 8; ++e) mb = fmaxf(mb, sv[e]);                      \
@@ -167,16 +164,11 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
     bf16x8 pf, pfl;                                                                           \
     split_p(ps, pf, pfl);                                                                     \
     if ((KB) + 32 > it.key1) { /* tail: values past the last key may be poisoned */           \
-      const int n0 = it.key1 - ((KB) + 4 * qd), n1 = it.key1 - ((KB) + 16 + 4 * qd);         \
-      _Pragma("unroll") for (int jj = 0; jj < NJ; ++jj) {                                     \
-        v0##SFX[jj] = keep_first(v0##SFX[jj], n0);                                            \
-        v1##SFX[jj] = keep_first(v1##SFX[jj], n1);                                            \
-      }                                                                                       \
+      _Pragma("unroll") for (int jj = 0; jj < NJ; ++jj) vv[jj] = keep_first8(vv[jj], _nv);    \
     }                                                                                         \
     _Pragma("unroll") for (int jj = 0; jj < NJ; ++jj) {                                       \
       acc[jj] *= alpha;                                                                       \
-      const bf16x8 vf =                                                                       \
-          as_bf16x8(make_uint4(v0##SFX[jj].x, v0##SFX[jj].y, v1##SFX[jj].x, v1##SFX[jj].y));  \
+      const bf16x8 vf = as_bf16x8(vv[jj]);                                                    \
       acc[jj] = mfma16x16x32(vf, pf, acc[jj]);                                                \
       acc[jj] = mfma16x16x32(vf, pfl, acc[jj]);                                               \
     }                                                                                         \
@@ -195,6 +187,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
   const hb_attn_item it = a.meta.decode_items[item_idx];
   const int g = a.group, nq = a.n_q_heads, nkv = a.n_kv_heads;
   const int r = lane & 15, qd = lane >> 4;
+  const int kslot = 8 * ((r >> 2) & 1) + (r & 3);   // K slot of MFMA 0's row r (MFMA 1: + 4)
   const int t = it.tok0;
   const int32_t* bt = a.meta.block_table + (size_t)it.seq * a.max_pages;
   const int npg = (it.key1 - it.key0 + 15) >> 4;
@@ -213,28 +206,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
   float m = -INFINITY, l = 0.f;
   const size_t hs = (size_t)16 * D;  // elements of one (page, kv head) block
 
-  uint4 k0A[KK], k1A[KK];
-  uint2 v0A[NJ], v1A[NJ];
+  uint4 k0[KK], k1[KK], vv[NJ];
   if constexpr (F8) {
     // two steps' codes in flight (the bytes of one bf16 step), each widened
     // just before its MFMAs
-    uint2 k0r[2][KK], k1r[2][KK];
-    uint32_t v0r[2][NJ], v1r[2][NJ];
+    uint2 k0r[2][KK], k1r[2][KK], vr[2][NJ];
     for (int kb = it.key0; kb < it.key1; kb += 64) {
       const bool second = kb + 32 < it.key1;
       DEC_LOAD8(kb, 0);
       if (second) DEC_LOAD8(kb + 32, 1);
-      DEC_WIDEN(0, A);
-      DEC_COMPUTE(kb, A);
+      DEC_WIDEN(0);
+      DEC_COMPUTE(kb);
       if (second) {
-        DEC_WIDEN(1, A);
-        DEC_COMPUTE(kb + 32, A);
+        DEC_WIDEN(1);
+        DEC_COMPUTE(kb + 32);
       }
     }
   } else {
     for (int kb = it.key0; kb < it.key1; kb += 32) {
-      DEC_LOAD(kb, A);
-      DEC_COMPUTE(kb, A);
+      DEC_LOAD(kb);
+      DEC_COMPUTE(kb);
     }
   }
   l += __shfl_xor(l, 16, 64);
@@ -255,6 +246,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
   }
 }
 
+#undef DEC_ADDR
 #undef DEC_LOAD
 #undef DEC_LOAD8
 #undef DEC_WIDEN
@@ -305,12 +297,6 @@ __device__ __forceinline__ int kperm(int i) {
   return 16 * (i >> 4) + 8 * ((i >> 2) & 1) + 4 * ((i >> 3) & 1) + (i & 3);
 }
 
-__device__ __forceinline__ uint4 keep_first8(uint4 v, int n) {
-  // keep the first n (0..8) bf16 values of an 8-value vector, zero the rest
-  const uint2 lo = keep_first(make_uint2(v.x, v.y), n);
-  const uint2 hi = keep_first(make_uint2(v.z, v.w), n - 4);
-  return make_uint4(lo.x, lo.y, hi.x, hi.y);
-}
 
 // F8: the cache holds FP8 e4m3 codes.  Pages then come through registers
 // (each wave loads its page's codes, widens them exactly to bf16 and writes the
