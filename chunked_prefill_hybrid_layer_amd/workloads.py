@@ -104,6 +104,11 @@ class Dims:
     kv_fp8: int = 0            # 1: FP8 e4m3 KV cache with the scales below
     k_scale: float = 1.0
     v_scale: float = 1.0
+    w8a8: int = 0              # 1: FP8 e4m3 projections (weights and their inputs)
+    x_scale: float = 1.0       # static scales of the four projection inputs
+    o_scale: float = 1.0
+    h_scale: float = 1.0
+    a_scale: float = 1.0
 
     @property
     def group(self) -> int:
@@ -193,6 +198,38 @@ def make_weights(dims: Dims, rng: np.random.Generator, std: float = 0.02) -> Dic
     w["g_attn"] = normal_bf16(kids[-2], (H,), 0.02, 1.0)
     w["g_ffn"] = normal_bf16(kids[-1], (H,), 0.02, 1.0)
     return w
+
+
+WEIGHT_SHAPES = ("w_q", "w_k", "w_v", "w_o", "w_g", "w_u", "w_d")
+
+
+def make_weights_fp8(dims: Dims, seed: np.random.SeedSequence, rms: float = 0.02) -> Dict[str, np.ndarray]:
+    """Projection matrices as e4m3 codes drawn bit field by bit field: random
+    sign, exponent field uniform in 4..11, mantissa field uniform in 0..7
+    (magnitudes 1/8 .. 30, log-uniform), and one float32 scale per output row,
+    rms / 9 * U(0.5, 1.5), so that the weights' rms is about ``rms``.  Norm
+    gains as in make_weights."""
+    H, d, F = dims.hidden, dims.head_dim, dims.ffn_dim
+    shapes = {"w_q": (dims.n_q_heads * d, H), "w_k": (dims.n_kv_heads * d, H), "w_v": (dims.n_kv_heads * d, H),
+              "w_o": (H, dims.n_q_heads * d), "w_g": (F, H), "w_u": (F, H), "w_d": (H, F)}
+    kids = seed.spawn(len(shapes) + 2)
+    w = {}
+    for kid, (name, shp) in zip(kids, shapes.items()):
+        g = np.random.Generator(np.random.PCG64(kid))
+        sign = g.integers(0, 2, size=shp, dtype=np.uint8) << 7
+        expo = g.integers(4, 12, size=shp, dtype=np.uint8) << 3
+        mant = g.integers(0, 8, size=shp, dtype=np.uint8)
+        w[name] = (sign | expo | mant).astype(np.uint8)
+        w["s_" + name] = (np.float32(rms / 9.0) * g.uniform(0.5, 1.5, size=shp[0]).astype(np.float32)).astype(np.float32)
+    w["g_attn"] = normal_bf16(kids[-2], (H,), 0.02, 1.0)
+    w["g_ffn"] = normal_bf16(kids[-1], (H,), 0.02, 1.0)
+    return w
+
+
+# static projection-input scales of the synthetic FP8 workloads (powers of two:
+# N(0, 1)-sized xn and h1n, attention outputs within +-4, SwiGLU outputs within
+# +-50, all well inside e4m3's +-448 over the scale)
+FP8_ACT_SCALES = dict(x_scale=2.0 ** -4, o_scale=2.0 ** -5, h_scale=2.0 ** -4, a_scale=2.0 ** -3)
 
 
 def make_activations(n_tokens: int, hidden: int, rng: np.random.Generator, std: float) -> np.ndarray:
@@ -321,6 +358,15 @@ def with_kv_fp8(wl: Workload, k_scale: float = FP8_K_SCALE, v_scale: float = FP8
     when they are written)."""
     wl.dims = dataclasses.replace(wl.dims, kv_fp8=1, k_scale=float(k_scale), v_scale=float(v_scale))
     wl.name += "_kvfp8"
+    return wl
+
+
+def with_w8a8(wl: Workload, seed: int = 0) -> Workload:
+    """The same workload with FP8 projections: fresh e4m3 weight codes and row
+    scales (make_weights_fp8) and the static input scales FP8_ACT_SCALES."""
+    wl.dims = dataclasses.replace(wl.dims, w8a8=1, **FP8_ACT_SCALES)
+    wl.weights = make_weights_fp8(wl.dims, np.random.SeedSequence([seed, 8]))
+    wl.name += "_w8a8"
     return wl
 
 

@@ -50,6 +50,17 @@ format's largest finite value; 0x7F / 0xFF are NaN and mark unwritten slots).
 The quotient x / scale is taken in single precision (see ``fp8_quotient``), and
 attention reads code * scale.
 
+FP8 projections (w8a8 = 1; not on the pages, which name FP8 only as moving
+the compute/bandwidth knee): the weights are e4m3 codes with one float32 scale
+per output channel (row of the [d_out][d_in] matrix), and the four
+projection inputs -- the normed input xn, the attention output o, the normed
+residual h1n and the SwiGLU output a -- are stored as e4m3 codes of
+value / scale with one static float32 scale each (x_scale, o_scale, h_scale,
+a_scale), taken as for the KV cache (``fp8_quotient``, nearest-even,
+saturating).  A projection is then (codes_a * s_a) . (codes_w * s_w)^T,
+computed exactly.  q, the KV cache (bf16 or its own FP8) and the fp32
+residual stream are unchanged.
+
 Page layout of the oracle's own cache: ``k[page][kv_head][slot][d]`` (logical
 order, float64); a sequence's position p lives in page
 ``block_table[s][p // page_size]`` at slot ``p % page_size`` ([notes] §3.5,
@@ -239,6 +250,19 @@ def fp8_quotient(x, scale) -> np.ndarray:
     code, so the kernels' single-precision product is the definition here."""
     inv = np.float32(1.0) / np.float32(scale)
     return (np.asarray(x, dtype=np.float64).astype(np.float32) * inv).astype(np.float64)
+
+
+def fp8_store(x, scale) -> np.ndarray:
+    """The value an e4m3 store of x with the given scale reads back:
+    decode(encode(x / scale)) * scale, the quotient as in ``fp8_quotient``."""
+    return e4m3_decode(e4m3_encode(fp8_quotient(x, scale))) * np.float64(np.float32(scale))
+
+
+def fp8_weight(codes, row_scales) -> np.ndarray:
+    """Weights [d_out][d_in] from e4m3 codes and one float32 scale per
+    output row."""
+    s = np.asarray(row_scales, dtype=np.float32).astype(np.float64)
+    return e4m3_decode(codes) * s[:, None]
 
 
 class PagedCache:
@@ -446,9 +470,14 @@ def layer_forward(dims, w: Dict[str, np.ndarray], x: np.ndarray, chunk_len, chun
     rows = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
     x = np.asarray(x, dtype=np.float64)
     flops = 0
+    # projection inputs: bf16 storage, or e4m3 codes with a static scale
+    if getattr(dims, "w8a8", 0):
+        gin = lambda a, name: fp8_store(a, getattr(dims, name))
+    else:
+        gin = lambda a, name: act(a)
 
     # a1: RMSNorm of the input (all tokens: K/V need it)
-    xn = act(rmsnorm(x, w["g_attn"], dims.rms_eps))
+    xn = gin(rmsnorm(x, w["g_attn"], dims.rms_eps), "x_scale")
     # a2 + a3: projections and rotary embedding
     k, f = linear(xn, w["w_k"]); flops += f
     v, f = linear(xn, w["w_v"]); flops += f
@@ -469,16 +498,16 @@ def layer_forward(dims, w: Dict[str, np.ndarray], x: np.ndarray, chunk_len, chun
 
     # a5: each token attends causally to positions 0..pos of its own sequence
     o, pairs = paged_attention(q, lay.seq[rows], lay.pos[rows], cache, block_table, nkv)
-    o = act(o.reshape(len(rows), nq * d))
+    o = gin(o.reshape(len(rows), nq * d), "o_scale")
 
     # a6: output projection + residual
     ao, f = linear(o, w["w_o"]); flops += f
     h1 = res(x[rows] + ao)
     # a7 + a8: RMSNorm, gate/up projections and SwiGLU
-    h1n = act(rmsnorm(h1, w["g_ffn"], dims.rms_eps))
+    h1n = gin(rmsnorm(h1, w["g_ffn"], dims.rms_eps), "h_scale")
     gt, f1 = linear(h1n, w["w_g"])
     up, f2 = linear(h1n, w["w_u"])
-    a = act(silu(gt) * up)
+    a = gin(silu(gt) * up, "a_scale")
     # a9: down projection + residual
     dn, f3 = linear(a, w["w_d"])
     flops += f1 + f2 + f3
@@ -487,4 +516,14 @@ def layer_forward(dims, w: Dict[str, np.ndarray], x: np.ndarray, chunk_len, chun
 
 
 def weights_to_float(wbits: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
-    return {k: bf16_bits_to_float(v) for k, v in wbits.items()}
+    """Layer parameters as float64: bf16 bit patterns, or (w8a8) projection
+    matrices as e4m3 codes with row scales under "s_" + name."""
+    out = {}
+    for k, v in wbits.items():
+        if k.startswith("s_"):
+            continue
+        if ("s_" + k) in wbits:
+            out[k] = fp8_weight(v, wbits["s_" + k])
+        else:
+            out[k] = bf16_bits_to_float(v)
+    return out

@@ -516,3 +516,63 @@ def test_fp8_quotient_is_single_precision():
     c.write(np.array([[0]], dtype=np.int32), 0, 0, np.full((1, 32), 0.75), np.full((1, 32), -0.75))
     assert np.all(c.codes[0][0] == np.where(np.arange(16)[:, None] == 0, 0x5D, 0x7F))
     assert np.all(c.pages[0][1, 0, 0] == -26 * np.float64(np.float32(0.03)))
+
+
+# ---------------------------------------------------------------- FP8 projections (w8a8)
+
+def test_fp8_weight_rows_take_their_own_scale():
+    """Row n of a projection is codes[n] * scale[n] (one scale per output
+    channel, taken as float32): worked by hand."""
+    codes = np.full((3, 4), 0x38, dtype=np.uint8)    # 1.0
+    codes[1, 2] = 0xC0                                 # -2.0
+    codes[2, 0] = 0x01                                 # 2^-9 (smallest subnormal)
+    w = O.fp8_weight(codes, [0.5, 2.0, 0.25])
+    assert np.array_equal(w, [[0.5] * 4, [2.0, 2.0, -4.0, 2.0], [2.0 ** -11, 0.25, 0.25, 0.25]])
+    assert O.fp8_weight(np.array([[0x38]], np.uint8), [0.1])[0, 0] == np.float64(np.float32(0.1))
+    wts = O.weights_to_float({"w_o": codes, "s_w_o": np.array([0.5, 2.0, 0.25], np.float32),
+                              "g_ffn": np.array([0x3F80], np.uint16)})
+    assert set(wts) == {"w_o", "g_ffn"} and np.array_equal(wts["w_o"], w) and wts["g_ffn"][0] == 1.0
+
+
+def test_fp8_store_reads_back_codes_times_scale():
+    s = 2.0 ** -4
+    # values that are codes * scale come back unchanged
+    codes = np.arange(0, 0x7F, dtype=np.uint8)
+    v = O.e4m3_decode(codes) * s
+    assert np.array_equal(O.fp8_store(v, s), v) and np.array_equal(O.fp8_store(-v, s), -v)
+    # others: nearest code, within half a step (relative 2^-4 for normals)
+    x = np.random.default_rng(3).standard_normal(10000)
+    y = O.fp8_store(x, s)
+    normal = np.abs(x) >= 2.0 ** -6 * s
+    assert np.all(np.abs(y - x)[normal] <= 2.0 ** -4 * np.abs(x)[normal] * 1.0000001)
+    assert np.all(np.abs(y - x)[~normal] <= 2.0 ** -10 * s)
+    # scale equivariance for a power-of-two factor, saturation at 448 * scale
+    assert np.array_equal(O.fp8_store(4 * x, 4 * s), 4 * y)
+    assert O.fp8_store(np.array([1e6, -1e6]), 0.01).tolist() == [448 * np.float64(np.float32(0.01)),
+                                                                  -448 * np.float64(np.float32(0.01))]
+
+
+def test_w8a8_layer_within_the_quantisation_error_of_the_exact_layer():
+    """With FP8 weights, the w8a8 layer differs from the exact layer over the
+    same (decoded) weights only by the e4m3 storage of the four projection
+    inputs: a relative error of at most 2^-4 per stored value (about 2^-4 /
+    sqrt(3) rms), so the layer's update y - x moves by a few percent, not by
+    factors (a missing or misplaced scale) and not by zero (no quantisation)."""
+    from chunked_prefill_hybrid_layer_amd import workloads as W
+    wl = W.with_w8a8(W.small(2, n_q=4, n_kv=2, head_dim=64, chunk_len=(20,), chunk_prefix=(5,),
+                             decode_ctx=(3, 17), hidden=128, ffn=256))
+    b = wl.batch
+    w = O.weights_to_float(wl.weights)
+    def run(dims, storage):
+        cache = O.PagedCache(b.num_pages, dims.n_kv_heads, dims.page_size, dims.head_dim)
+        for s in range(b.n_seq):
+            cache.load_prefix(b.block_table, s, O.bf16_bits_to_float(wl.prefix_k[s]),
+                              O.bf16_bits_to_float(wl.prefix_v[s]))
+        return O.layer_forward(dims, w, wl.x, b.chunk_len, b.chunk_prefix, b.decode_ctx, b.block_table, cache,
+                               storage=storage).y
+    import dataclasses
+    y8 = run(wl.dims, "exact")
+    ye = run(dataclasses.replace(wl.dims, w8a8=0), "exact")
+    d8, de = y8 - wl.x, ye - wl.x
+    rel = np.linalg.norm(d8 - de) / np.linalg.norm(de)
+    assert 1e-3 < rel < 0.1, rel
