@@ -31,6 +31,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 STAGE_EVERY = 8                # timed steps per step that records the per-stage HIP events
 
@@ -63,23 +64,24 @@ def stage_model(wl):
     dec_pairs = int(np.sum(b.decode_ctx.astype(np.int64) + 1))
     kv_elem = 1 if getattr(d, "kv_fp8", 0) else 2            # bytes per cached K/V element
     kv_bytes_per_key = nkv * D * 2 * kv_elem                # K and V
+    we = 1 if getattr(d, "w8a8", 0) else 2                   # bytes per weight / projection-input element
     chunk_kv_keys = int(np.sum(cached[:b.n_chunks] + new[:b.n_chunks]))
     blob, _ = hb.pack_metadata(hb.make_dims(d), b.chunk_len, b.chunk_prefix, b.decode_ctx, b.block_table,
                                b.num_pages, b.token_budget)
     npart = hb.header(blob).n_partials
     part_bytes = npart * nq * (D + 2) * 4
     m = {
-        "rmsnorm_attn": (0, T * H * 4 + T * H * 2 + H * 2, "hbm"),
+        "rmsnorm_attn": (0, T * H * 4 + T * H * we + H * 2, "hbm"),
         "qkv_rope_append": (2 * T * H * (nq + 2 * nkv) * D,
-                            (nq + 2 * nkv) * D * H * 2 + T * H * 2 + T * nq * D * 2 + T * 2 * nkv * D * kv_elem,
+                            (nq + 2 * nkv) * D * H * we + T * H * we + T * nq * D * 2 + T * 2 * nkv * D * kv_elem,
                             "mfma"),
         "attn_chunk": (4 * chunk_pairs * nq * D, chunk_kv_keys * kv_bytes_per_key, "mfma"),
         "attn_decode": (4 * dec_pairs * nq * D, dec_pairs * kv_bytes_per_key, "hbm"),
-        "attn_merge": (0, part_bytes + T * nq * D * 2, "hbm"),
-        "o_proj_residual": (2 * T * nq * D * H, nq * D * H * 2 + T * nq * D * 2 + 2 * T * H * 4, "mfma"),
-        "rmsnorm_ffn": (0, T * H * 4 + T * H * 2 + H * 2, "hbm"),
-        "gate_up_swiglu": (2 * T * H * 2 * F, 2 * F * H * 2 + T * H * 2 + T * F * 2, "mfma"),
-        "down_residual": (2 * T * F * H, F * H * 2 + T * F * 2 + 2 * T * H * 4, "mfma"),
+        "attn_merge": (0, part_bytes + T * nq * D * we, "hbm"),
+        "o_proj_residual": (2 * T * nq * D * H, nq * D * H * we + T * nq * D * we + 2 * T * H * 4, "mfma"),
+        "rmsnorm_ffn": (0, T * H * 4 + T * H * we + H * 2, "hbm"),
+        "gate_up_swiglu": (2 * T * H * 2 * F, 2 * F * H * we + T * H * we + T * F * we, "mfma"),
+        "down_residual": (2 * T * F * H, F * H * we + T * F * we + 2 * T * H * 4, "mfma"),
     }
     return m
 
@@ -289,12 +291,17 @@ def bench_batch(wl, name, steps, warmup, copies, calibrate_copy=False):
     stage_mean = stage_ms.mean(axis=0)
 
     model = stage_model(wl)
+    w8a8 = bool(getattr(d, "w8a8", 0))
+    # projections (and attention's QK/PV) on MFMA: the projections' peak sets the
+    # roofline of MFMA-bound stages (attention stays bf16; its stages are not
+    # the dominant ones in either precision)
+    peak_mfma = PEAK_FP8_TFLOPS if w8a8 else PEAK_BF16_TFLOPS
     stages = {}
     t_roof = 0.0
     for k, sname in enumerate(hb.STAGE_NAMES):
         fl, by, bound = model[sname]
         t = float(stage_mean[k]) * 1e-3
-        t_ideal = max(fl / (PEAK_BF16_TFLOPS * 1e12), by / (PEAK_HBM_GBS * 1e9))
+        t_ideal = max(fl / (peak_mfma * 1e12), by / (PEAK_HBM_GBS * 1e9))
         t_roof += t_ideal
         stages[sname] = {"ms": round(float(stage_mean[k]), 5), "tflops": round(fl / t / 1e12, 2) if t > 0 else None,
                          "gbs": round(by / t / 1e9, 1) if t > 0 else None, "bound": bound,
@@ -303,7 +310,7 @@ def bench_batch(wl, name, steps, warmup, copies, calibrate_copy=False):
     fl, by, bound = model[dom]
     tdom = stages[dom]["ms"] * 1e-3
     if bound == "mfma":
-        roof = {"bound": "mfma", "achieved": round(fl / tdom / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
+        roof = {"bound": "mfma", "achieved": round(fl / tdom / 1e12, 2), "peak": peak_mfma,
                 "unit": "TFLOP/s"}
     else:
         roof = {"bound": "hbm", "achieved": round(by / tdom / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
@@ -323,7 +330,7 @@ def bench_batch(wl, name, steps, warmup, copies, calibrate_copy=False):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8 e4m3 projections, bf16 attention" if w8a8 else "bf16",
         "data": "synthetic",
         "config": {"workload": name, "hidden": d.hidden, "n_q_heads": d.n_q_heads,
                    "n_kv_heads": d.n_kv_heads, "head_dim": d.head_dim, "ffn_dim": d.ffn_dim,
@@ -332,7 +339,9 @@ def bench_batch(wl, name, steps, warmup, copies, calibrate_copy=False):
                    "decode_ctx_mean": float(np.mean(b.decode_ctx)) if b.n_decodes else 0.0,
                    "token_budget": b.token_budget, "page_size": d.page_size, "copies_rotated": copies,
                    "kv_cache": ("fp8_e4m3 (k_scale %g, v_scale %g)" % (d.k_scale, d.v_scale)) if d.kv_fp8
-                   else "bf16"},
+                   else "bf16",
+                   "projections": ("fp8_e4m3 (row-scaled weights, input scales %g/%g/%g/%g)" %
+                                   (d.x_scale, d.o_scale, d.h_scale, d.a_scale)) if w8a8 else "bf16"},
         "layer_iters_per_s": round(1e3 / ms, 1),
         "layer_roofline_frac": round(t_roof / (ms * 1e-3), 4),
         "step_ms_p10_p50_p90": [round(float(np.percentile(step_ms, q)), 5) for q in (10, 50, 90)],
@@ -625,6 +634,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kv-fp8", action="store_true",
                     help="FP8 e4m3 KV cache (k_scale 2^-4, v_scale 2^-3) instead of bf16")
+    ap.add_argument("--w8a8", action="store_true",
+                    help="FP8 e4m3 projections (weights and their inputs) on the FP8 MFMA")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, copy 256 MiB device-to-device once (counter calibration)")
     ap.add_argument("--sweep-tau", action="store_true", help="token-budget sweep, one line per tau")
@@ -652,8 +663,11 @@ def main():
         return chunk_sweep_bench(args)
     wl = workload_by_name(args.workload)
     name = args.workload
+    from chunked_prefill_hybrid_layer_amd import workloads as W
+    if args.w8a8:
+        wl = W.with_w8a8(wl)
+        name += "_w8a8"
     if args.kv_fp8:
-        from chunked_prefill_hybrid_layer_amd import workloads as W
         wl = W.with_kv_fp8(wl)
         name += "_kvfp8"
     out = bench_batch(wl, name, args.steps, args.warmup, args.copies, args.calibrate_copy)

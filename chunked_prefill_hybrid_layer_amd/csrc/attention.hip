@@ -630,10 +630,17 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
     }
   }
   const float inv = 1.0f / L;
-  uint2 pk;
-  pk.x = pack2bf(o.x * inv, o.y * inv);
-  pk.y = pack2bf(o.z * inv, o.w * inv);
-  *reinterpret_cast<uint2*>(a.out + (size_t)t * nq * D + (size_t)h * D + l4 * 4) = pk;
+  const size_t oi = (size_t)t * nq * D + (size_t)h * D + l4 * 4;
+  if (a.out_inv_scale > 0.0f) {   // FP8 codes of o / o_scale (the O projection's input)
+    const float q = a.out_inv_scale;
+    *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(a.out) + oi) =
+        pack4fp8(o.x * inv * q, o.y * inv * q, o.z * inv * q, o.w * inv * q);
+  } else {
+    uint2 pk;
+    pk.x = pack2bf(o.x * inv, o.y * inv);
+    pk.y = pack2bf(o.z * inv, o.w * inv);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + oi) = pk;
+  }
 }
 
 template <int D, bool F8>

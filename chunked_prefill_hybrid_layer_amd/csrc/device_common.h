@@ -77,6 +77,18 @@ __device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b,
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// FP8 e4m3 x e4m3 MFMA (gfx950 f8f6f4 family, format 0 for both operands,
+// unit E8M0 block scales): D[16][16] += A[16][128] B^T.  Lane l holds row
+// (or column) l % 16 and 32 of the 128 K positions; which 32 does not matter
+// as long as A and B use the same assignment (checked on the device).
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x4 mfma16x16x128_f8(const i32x8& a, const i32x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+__device__ __forceinline__ i32x8 cat_i32x8(const uint4& lo, const uint4& hi) {
+  return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
 // LDS destination of a direct-to-LDS load (global_load_lds_dwordx4): the
 // wave's 64 lanes land at consecutive 16-byte chunks from this address.
 typedef __attribute__((address_space(3))) void* lds_ptr_t;

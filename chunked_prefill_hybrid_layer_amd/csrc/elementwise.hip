@@ -18,7 +18,8 @@ constexpr int kNormMaxChunks = 16;
 
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x,
                                                       const uint16_t* __restrict__ gain,
-                                                      uint16_t* __restrict__ out, int hidden, float eps) {
+                                                      void* __restrict__ out, int hidden, float eps,
+                                                      float out_inv_scale) {
   __shared__ float red[4];
   const int row = blockIdx.x;
   const float4* xr = reinterpret_cast<const float4*>(x + (size_t)row * hidden);
@@ -38,26 +39,32 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
   __syncthreads();
   const float total = (red[0] + red[1]) + (red[2] + red[3]);
   const float r = 1.0f / sqrtf(total / (float)hidden + eps);
-  uint2* orow = reinterpret_cast<uint2*>(out + (size_t)row * hidden);
   const uint2* g2 = reinterpret_cast<const uint2*>(gain);
+  const bool f8 = out_inv_scale > 0.0f;   // FP8 codes of the normed row / scale
+  uint2* orow = reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + (size_t)row * hidden);
+  uint32_t* crow = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(out) + (size_t)row * hidden);
 #pragma unroll
   for (int k = 0; k < kNormMaxChunks; ++k) {
     const int i = threadIdx.x + 256 * k;
     if (i < n4) {
       const uint2 gg = g2[i];
-      uint2 o;
-      o.x = pack2bf(v[k].x * r * bf2f((uint16_t)(gg.x & 0xffff)), v[k].y * r * bf2f((uint16_t)(gg.x >> 16)));
-      o.y = pack2bf(v[k].z * r * bf2f((uint16_t)(gg.y & 0xffff)), v[k].w * r * bf2f((uint16_t)(gg.y >> 16)));
-      orow[i] = o;
+      const float y0 = v[k].x * r * bf2f((uint16_t)(gg.x & 0xffff)), y1 = v[k].y * r * bf2f((uint16_t)(gg.x >> 16));
+      const float y2 = v[k].z * r * bf2f((uint16_t)(gg.y & 0xffff)), y3 = v[k].w * r * bf2f((uint16_t)(gg.y >> 16));
+      if (f8) {
+        crow[i] = pack4fp8(y0 * out_inv_scale, y1 * out_inv_scale, y2 * out_inv_scale, y3 * out_inv_scale);
+      } else {
+        orow[i] = make_uint2(pack2bf(y0, y1), pack2bf(y2, y3));
+      }
     }
   }
 }
 
-hb_status launch_rmsnorm(const float* x, const uint16_t* gain, uint16_t* out, int rows, int hidden,
-                         float eps, stream_t s) {
+hb_status launch_rmsnorm(const float* x, const uint16_t* gain, void* out, int rows, int hidden,
+                         float eps, stream_t s, float out_inv_scale) {
   if (rows <= 0) return HB_OK;
   if (hidden > 256 * 4 * kNormMaxChunks) return fail(HB_E_SHAPE, "rmsnorm: hidden above 16384");
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3(rows), dim3(256), 0, (hipStream_t)s, x, gain, out, hidden, eps);
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(rows), dim3(256), 0, (hipStream_t)s, x, gain, out, hidden, eps,
+                     out_inv_scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(HB_E_HIP, std::string("rmsnorm launch: ") + hipGetErrorString(e));
   return HB_OK;

@@ -108,6 +108,24 @@ __device__ __forceinline__ const uint16_t* weight_row(const GemmArgs& g, int n, 
     return g.w0 + (size_t)n * g.K;
   }
 }
+// FP8 projections: the scale of the weight row behind GEMM column n (the
+// same mapping as weight_row).
+template <int MODE, int BN>
+__device__ __forceinline__ float weight_scale(const GemmArgs& g, int n, int n0) {
+  if (MODE == kGemmQkvRope) {
+    const int d = g.head_dim, h = n / d, p = n - h * d;
+    n = h * d + (p >> 1) + (p & 1) * (d >> 1);
+    if (n < g.n0) return g.ws0[n];
+    if (n < g.n0 + g.n1) return g.ws1[n - g.n0];
+    return g.ws2[n - g.n0 - g.n1];
+  } else if (MODE == kGemmSwiglu) {
+    const int f0 = n0 / 2, c = n - n0;
+    return (c < BN / 2) ? g.ws0[f0 + c] : g.ws1[f0 + c - BN / 2];
+  } else {
+    return g.ws0[n];
+  }
+}
+
 // QKV output of token m, GEMM columns n .. n + 7 (n a multiple of 8): dims
 // i0 .. i0 + 3 (x0) and i0 + d/2 .. i0 + d/2 + 3 (x1) of one head, where
 // i0 = (n mod d) / 2.  q and k are rotated by the token's position (rotate-
@@ -194,6 +212,15 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x4 (&acc)[TL
   constexpr int WROWS = BM / TL::WM, WCOLS = BN / TL::WN, CS_LD = TL::CS_LD;
   float* Cs = reinterpret_cast<float*>(smem);
   constexpr int ER = TL::EPI_ROWS;
+  if (g.f8) {   // codes -> values: input scale times the weight row's scale, per column
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int n = n0 + wn * WCOLS + j * 16 + (lane & 15);
+      const float sc = g.a_scale * weight_scale<MODE, BN>(g, n, n0);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) acc[i][j] *= sc;
+    }
+  }
 #pragma unroll
   for (int p = 0; p < BM / ER; ++p) {
     if (p > 0) __syncthreads();
@@ -245,10 +272,16 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x4 (&acc)[TL
           const float z = gr[e];
           o[e] = z / (1.0f + __expf(-z)) * ur[e];
         }
-        uint2 pk;
-        pk.x = pack2bf(o[0], o[1]);
-        pk.y = pack2bf(o[2], o[3]);
-        *reinterpret_cast<uint2*>(g.out_b + (size_t)m * g.ldo + f0 + c4 * 4) = pk;
+        if (g.f8) {   // the down projection's input: FP8 codes of out / a_scale
+          const float q = g.out_inv_scale;
+          *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(g.out_b) + (size_t)m * g.ldo + f0 + c4 * 4) =
+              pack4fp8(o[0] * q, o[1] * q, o[2] * q, o[3] * q);
+        } else {
+          uint2 pk;
+          pk.x = pack2bf(o[0], o[1]);
+          pk.y = pack2bf(o[2], o[3]);
+          *reinterpret_cast<uint2*>(g.out_b + (size_t)m * g.ldo + f0 + c4 * 4) = pk;
+        }
       }
     } else {  // QKV + RoPE + KV append: one thread per (token, 4 rotated pairs)
       for (int idx = tid; idx < ER * (BN / 8); idx += NT) {
@@ -264,7 +297,11 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x4 (&acc)[TL
   }
 }
 
-template <int MODE, class TL>
+// F8: A and the weights are e4m3 codes (K counted in 16-bit units, so a 64-unit
+// stage row is 128 codes).  The LDS images, loads and swizzles are the bf16
+// ones; a lane's MFMA operand is the two 16-byte chunks qd and 4 + qd of its
+// row (the chunks the two bf16 K steps read), one 16x16x128 MFMA per stage.
+template <int MODE, class TL, bool F8>
 __global__ __launch_bounds__(TL::THREADS) void gemm_kernel(GemmArgs g) {
   constexpr int BM = TL::BM, BN = TL::BN, BK = TL::BK, NST = TL::NST, SE = TL::STAGE_ELEMS;
   constexpr int NL = TL::LOADS, NT = TL::THREADS, FM = TL::FM, FN = TL::FN, KS = TL::KS, CPR = TL::CPR;
@@ -364,6 +401,39 @@ __global__ __launch_bounds__(TL::THREADS) void gemm_kernel(GemmArgs g) {
   // fragment reads of stage KT+1 in between.
   static_assert(FN >= FM, "A fragments are read alongside the first FM column blocks");
   constexpr int LEAD = NST;   // stages issued ahead of the one computed
+
+  // FP8 operands: 32 codes per lane (chunks qd and 4 + qd of the row).  The
+  // chunks are read as bf16x8, the type the bf16 path reads: read as uint4,
+  // the compiler put a wait for every in-flight direct-to-LDS load before each
+  // LDS read of the stage loop, which serialised the prefetch.
+  i32x8 fa8[2][FM], fb8[FN];
+#define FRAG8(DST, BASE, R)                                                                      \
+  {                                                                                              \
+    const int _r = (R);                                                                          \
+    const bf16x8 _lo = *reinterpret_cast<const bf16x8*>((BASE) + _r * BK + swz<CPR>(_r, (lane >> 4)) * 8); \
+    const bf16x8 _hi = *reinterpret_cast<const bf16x8*>((BASE) + _r * BK + swz<CPR>(_r, 4 + (lane >> 4)) * 8); \
+    DST = cat_i32x8(__builtin_bit_cast(uint4, _lo), __builtin_bit_cast(uint4, _hi));             \
+  }
+#define LOAD_FRAGS8(B, KT)                                                                       \
+  {                                                                                              \
+    const uint16_t* _as = lds + ((KT) % NST) * SE;                                               \
+    const uint16_t* _bs = _as + BM * BK;                                                         \
+    _Pragma("unroll") for (int i = 0; i < FM; ++i) FRAG8(fa8[B][i], _as, wm * WROWS + i * 16 + (lane & 15)); \
+    _Pragma("unroll") for (int j = 0; j < FN; ++j) FRAG8(fb8[j], _bs, wn * WCOLS + j * 16 + (lane & 15)); \
+  }
+#define MFMAS8(CUR, NXT, KT1, NEXT)                                                              \
+  {                                                                                              \
+    const uint16_t* _as = lds + ((KT1) % NST) * SE;                                              \
+    const uint16_t* _bs = _as + BM * BK;                                                         \
+    _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                             \
+      _Pragma("unroll") for (int i = 0; i < FM; ++i)                                             \
+        acc[i][j] = mfma16x16x128_f8(fa8[CUR][i], fb8[j], acc[i][j]);                            \
+      if (NEXT) {                                                                                \
+        FRAG8(fb8[j], _bs, wn * WCOLS + j * 16 + (lane & 15));                                   \
+        if (j < FM) FRAG8(fa8[NXT][j < FM ? j : 0], _as, wm * WROWS + j * 16 + (lane & 15));      \
+      }                                                                                          \
+    }                                                                                            \
+  }
 #define STEP(CUR, NXT, KT)                                                                       \
   {                                                                                              \
     const int _later = min(LEAD - 2, nk - 2 - (KT));                                             \
@@ -375,15 +445,27 @@ __global__ __launch_bounds__(TL::THREADS) void gemm_kernel(GemmArgs g) {
     __builtin_amdgcn_s_barrier();                                                                \
     asm volatile("" ::: "memory");                                                               \
     if ((KT) + LEAD < nk) ISSUE_STAGE((KT) + LEAD);                                              \
-    MFMAS(CUR, NXT, (KT) + 1, true);                                                             \
-    _Pragma("unroll") for (int _k = 0; _k < KS; ++_k) {                                          \
+    if constexpr (F8) {                                                                          \
+      MFMAS8(CUR, NXT, (KT) + 1, true);                                                          \
       _Pragma("unroll") for (int _j = 0; _j < FM; ++_j) {                                        \
         __builtin_amdgcn_sched_group_barrier(0x008, FM, 0);                                      \
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                                       \
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);                                       \
       }                                                                                          \
       _Pragma("unroll") for (int _j = FM; _j < FN; ++_j) {                                       \
         __builtin_amdgcn_sched_group_barrier(0x008, FM, 0);                                      \
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                       \
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                                       \
+      }                                                                                          \
+    } else {                                                                                     \
+      MFMAS(CUR, NXT, (KT) + 1, true);                                                           \
+      _Pragma("unroll") for (int _k = 0; _k < KS; ++_k) {                                        \
+        _Pragma("unroll") for (int _j = 0; _j < FM; ++_j) {                                      \
+          __builtin_amdgcn_sched_group_barrier(0x008, FM, 0);                                    \
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                                     \
+        }                                                                                        \
+        _Pragma("unroll") for (int _j = FM; _j < FN; ++_j) {                                     \
+          __builtin_amdgcn_sched_group_barrier(0x008, FM, 0);                                    \
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                     \
+        }                                                                                        \
       }                                                                                          \
     }                                                                                            \
   }
@@ -399,7 +481,11 @@ __global__ __launch_bounds__(TL::THREADS) void gemm_kernel(GemmArgs g) {
     else WAIT_VMCNT(0);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    LOAD_FRAGS(0, 0);
+    if constexpr (F8) {
+      LOAD_FRAGS8(0, 0);
+    } else {
+      LOAD_FRAGS(0, 0);
+    }
   }
   int kt = 0;
   for (; kt + 2 < nk; kt += 2) {
@@ -409,13 +495,24 @@ __global__ __launch_bounds__(TL::THREADS) void gemm_kernel(GemmArgs g) {
   if (kt + 1 < nk) {
     STEP(0, 1, kt);
     WAIT_LGKM0();
-    MFMAS(1, 0, 0, false);
+    if constexpr (F8) {
+      MFMAS8(1, 0, 0, false);
+    } else {
+      MFMAS(1, 0, 0, false);
+    }
   } else {
     WAIT_LGKM0();
-    MFMAS(0, 1, 0, false);
+    if constexpr (F8) {
+      MFMAS8(0, 1, 0, false);
+    } else {
+      MFMAS(0, 1, 0, false);
+    }
   }
 #undef STEP
 #undef MFMAS
+#undef MFMAS8
+#undef LOAD_FRAGS8
+#undef FRAG8
 #undef LOAD_FRAGS
 #undef FRAG_A
 #undef FRAG_B
@@ -563,7 +660,8 @@ constexpr int kReduceMaxChunks = 16;
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int splits,
                                                             const float* __restrict__ res, float* __restrict__ out,
                                                             int M, int N, const uint16_t* __restrict__ gain,
-                                                            uint16_t* __restrict__ norm_out, float eps) {
+                                                            void* __restrict__ norm_out, float eps,
+                                                            float norm_inv_scale) {
   __shared__ float red[4];
   const int m = blockIdx.x;
   const int n4 = N >> 2;
@@ -596,10 +694,16 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     const int i = threadIdx.x + 256 * k;
     if (i < n4) {
       const uint2 gg = reinterpret_cast<const uint2*>(gain)[i];
-      uint2 o;
-      o.x = pack2bf(v[k].x * rs * bf2f((uint16_t)(gg.x & 0xffff)), v[k].y * rs * bf2f((uint16_t)(gg.x >> 16)));
-      o.y = pack2bf(v[k].z * rs * bf2f((uint16_t)(gg.y & 0xffff)), v[k].w * rs * bf2f((uint16_t)(gg.y >> 16)));
-      reinterpret_cast<uint2*>(norm_out + (size_t)m * N)[i] = o;
+      const float y0 = v[k].x * rs * bf2f((uint16_t)(gg.x & 0xffff)), y1 = v[k].y * rs * bf2f((uint16_t)(gg.x >> 16));
+      const float y2 = v[k].z * rs * bf2f((uint16_t)(gg.y & 0xffff)), y3 = v[k].w * rs * bf2f((uint16_t)(gg.y >> 16));
+      if (norm_inv_scale > 0.0f) {   // FP8 codes of the normed row / scale
+        const float q = norm_inv_scale;
+        reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(norm_out) + (size_t)m * N)[i] =
+            pack4fp8(y0 * q, y1 * q, y2 * q, y3 * q);
+      } else {
+        reinterpret_cast<uint2*>(static_cast<uint16_t*>(norm_out) + (size_t)m * N)[i] =
+            make_uint2(pack2bf(y0, y1), pack2bf(y2, y3));
+      }
     }
   }
 }
@@ -661,13 +765,17 @@ static void plan_try(GemmPlan& best, double& best_cost, int tile, int mode, int 
 // Efficiencies: fraction of the MFMA peak per busy CU with every CU busy (fit;
 // 256x224 raised from 0.455 to 0.485 to match the layer, where it beats
 // 256x256 by 3-6 % on gate/up, O and down whenever both apply).
-GemmPlan gemm_plan(int mode, int M, int N, int K) {
+// FP8 (f8): K counts codes; the plan is made for K / 2 units (same bytes and
+// the same MFMA cycles per stage as bf16), on the ring-pipeline tiles.
+GemmPlan gemm_plan(int mode, int M, int N, int K, bool f8) {
   GemmPlan p{kTile128W8, 1};
   double cost = 1e30;
+  if (f8) K /= 2;
   plan_try<Tile128W8>(p, cost, kTile128W8, mode, M, N, K, 0.344);
   plan_try<Tile128N96>(p, cost, kTile128N96, mode, M, N, K, 0.291);
   if (M < 256) return p;
   plan_try<Tile256>(p, cost, kTile256, mode, M, N, K, 0.426);
+  if (f8) return p;
   plan_try<TileW256>(p, cost, kTileW256, mode, M, N, K, 0.515);
   plan_try<TileW224>(p, cost, kTileW224, mode, M, N, K, 0.485);
   return p;
@@ -683,28 +791,39 @@ static void launch_sub(const GemmArgs& g, int splits, hipStream_t s) {
   }
 }
 
-template <class TL>
+template <class TL, bool F8>
 static void launch_tile(const GemmArgs& g, int splits, hipStream_t s) {
   const dim3 grid((unsigned)(((g.M + TL::BM - 1) / TL::BM) * (g.N / TL::BN)), 1, splits);
   switch (g.mode) {
-    case kGemmQkvRope: hipLaunchKernelGGL((gemm_kernel<kGemmQkvRope, TL>), grid, dim3(TL::THREADS), 0, s, g); break;
-    case kGemmResidual: hipLaunchKernelGGL((gemm_kernel<kGemmResidual, TL>), grid, dim3(TL::THREADS), 0, s, g); break;
-    default: hipLaunchKernelGGL((gemm_kernel<kGemmSwiglu, TL>), grid, dim3(TL::THREADS), 0, s, g); break;
+    case kGemmQkvRope: hipLaunchKernelGGL((gemm_kernel<kGemmQkvRope, TL, F8>), grid, dim3(TL::THREADS), 0, s, g); break;
+    case kGemmResidual: hipLaunchKernelGGL((gemm_kernel<kGemmResidual, TL, F8>), grid, dim3(TL::THREADS), 0, s, g); break;
+    default: hipLaunchKernelGGL((gemm_kernel<kGemmSwiglu, TL, F8>), grid, dim3(TL::THREADS), 0, s, g); break;
   }
 }
 
-hb_status launch_gemm(const GemmArgs& g, stream_t s) {
-  if (g.M <= 0) return HB_OK;
-  if (g.N % 128 || g.K % 64) return fail(HB_E_SHAPE, "gemm N/K not multiples of 128/64");
-  if (g.mode < kGemmQkvRope || g.mode > kGemmSwiglu) return fail(HB_E_SHAPE, "bad gemm mode");
-  const GemmPlan p = gemm_plan(g.mode, g.M, g.N, g.K);
+hb_status launch_gemm(const GemmArgs& ga, stream_t s) {
+  if (ga.M <= 0) return HB_OK;
+  if (ga.N % 128 || ga.K % (ga.f8 ? 128 : 64)) return fail(HB_E_SHAPE, "gemm N/K not multiples of 128/64 (FP8: 128/128)");
+  if (ga.mode < kGemmQkvRope || ga.mode > kGemmSwiglu) return fail(HB_E_SHAPE, "bad gemm mode");
+  if (ga.f8 && (!ga.ws0 || (ga.mode != kGemmResidual && !ga.ws1) || (ga.mode == kGemmQkvRope && !ga.ws2)))
+    return fail(HB_E_NULL, "FP8 gemm needs the weight row scales");
+  const GemmPlan p = gemm_plan(ga.mode, ga.M, ga.N, ga.K, ga.f8 != 0);
+  GemmArgs g = ga;
+  if (g.f8) {   // count K and lda in 16-bit units (two codes)
+    g.K /= 2;
+    g.lda /= 2;
+  }
   if (p.splits > 1 && !g.part) return fail(HB_E_NULL, "gemm split-K needs a partial buffer");
-  if (p.tile == kTileW224) launch_sub<TileW224>(g, p.splits, (hipStream_t)s);
+  if (g.f8) {
+    if (p.tile == kTile256) launch_tile<Tile256, true>(g, p.splits, (hipStream_t)s);
+    else if (p.tile == kTile128N96) launch_tile<Tile128N96, true>(g, p.splits, (hipStream_t)s);
+    else launch_tile<Tile128W8, true>(g, p.splits, (hipStream_t)s);
+  } else if (p.tile == kTileW224) launch_sub<TileW224>(g, p.splits, (hipStream_t)s);
   else if (p.tile == kTileW256) launch_sub<TileW256>(g, p.splits, (hipStream_t)s);
-  else if (p.tile == kTile256) launch_tile<Tile256>(g, p.splits, (hipStream_t)s);
-  else if (p.tile == kTile128W8) launch_tile<Tile128W8>(g, p.splits, (hipStream_t)s);
-  else if (p.tile == kTile128N96) launch_tile<Tile128N96>(g, p.splits, (hipStream_t)s);
-  else launch_tile<Tile128W8>(g, p.splits, (hipStream_t)s);
+  else if (p.tile == kTile256) launch_tile<Tile256, false>(g, p.splits, (hipStream_t)s);
+  else if (p.tile == kTile128W8) launch_tile<Tile128W8, false>(g, p.splits, (hipStream_t)s);
+  else if (p.tile == kTile128N96) launch_tile<Tile128N96, false>(g, p.splits, (hipStream_t)s);
+  else launch_tile<Tile128W8, false>(g, p.splits, (hipStream_t)s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(HB_E_HIP, std::string("gemm launch: ") + hipGetErrorString(e));
   if (p.splits > 1 && g.mode == kGemmQkvRope) {
@@ -718,11 +837,11 @@ hb_status launch_gemm(const GemmArgs& g, stream_t s) {
 }
 
 hb_status launch_splitk_reduce(const float* part, int splits, const float* res, float* out, int M, int N,
-                               const uint16_t* gain, uint16_t* norm_out, float eps, stream_t s) {
+                               const uint16_t* gain, void* norm_out, float eps, stream_t s, float norm_inv_scale) {
   if (M <= 0) return HB_OK;
   if (N > 256 * 4 * kReduceMaxChunks) return fail(HB_E_SHAPE, "split-K reduce: row above 16384");
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3(M), dim3(256), 0, (hipStream_t)s, part, splits, res, out, M, N, gain,
-                     norm_out, eps);
+                     norm_out, eps, norm_inv_scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(HB_E_HIP, std::string("split-K reduce launch: ") + hipGetErrorString(e));
   return HB_OK;

@@ -71,8 +71,9 @@ DevMeta dev_meta(const hb_meta_header* h, const void* meta_dev);
 
 typedef struct ihipStream_t* stream_t;
 
-hb_status launch_rmsnorm(const float* x, const uint16_t* gain, uint16_t* out, int rows, int hidden,
-                         float eps, stream_t s);
+// out: bf16, or with out_inv_scale > 0 FP8 e4m3 codes of value * out_inv_scale
+hb_status launch_rmsnorm(const float* x, const uint16_t* gain, void* out, int rows, int hidden,
+                         float eps, stream_t s, float out_inv_scale = 0.0f);
 hb_status launch_kv_append(const hb_dims& d, const DevMeta& m, int n_tokens, const uint16_t* k,
                            const uint16_t* v, int64_t row_stride, void* kc, void* vc, stream_t s);
 
@@ -80,6 +81,15 @@ enum GemmMode { kGemmQkvRope = 0, kGemmResidual = 1, kGemmSwiglu = 2 };
 
 struct GemmArgs {
   int mode;
+  // f8: A and the weights are FP8 e4m3 codes.  Then K and lda count 16-bit
+  // units (two codes each), so that every address computation is the bf16
+  // one over the same bytes; acc is scaled by a_scale * (row scale of the
+  // weight row) and a SwiGLU output is written as codes of out * out_inv_scale.
+  int f8;
+  const float* ws0;
+  const float* ws1;
+  const float* ws2;
+  float a_scale, out_inv_scale;
   const uint16_t* a;  // [M][K] bf16
   int lda;
   int M, N, K;
@@ -113,10 +123,12 @@ struct GemmArgs {
 struct GemmPlan {
   int tile, splits;
 };
-GemmPlan gemm_plan(int mode, int M, int N, int K);
+GemmPlan gemm_plan(int mode, int M, int N, int K, bool f8 = false);
 hb_status launch_gemm(const GemmArgs& g, stream_t s);
+// norm_out: bf16, or with norm_inv_scale > 0 FP8 e4m3 codes of value * norm_inv_scale
 hb_status launch_splitk_reduce(const float* part, int splits, const float* res, float* out, int M, int N,
-                               const uint16_t* gain, uint16_t* norm_out, float eps, stream_t s);
+                               const uint16_t* gain, void* norm_out, float eps, stream_t s,
+                               float norm_inv_scale = 0.0f);
 
 struct AttnArgs {
   const uint16_t* q;       // [T][n_q * d]
@@ -130,7 +142,8 @@ struct AttnArgs {
   int n_chunk_items, n_decode_items, n_tokens;
   float* part_o;           // [n_partials][n_q][d]
   float* part_ml;          // [n_partials][n_q][2]
-  uint16_t* out;           // [T][n_q * d]
+  void* out;               // [T][n_q * d] bf16, or FP8 codes of o * out_inv_scale (> 0)
+  float out_inv_scale;
 };
 // Attention in three launches (chunk items, decode items, merge); ev, if not
 // NULL, holds the events to record before each launch (3 entries).

@@ -68,6 +68,9 @@ extern "C" hb_status hb_layer_forward(const hb_dims* dims, const hb_weights* w, 
     return fail(HB_E_NULL, "layer_forward: NULL pointer");
   if (!w->w_q || !w->w_k || !w->w_v || !w->w_o || !w->w_g || !w->w_u || !w->w_d || !w->g_attn || !w->g_ffn)
     return fail(HB_E_NULL, "layer_forward: NULL weight");
+  const bool f8 = dims->w8a8 != 0;
+  if (f8 && (!w->s_q || !w->s_k || !w->s_v || !w->s_o || !w->s_g || !w->s_u || !w->s_d))
+    return fail(HB_E_NULL, "layer_forward: FP8 projections need every weight row scale");
   if ((const void*)x == (const void*)y) return fail(HB_E_SHAPE, "layer_forward: x and y alias");
   const hb_meta_header* h = (const hb_meta_header*)meta_host;
   if (h->max_kv_len > rope_max_pos)
@@ -101,7 +104,7 @@ extern "C" hb_status hb_layer_forward(const hb_dims* dims, const hb_weights* w, 
 
   // a1: RMSNorm of the input
   mark(0);
-  HB_TRY(launch_rmsnorm(x, w->g_attn, xn, T, H, dims->rms_eps, s));
+  HB_TRY(launch_rmsnorm(x, w->g_attn, xn, T, H, dims->rms_eps, s, f8 ? 1.0f / dims->x_scale : 0.0f));
 
   // a2-a4: QKV projection, RoPE, KV append
   GemmArgs g{};
@@ -111,9 +114,14 @@ extern "C" hb_status hb_layer_forward(const hb_dims* dims, const hb_weights* w, 
   g.M = T;
   g.N = (nq + 2 * nkv) * d;
   g.K = H;
-  g.w0 = w->w_q;
-  g.w1 = w->w_k;
-  g.w2 = w->w_v;
+  g.w0 = static_cast<const uint16_t*>(w->w_q);
+  g.w1 = static_cast<const uint16_t*>(w->w_k);
+  g.w2 = static_cast<const uint16_t*>(w->w_v);
+  g.f8 = f8;
+  g.ws0 = w->s_q;
+  g.ws1 = w->s_k;
+  g.ws2 = w->s_v;
+  g.a_scale = dims->x_scale;
   g.n0 = nq * d;
   g.n1 = nkv * d;
   g.out_b = qb;
@@ -152,13 +160,14 @@ extern "C" hb_status hb_layer_forward(const hb_dims* dims, const hb_weights* w, 
   at.part_o = (float*)(ws + L.part_o);
   at.part_ml = (float*)(ws + L.part_ml);
   at.out = ob;
+  at.out_inv_scale = f8 ? 1.0f / dims->o_scale : 0.0f;
   HB_TRY(launch_attention(at, s, stage_events ? stage_events + 2 : nullptr));
 
   // a6: O projection + residual, a7: RMSNorm (split-K: the reduce adds the
   // residual and normalises in one pass)
   float* gpart = (float*)(ws + L.gemm_part);
-  const GemmPlan po = gemm_plan(kGemmResidual, T, H, nq * d);
-  const GemmPlan pd = gemm_plan(kGemmResidual, T, H, F);
+  const GemmPlan po = gemm_plan(kGemmResidual, T, H, nq * d, f8);
+  const GemmPlan pd = gemm_plan(kGemmResidual, T, H, F, f8);
   GemmArgs go{};
   go.mode = kGemmResidual;
   go.a = ob;
@@ -166,7 +175,10 @@ extern "C" hb_status hb_layer_forward(const hb_dims* dims, const hb_weights* w, 
   go.M = T;
   go.N = H;
   go.K = nq * d;
-  go.w0 = w->w_o;
+  go.w0 = static_cast<const uint16_t*>(w->w_o);
+  go.f8 = f8;
+  go.ws0 = w->s_o;
+  go.a_scale = dims->o_scale;
   go.res = x;
   go.out_f = h1;
   go.ldo = H;
@@ -174,10 +186,11 @@ extern "C" hb_status hb_layer_forward(const hb_dims* dims, const hb_weights* w, 
   mark(5);
   HB_TRY(launch_gemm(go, s));
   mark(6);
+  const float h_inv = f8 ? 1.0f / dims->h_scale : 0.0f;
   if (po.splits > 1) {
-    HB_TRY(launch_splitk_reduce(gpart, po.splits, x, h1, T, H, w->g_ffn, h1n, dims->rms_eps, s));
+    HB_TRY(launch_splitk_reduce(gpart, po.splits, x, h1, T, H, w->g_ffn, h1n, dims->rms_eps, s, h_inv));
   } else {
-    HB_TRY(launch_rmsnorm(h1, w->g_ffn, h1n, T, H, dims->rms_eps, s));
+    HB_TRY(launch_rmsnorm(h1, w->g_ffn, h1n, T, H, dims->rms_eps, s, h_inv));
   }
 
   // a8: gate/up projection + SwiGLU
@@ -188,8 +201,13 @@ extern "C" hb_status hb_layer_forward(const hb_dims* dims, const hb_weights* w, 
   gu.M = T;
   gu.N = 2 * F;
   gu.K = H;
-  gu.w0 = w->w_g;
-  gu.w1 = w->w_u;
+  gu.w0 = static_cast<const uint16_t*>(w->w_g);
+  gu.w1 = static_cast<const uint16_t*>(w->w_u);
+  gu.f8 = f8;
+  gu.ws0 = w->s_g;
+  gu.ws1 = w->s_u;
+  gu.a_scale = dims->h_scale;
+  gu.out_inv_scale = f8 ? 1.0f / dims->a_scale : 0.0f;
   gu.out_b = act;
   gu.ldo = F;
   mark(7);
@@ -203,7 +221,10 @@ extern "C" hb_status hb_layer_forward(const hb_dims* dims, const hb_weights* w, 
   gd.M = T;
   gd.N = H;
   gd.K = F;
-  gd.w0 = w->w_d;
+  gd.w0 = static_cast<const uint16_t*>(w->w_d);
+  gd.f8 = f8;
+  gd.ws0 = w->s_d;
+  gd.a_scale = dims->a_scale;
   gd.res = h1;
   gd.out_f = y;
   gd.ldo = H;

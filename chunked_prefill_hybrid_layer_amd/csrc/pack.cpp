@@ -45,6 +45,12 @@ hb_status check_dims(const hb_dims* d) {
   if (d->kv_fp8 && !(std::isfinite(d->k_scale) && d->k_scale > 0.0f && std::isfinite(d->v_scale) &&
                      d->v_scale > 0.0f))
     return fail(HB_E_SHAPE, "FP8 KV cache needs finite positive k_scale and v_scale");
+  if (d->w8a8 != 0 && d->w8a8 != 1) return fail(HB_E_SHAPE, "w8a8 must be 0 or 1");
+  if (d->w8a8) {
+    for (float sc : {d->x_scale, d->o_scale, d->h_scale, d->a_scale})
+      if (!(std::isfinite(sc) && sc > 0.0f))
+        return fail(HB_E_SHAPE, "FP8 projections need finite positive x/o/h/a scales");
+  }
   return HB_OK;
 }
 

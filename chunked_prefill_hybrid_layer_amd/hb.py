@@ -40,12 +40,15 @@ class Dims(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("ffn_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float), ("kv_fp8", ctypes.c_int32),
-                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
+                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float), ("w8a8", ctypes.c_int32),
+                ("x_scale", ctypes.c_float), ("o_scale", ctypes.c_float), ("h_scale", ctypes.c_float),
+                ("a_scale", ctypes.c_float)]
 
 
 class Weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
-                ("w_q", "w_k", "w_v", "w_o", "w_g", "w_u", "w_d", "g_attn", "g_ffn")]
+                ("w_q", "w_k", "w_v", "w_o", "w_g", "w_u", "w_d", "g_attn", "g_ffn",
+                 "s_q", "s_k", "s_v", "s_o", "s_g", "s_u", "s_d")]
 
 
 class AttnItem(ctypes.Structure):
@@ -118,7 +121,9 @@ def make_dims(d) -> Dims:
     """hb_dims from any object with the layer-shape attributes."""
     return Dims(d.hidden, d.n_q_heads, d.n_kv_heads, d.head_dim, d.ffn_dim, d.page_size,
                 float(d.rms_eps), float(d.rope_theta), int(getattr(d, "kv_fp8", 0)),
-                float(getattr(d, "k_scale", 1.0)), float(getattr(d, "v_scale", 1.0)))
+                float(getattr(d, "k_scale", 1.0)), float(getattr(d, "v_scale", 1.0)),
+                int(getattr(d, "w8a8", 0)), *[float(getattr(d, n, 1.0)) for n in
+                                              ("x_scale", "o_scale", "h_scale", "a_scale")])
 
 
 def _i32(a) -> np.ndarray:

@@ -17,6 +17,7 @@ from . import hb
 BF16_NAN = 0x7FC0
 E4M3_NAN = 0x7F
 WEIGHT_NAMES = ("w_q", "w_k", "w_v", "w_o", "w_g", "w_u", "w_d", "g_attn", "g_ffn")
+SCALE_NAMES = ("w_q", "w_k", "w_v", "w_o", "w_g", "w_u", "w_d")   # row scales of FP8 projections
 
 
 def to_device_u16(a: np.ndarray, device) -> torch.Tensor:
@@ -60,8 +61,20 @@ class DeviceLayer:
         self.dims = dims
         self.hd = hb.make_dims(dims)
         self.device = device
-        self.w = {n: to_device_u16(weights[n], device) for n in WEIGHT_NAMES}
-        self.hw = hb.Weights(*[self.w[n].data_ptr() for n in WEIGHT_NAMES])
+        # bf16 bit patterns; with dims.w8a8 the projections are e4m3 codes
+        # (uint8) with float32 row scales under "s_" + name
+        self.w = {}
+        for n in WEIGHT_NAMES:
+            a = weights[n]
+            self.w[n] = (torch.from_numpy(np.ascontiguousarray(a)).to(device) if a.dtype == np.uint8
+                         else to_device_u16(a, device))
+        scales = [0] * len(SCALE_NAMES)
+        if getattr(dims, "w8a8", 0):
+            for i, n in enumerate(SCALE_NAMES):
+                t = torch.from_numpy(np.ascontiguousarray(weights["s_" + n], dtype=np.float32)).to(device)
+                self.w["s_" + n] = t
+                scales[i] = t.data_ptr()
+        self.hw = hb.Weights(*[self.w[n].data_ptr() for n in WEIGHT_NAMES], *scales)
         self.num_pages = int(num_pages)
         # K page blocks are [head_dim/32][page_size][32]; V page blocks [head_dim][page_size]
         self.kv_fp8 = bool(getattr(dims, "kv_fp8", 0))

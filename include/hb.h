@@ -94,15 +94,31 @@ typedef struct {
   int32_t kv_fp8;
   float k_scale;
   float v_scale;
+  /* Projection precision.  0: bf16 weights and inputs.  1: FP8 e4m3 on the
+   * gfx950 FP8 matrix cores: the projection weights are e4m3 codes with one
+   * float scale per output channel (hb_weights s_*), and the four projection
+   * inputs -- the normed input (into QKV), the attention output (into O), the
+   * normed residual (into gate/up) and the SwiGLU output (into down) -- are
+   * stored as e4m3 codes of value / scale with the static per-layer scales
+   * below (quotient in single precision as for the FP8 cache, nearest even,
+   * saturating).  A projection is (a codes * scale) . (w codes * row scale)^T
+   * with fp32 accumulation.  q, the KV cache and the fp32 residual stream are
+   * unaffected.  Scales must be finite and > 0 (HB_E_SHAPE otherwise). */
+  int32_t w8a8;
+  float x_scale, o_scale, h_scale, a_scale;
 } hb_dims;
 
-/* Device pointers to the layer's parameters (bf16 bits).  Projection
- * matrices are row-major [d_out][d_in]:
+/* Device pointers to the layer's parameters.  Projection matrices are
+ * row-major [d_out][d_in], bf16 bits (or e4m3 codes with dims->w8a8):
  *   w_q [n_q*d][hidden], w_k and w_v [n_kv*d][hidden], w_o [hidden][n_q*d],
- *   w_g and w_u [ffn][hidden], w_d [hidden][ffn];  g_attn, g_ffn [hidden]. */
+ *   w_g and w_u [ffn][hidden], w_d [hidden][ffn];  g_attn, g_ffn [hidden]
+ * (bf16 bits).  With dims->w8a8, s_q .. s_d hold one float scale per output
+ * channel (d_out entries each; row n of a matrix is codes[n] * s[n]); they
+ * are not read otherwise. */
 typedef struct {
-  const uint16_t *w_q, *w_k, *w_v, *w_o, *w_g, *w_u, *w_d;
+  const void *w_q, *w_k, *w_v, *w_o, *w_g, *w_u, *w_d;
   const uint16_t *g_attn, *g_ffn;
+  const float *s_q, *s_k, *s_v, *s_o, *s_g, *s_u, *s_d;
 } hb_weights;
 
 /* ---------------------------------------------------------------------------

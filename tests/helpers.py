@@ -49,27 +49,47 @@ def errors(got, ref):
     return rel, mx
 
 
-def assert_close(got, ref, what="", max_abs=TOL_MAX_ABS):
+def assert_close(got, ref, what="", max_abs=TOL_MAX_ABS, rel_l2=TOL_REL_L2):
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     rel, mx = errors(got, ref)
     log(f"{what}: rel_l2={rel:.3e} max_abs={mx:.3e} (|ref|max={np.max(np.abs(ref)):.3f}, "
-        f"max_abs bound {max_abs:.3e})")
-    assert rel <= TOL_REL_L2 and mx <= max_abs, (what, rel, mx)
+        f"bounds {rel_l2:.3e} / {max_abs:.3e})")
+    assert rel <= rel_l2 and mx <= max_abs, (what, rel, mx)
     return rel, mx
 
 
-def conditioning_floor(wl, rows, cache_seqs, seed=0):
+def conditioning_floor(wl, rows, cache_seqs, seed=0, eps=1e-7):
     """Max-abs change of the oracle's own output (bf16 storage) when its input
-    x is multiplied by 1 + 1e-7 N(0, 1): the size of the rounding cascade any
-    implementation whose arithmetic differs from float64 by an fp32 ulp must
-    show on these rows (each bf16 storage point turns a perturbation eps into
-    one-step flips with probability eps/ulp)."""
+    x is multiplied by 1 + eps N(0, 1), eps = 1e-7 by default: the size of the
+    rounding cascade any implementation whose arithmetic differs from float64
+    by an fp32 ulp must show on these rows (each storage point turns a
+    perturbation eps into one-step flips with probability eps/ulp)."""
     rng = np.random.default_rng(seed)
     x = wl.x.astype(np.float64)
-    xp = x * (1.0 + 1e-7 * rng.standard_normal(x.shape))
+    xp = x * (1.0 + eps * rng.standard_normal(x.shape))
     y0, _ = oracle_forward(wl, x=x, rows=rows, cache=oracle_cache(wl, seqs=cache_seqs))
     y1, _ = oracle_forward(wl, x=xp, rows=rows, cache=oracle_cache(wl, seqs=cache_seqs))
     return errors(y1.y, y0.y)
+
+
+# relative error of one FP8 MFMA's sum, as a fraction of the sum of |products|
+# (measured worst: about 1800 fp32 ulps, 2^-13)
+FP8_MFMA_REL_ERR = 2.0 ** -13
+
+
+def w8a8_bound(wl, rows=None, cache_seqs=None):
+    """Max-abs bar for FP8 projections.  A relative error of the FP8 MFMA's
+    summation (FP8_MFMA_REL_ERR) moves a pre-quantisation value across an e4m3
+    rounding boundary now and then, and such a code is a full e4m3 step (6 to
+    12 %) away from the oracle's; the flips propagate through the layer.  The
+    bars are the literal ones, or twice the oracle's own response to a
+    relative perturbation of its input of that size where that is larger.
+    Returns keyword arguments for assert_close."""
+    frel, fmax = conditioning_floor(wl, rows, cache_seqs, eps=FP8_MFMA_REL_ERR)
+    bars = dict(rel_l2=max(TOL_REL_L2, 2.0 * frel), max_abs=max(TOL_MAX_ABS, 2.0 * fmax))
+    log(f"{wl.name}: oracle response to a {FP8_MFMA_REL_ERR:.1e} relative input perturbation: "
+        f"rel_l2={frel:.3e} max_abs={fmax:.3e}; bars {bars['rel_l2']:.3e} / {bars['max_abs']:.3e}")
+    return bars
 
 
 def sample_rows(wl, n_random=48, seed=0):
@@ -105,7 +125,14 @@ def expected_cache_bits(cache, num_pages):
     return bits(k), bits(v)
 
 
-def new_values_close(g_bits, e_vals, what):
+# FP8 projections: gfx950's e4m3 MFMA (16x16x128) sums its 128 products to
+# about 16 significant bits (measured: mean 200, worst 1800 fp32 ulps of the
+# sum of |products| per instruction, against a few ulps for fp32 summation of
+# exact products), so more new K/V values sit one bf16 step from the oracle's.
+MIN_IDENTICAL_W8A8 = 0.95
+
+
+def new_values_close(g_bits, e_vals, what, min_identical=0.99):
     """New K/V written by the layer: the GPU rounds an fp32 sum to bf16, the
     oracle a float64 one, so a value may land one bf16 step away, and a value
     near zero (cancellation in the dot product) may differ by the fp32
@@ -122,7 +149,7 @@ def new_values_close(g_bits, e_vals, what):
     frac = 1.0 - float(np.mean(same)) if same.size else 0.0
     log(f"{what}: {frac * 100:.3f}% of new values not bit-identical, max |diff| {err.max(initial=0):.2e}")
     assert np.all(err <= bound), f"{what}: {int(np.sum(err > bound))} values out of bound"
-    assert frac <= 0.01, (what, frac)
+    assert frac <= 1.0 - min_identical, (what, frac)
 
 
 def expected_cache_codes(cache):
@@ -136,7 +163,7 @@ def expected_cache_codes(cache):
     return k, v
 
 
-def new_codes_close(g_codes, e_codes, what):
+def new_codes_close(g_codes, e_codes, what, min_identical=0.99):
     """New FP8 K/V written by the layer: both sides encode x / scale with the
     same rounding, but the GPU's x is an fp32 sum and the oracle's a float64
     one, so a value at a rounding boundary may land one code step away.
@@ -154,10 +181,10 @@ def new_codes_close(g_codes, e_codes, what):
     frac = 1.0 - float(np.mean(same)) if same.size else 0.0
     log(f"{what}: {frac * 100:.3f}% of new codes not identical, max |diff| {err.max(initial=0):.2e}")
     assert np.all(err <= bound), f"{what}: {int(np.sum(err > bound))} codes out of bound"
-    assert frac <= 0.01, (what, frac)
+    assert frac <= 1.0 - min_identical, (what, frac)
 
 
-def compare_cache(gpu_kv, cache, num_pages, written_pages_slots=None, what="cache"):
+def compare_cache(gpu_kv, cache, num_pages, written_pages_slots=None, what="cache", min_identical=0.99):
     """Bit-exact everywhere the batch did not write (prefixes, NaN decoys and
     tails).  At the batch's new slots: bit-exact if ``written_pages_slots`` is
     None (a pure copy), else ``new_values_close`` (bf16) or ``new_codes_close``
@@ -181,4 +208,4 @@ def compare_cache(gpu_kv, cache, num_pages, written_pages_slots=None, what="cach
         for page, slot in written_pages_slots:
             mask[page, :, slot, :] = True
         assert not (diff & ~mask).any(), f"{what} {name}: bytes outside the new slots changed"
-        close(g[mask], dense[mask], f"{what} {name}")
+        close(g[mask], dense[mask], f"{what} {name}", min_identical)

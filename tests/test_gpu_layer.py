@@ -6,8 +6,9 @@ import pytest
 
 from oracle import hybrid_layer as O
 from chunked_prefill_hybrid_layer_amd import workloads as W
-from tests.helpers import (TOL_MAX_ABS, assert_close, compare_cache, conditioning_floor, errors, log,
-                           new_codes_close, new_values_close, oracle_cache, oracle_forward, sample_rows)
+from tests.helpers import (MIN_IDENTICAL_W8A8, TOL_MAX_ABS, assert_close, compare_cache, conditioning_floor, errors,
+                           log, new_codes_close, new_values_close, oracle_cache, oracle_forward, sample_rows,
+                           w8a8_bound)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -226,7 +227,11 @@ def _full_size(wl, n_random, calibrate=False):
     log(f"{wl.name}: oracle on {len(rows)} rows of {len(seqs)} sequences")
     r, cache = oracle_forward(wl, rows=rows, cache=cache)
     bound = TOL_MAX_ABS
-    if calibrate:
+    bars = None
+    if wl.dims.w8a8:
+        crows = rows[:96]
+        bars = w8a8_bound(wl, crows, sorted(set(int(s) for s in lay.seq[crows])))
+    elif calibrate:
         # output scale where the layer's own rounding cascade exceeds the
         # literal max-abs bar: allow twice the oracle's own response to a
         # 1e-7 relative input perturbation (rel-L2 keeps the literal bar)
@@ -235,7 +240,9 @@ def _full_size(wl, n_random, calibrate=False):
         log(f"{wl.name}: oracle conditioning floor on {len(crows)} rows: rel_l2={floor_rel:.3e} "
             f"max_abs={floor_max:.3e}")
         bound = max(TOL_MAX_ABS, 2.0 * floor_max)
-    assert_close(y[rows], r.y, f"{wl.name} sampled y", max_abs=bound)
+    if bars is None:
+        bars = dict(max_abs=bound)
+    assert_close(y[rows], r.y, f"{wl.name} sampled y", **bars)
     # every new K/V row: the GPU cache at the new slots against the oracle's
     slots = _new_slots(b)
     gk, gv = layer.gather_kv([p for p, _ in slots], [s for _, s in slots])   # [T][kv][d] each
@@ -247,8 +254,9 @@ def _full_size(wl, n_random, calibrate=False):
         ek = np.stack([cache.pages[p][0, :, sl, :] for p, sl in slots])
         ev = np.stack([cache.pages[p][1, :, sl, :] for p, sl in slots])
         close = new_values_close
+    ident = MIN_IDENTICAL_W8A8 if wl.dims.w8a8 else 0.99
     for name, g, e in (("K", gk, ek), ("V", gv, ev)):
-        close(g, e, f"{wl.name} new {name}")
+        close(g, e, f"{wl.name} new {name}", ident)
 
 
 def test_full_size_mistral_tau512():
@@ -379,3 +387,63 @@ def test_layer_edge_cases_kv_fp8(case):
 
 def test_full_size_mistral_tau512_kv_fp8():
     _full_size(W.with_kv_fp8(W.mistral_tau512(0)), 48)
+
+
+# ---------------------------------------------------------------- FP8 projections (w8a8)
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_layer_parity_small_w8a8(name):
+    """FP8 weights and projection inputs on the FP8 MFMA: y within the
+    floating-point bar of the oracle, which stores the same four inputs as
+    e4m3 codes and uses the same decoded weights; the bf16 cache's new K/V
+    within one bf16 step."""
+    log(f"layer parity small w8a8 {name}")
+    wl = W.with_w8a8(W.small(2, **SMALL[name]))
+    b = wl.batch
+    layer = _layer_for(wl)
+    layer.fill_prefixes(b.block_table, range(b.n_seq), wl.prefix_k, wl.prefix_v)
+    y, _ = _run(layer, wl)
+    r, cache = oracle_forward(wl)
+    assert_close(y, r.y, f"small {name} w8a8 y", **w8a8_bound(wl))
+    compare_cache(layer.cache_logical(), cache, b.num_pages, _new_slots(b), f"small {name} w8a8", MIN_IDENTICAL_W8A8)
+
+
+@pytest.mark.parametrize("case", ["decodes_only", "one_token_chunk", "page_edge_chunks"])
+def test_layer_edge_cases_w8a8(case):
+    log(f"edge case w8a8 {case}")
+    kw = {
+        "decodes_only": dict(chunk_len=(), chunk_prefix=(), decode_ctx=(1, 16, 17, 255, 256, 257, 999)),
+        "one_token_chunk": dict(chunk_len=(1, 1), chunk_prefix=(0, 16), decode_ctx=(3,)),
+        "page_edge_chunks": dict(chunk_len=(16, 17, 15, 129), chunk_prefix=(16, 15, 1, 1023), decode_ctx=()),
+    }[case]
+    wl = W.with_w8a8(W.small(7, n_q=8, n_kv=2, head_dim=128, **kw))
+    b = wl.batch
+    layer = _layer_for(wl)
+    layer.fill_prefixes(b.block_table, range(b.n_seq), wl.prefix_k, wl.prefix_v)
+    y, _ = _run(layer, wl)
+    r, cache = oracle_forward(wl)
+    assert_close(y, r.y, f"{case} w8a8", **w8a8_bound(wl))
+    compare_cache(layer.cache_logical(), cache, b.num_pages, _new_slots(b), f"{case} w8a8", MIN_IDENTICAL_W8A8)
+
+
+def test_layer_parity_w8a8_with_fp8_cache():
+    log("layer parity w8a8 + FP8 KV cache")
+    wl = W.with_kv_fp8(W.with_w8a8(W.small(3, n_q=8, n_kv=2, head_dim=128)))
+    b = wl.batch
+    layer = _layer_for(wl)
+    layer.fill_prefixes(b.block_table, range(b.n_seq), wl.prefix_k, wl.prefix_v)
+    y, _ = _run(layer, wl)
+    r, cache = oracle_forward(wl)
+    assert_close(y, r.y, "w8a8 + kv fp8 y", **w8a8_bound(wl))
+    compare_cache(layer.cache_logical(), cache, b.num_pages, _new_slots(b), "w8a8 + kv fp8", MIN_IDENTICAL_W8A8)
+
+
+def test_full_size_mistral_tau512_w8a8():
+    _full_size(W.with_w8a8(W.mistral_tau512(0)), 48)
+
+
+def test_full_size_mistral_T2048_w8a8():
+    """Mistral at T = 2048: the FP8 plans on 256x128 tiles."""
+    rng = np.random.default_rng(11)
+    ctx = rng.integers(1, 1500, size=48).astype(np.int32)
+    _full_size(W.with_w8a8(W.build_workload("mistral_T2048", W.MISTRAL, [2000], [300], ctx, 3)), 16)
