@@ -221,6 +221,13 @@ def test_pack_rejects_invalid_batches():
                dict(kv_fp8=1, k_scale=float("nan")), dict(kv_fp8=1, v_scale=float("inf"))):
         bad = W.Dims(256, 4, 4, 64, 512, **kw)
         assert _err(lambda: _pack(bad, [4], [0], [], np.array([[0]]), 1)) == "HB_E_SHAPE", kw
+    # FP8 projection settings: w8a8 is 0 or 1, its four input scales finite and positive
+    _pack(W.Dims(256, 4, 4, 64, 512, w8a8=1, x_scale=0.5, o_scale=2.0, h_scale=0.1, a_scale=1.0), [4], [0], [],
+          np.array([[0]]), 1)
+    for kw in (dict(w8a8=3), dict(w8a8=1, x_scale=0.0), dict(w8a8=1, o_scale=-2.0), dict(w8a8=1, h_scale=float("nan")),
+               dict(w8a8=1, a_scale=float("inf"))):
+        bad = W.Dims(256, 4, 4, 64, 512, **kw)
+        assert _err(lambda: _pack(bad, [4], [0], [], np.array([[0]]), 1)) == "HB_E_SHAPE", kw
     # a too-small buffer is reported, and nothing is written
     dims = hb.make_dims(d)
     with pytest.raises(hb.HbError) as ei:
