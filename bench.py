@@ -381,11 +381,21 @@ def sweep_tau(args):
     from chunked_prefill_hybrid_layer_amd import workloads as W
     points = []
     gemm = ("qkv_rope_append", "o_proj_residual", "gate_up_swiglu", "down_residual")
+    suffix = ("_w8a8" if args.w8a8 else "") + ("_kvfp8" if args.kv_fp8 else "")
+
+    def variant(wl):
+        if args.w8a8:
+            wl = W.with_w8a8(wl)
+        if args.kv_fp8:
+            wl = W.with_kv_fp8(wl)
+        return wl
+    wbytes = 1 if args.w8a8 else 2
+    peak = PEAK_FP8_TFLOPS if args.w8a8 else PEAK_BF16_TFLOPS
     # a discarded first point: clocks settle during the first few hundred steps of a process
-    bench_batch(W.tau_sweep(TAU_SWEEP[0], 0), "warm-up", args.steps, args.warmup, 1)
+    bench_batch(variant(W.tau_sweep(TAU_SWEEP[0], 0)), "warm-up", args.steps, args.warmup, 1)
     for tau in TAU_SWEEP:
-        wl = W.tau_sweep(tau, 0)
-        out = bench_batch(wl, f"tau_sweep_{tau}", args.steps, args.warmup, args.copies)
+        wl = variant(W.tau_sweep(tau, 0))
+        out = bench_batch(wl, f"tau_sweep_{tau}{suffix}", args.steps, args.warmup, args.copies)
         out["metric"] = "hybrid-layer tokens/s, token-budget sweep (Mistral-7B-shaped layer)"
         if not args.no_cpu_baseline:
             out["cpu_baseline"] = cpu_baseline(wl, stride=max(4, tau // 64))
@@ -397,12 +407,13 @@ def sweep_tau(args):
         points.append({"tau": tau, "tokens_per_s": out["value"], "ms_per_step": out["ms_per_step"],
                        "gemm_ms": round(t_gemm * 1e3, 4),
                        "gemm_tflops": round(2 * tau * psi / t_gemm / 1e12, 1),
-                       "gemm_weight_gbs": round(2 * psi / t_gemm / 1e9, 1),
-                       "gemm_bound_ms": round(max(2 * psi / (PEAK_HBM_GBS * 1e9),
-                                                  2 * tau * psi / (PEAK_BF16_TFLOPS * 1e12)) * 1e3, 4)})
-    # algorithmic knee (bf16 weights): n* = bytes_w * FLOPS / (2 BW)
-    knee = 2 * PEAK_BF16_TFLOPS * 1e12 / (2 * PEAK_HBM_GBS * 1e9)
-    print(json.dumps({"metric": "tau sweep summary", "points": points,
+                       "gemm_weight_gbs": round(wbytes * psi / t_gemm / 1e9, 1),
+                       "gemm_bound_ms": round(max(wbytes * psi / (PEAK_HBM_GBS * 1e9),
+                                                  2 * tau * psi / (peak * 1e12)) * 1e3, 4)})
+    # algorithmic knee: n* = bytes_w * FLOPS / (2 BW) (bf16: 2 bytes at 2.5 PFLOP/s;
+    # FP8: 1 byte at 5.0 PFLOP/s -- the same n*)
+    knee = wbytes * peak * 1e12 / (2 * PEAK_HBM_GBS * 1e9)
+    print(json.dumps({"metric": "tau sweep summary" + (" (" + suffix[1:] + ")" if suffix else ""), "points": points,
                       "knee_tokens_algorithmic": round(knee, 1)}), flush=True)
 
 
