@@ -209,52 +209,76 @@ def bench_batch(wl, name, steps, warmup, copies, calibrate_copy=False):
     hd = hb.make_dims(d)
     x = torch.from_numpy(wl.x).cuda()
     y = torch.empty_like(x)
-    # metadata: pinned host blobs and device blobs, double-buffered
+    # metadata: a ring of pinned host blobs and device blobs
+    RING, REC = 8, 4
     blob0 = hb.pack_metadata(hd, b.chunk_len, b.chunk_prefix, b.decode_ctx, b.block_table, b.num_pages,
                              b.token_budget)[0]
     size = blob0.nbytes
-    pin = [torch.empty(size, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
+    pin = [torch.empty(size, dtype=torch.uint8, pin_memory=True) for _ in range(RING)]
     pin_np = [p.numpy() for p in pin]
-    dev = [torch.empty(size, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    dev = [torch.empty(size, dtype=torch.uint8, device="cuda") for _ in range(RING)]
     ws = torch.empty(hb.workspace_bytes(hd, blob0), dtype=torch.uint8, device="cuda")
     stream = stream_handle()
     # per-step host work is one C call each for packing and for the forward
     packers = [hb.Packer(hd, b.chunk_len, b.chunk_prefix, b.decode_ctx, b.block_table, b.num_pages,
-                         b.token_budget, pin_np[j]) for j in range(2)]
+                         b.token_budget, pin_np[j]) for j in range(RING)]
     fwds = [[hb.Forward(hd, L.hw, pin_np[j], dev[j].data_ptr(), L.rope.data_ptr(), L.rope_max_pos, x.data_ptr(),
                         y.data_ptr(), L.k_cache.data_ptr(), L.v_cache.data_ptr(), ws.data_ptr(), ws.numel(), stream)
-             for j in range(2)] for L in layers]
-    # The metadata upload of step i+1 runs on its own stream while step i
-    # computes; the compute stream waits only for that copy, and a device
-    # buffer is refilled only after the forward that read it has finished.
+             for j in range(RING)] for L in layers]
+    # Step s packs its metadata into pinned buffer s % RING and copies it to
+    # device buffer s % RING on its own stream, one step ahead.  The compute
+    # stream never waits on that stream: the host confirms the copy has
+    # completed before it enqueues the step's forward.  A device buffer is
+    # refilled only after the forward that read it RING steps earlier has
+    # finished: the compute stream records an event after every REC-th forward
+    # (each packet between two kernels leaves a bubble of about 6-8 us, so not
+    # after every one), and the copy waits for the first one at or after it.
     compute = torch.cuda.current_stream()
     upload = torch.cuda.Stream()
-    copied = [torch.cuda.Event(), torch.cuda.Event()]
-    consumed = [torch.cuda.Event(), torch.cuda.Event()]
-    for e in copied + consumed:
-        e.record(compute)
+    copied = [torch.cuda.Event() for _ in range(RING)]
+    for e in copied:
+        e.record(upload)
+    done = {}
 
-    def step(i, events=None):
-        j = i & 1
-        copied[j].synchronize()                # the copy that last read this pinned buffer is done
+    def upload_step(s):
+        j = s % RING
+        copied[j].synchronize()                # the copy that last read pinned buffer j is done
         packers[j]()
-        upload.wait_event(consumed[j])
+        if s >= RING:
+            upload.wait_event(done[(s - RING) // REC])
         with torch.cuda.stream(upload):
             dev[j].copy_(pin[j], non_blocking=True)
         copied[j].record(upload)
-        compute.wait_event(copied[j])
-        fwds[i % len(layers)][j](events)
-        consumed[j].record(compute)
+
+    def forward_step(s, events=None):
+        j = s % RING
+        copied[j].synchronize()                # this step's metadata is on the device
+        fwds[s % len(layers)][j](events)
+        if s % REC == REC - 1:
+            ev = torch.cuda.Event()
+            ev.record(compute)
+            done[s // REC] = ev
+            done.pop(s // REC - RING // REC - 2, None)
+
+    s_next = 0
+    upload_step(0)
+
+    def run_step(events=None):
+        nonlocal s_next
+        upload_step(s_next + 1)
+        forward_step(s_next, events)
+        s_next += 1
 
     for i in range(warmup):
-        step(i)
+        run_step()
     torch.cuda.synchronize()
     nst = hb.NUM_STAGES
     # Per-stage HIP events go on every STAGE_EVERY-th timed step only: each
     # event recorded between two kernels leaves a bubble of about 6 us on the
     # stream, so events on every step would add ~50 us to each.  The stage
     # breakdown (and the dominant kernel's live timing) are the means over the
-    # instrumented steps; ms_per_step covers all timed steps.
+    # instrumented steps; ms_per_step covers all timed steps, bubbles of the
+    # instrumented ones included.
     inst = [i for i in range(steps) if i % STAGE_EVERY == STAGE_EVERY - 1] or [steps - 1]
     evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for i in inst}
     for row in evs.values():   # torch creates the hipEvent on first record
@@ -263,30 +287,36 @@ def bench_batch(wl, name, steps, warmup, copies, calibrate_copy=False):
     torch.cuda.synchronize()
     assert all(e.cuda_event for row in evs.values() for e in row)
     ev_arrays = {i: hb.make_events([e.cuda_event for e in row]) for i, row in evs.items()}
-    # step-boundary events (the compute stream already waits there for the
-    # step's metadata copy; with and without them the step time measured the same)
-    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     host_s = np.zeros(steps)
+    t_start.record()
     for i in range(steps):
         h0 = time.perf_counter()
-        step_ev[i].record()
-        step(warmup + i, ev_arrays.get(i))
+        run_step(ev_arrays.get(i))
         host_s[i] = time.perf_counter() - h0
-    step_ev[steps].record()
+    t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms = step_ev[0].elapsed_time(step_ev[steps]) / steps
+    ms = t_start.elapsed_time(t_end) / steps
     if calibrate_copy:
         src = torch.empty(64 << 20, dtype=torch.int32, device="cuda").fill_(1)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
-    plain = [i for i in range(steps) if i not in evs] or list(range(steps))
-    step_ms = np.array([step_ev[i].elapsed_time(step_ev[i + 1]) for i in plain])
-    inst_ms = np.array([step_ev[i].elapsed_time(step_ev[i + 1]) for i in inst])
+    # step-time distribution: a separate, untimed pass with an event at every
+    # step boundary (each adds its own bubble to the step it opens)
+    NPCT = 32
+    pct_ev = [torch.cuda.Event(enable_timing=True) for _ in range(NPCT + 1)]
+    for i in range(NPCT):
+        pct_ev[i].record()
+        run_step()
+    pct_ev[NPCT].record()
+    torch.cuda.synchronize()
+    step_ms = np.array([pct_ev[i].elapsed_time(pct_ev[i + 1]) for i in range(NPCT)])
+    inst_ms = np.array([evs[i][0].elapsed_time(evs[i][nst]) for i in inst])
     stage_ms = np.array([[evs[i][k].elapsed_time(evs[i][k + 1]) for k in range(nst)] for i in inst])
     stage_mean = stage_ms.mean(axis=0)
 
@@ -345,6 +375,7 @@ def bench_batch(wl, name, steps, warmup, copies, calibrate_copy=False):
         "layer_iters_per_s": round(1e3 / ms, 1),
         "layer_roofline_frac": round(t_roof / (ms * 1e-3), 4),
         "step_ms_p10_p50_p90": [round(float(np.percentile(step_ms, q)), 5) for q in (10, 50, 90)],
+        "step_ms_note": "p10/p50/p90 from a separate pass of %d steps with an event at every step boundary" % NPCT,
         "instrumented_step_ms_p50": round(float(np.median(inst_ms)), 5),
         "instrumented_steps": len(inst),
         "host_issue_ms_p50": round(float(np.median(host_s)) * 1e3, 4),
