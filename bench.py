@@ -44,6 +44,8 @@ def workload_by_name(name):
         return W.tau_sweep(int(name.rsplit("_", 1)[1]), 0)
     if name == "yi_tau2048":
         return W.yi_tau2048(0)
+    if name == "yi_tau2048_tp2":
+        return W.yi_tau2048_tp2(0)
     if name == "tiny":
         return W.tiny(0)
     raise SystemExit(f"unknown workload {name}")

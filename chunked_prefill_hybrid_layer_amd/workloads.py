@@ -370,6 +370,19 @@ def with_w8a8(wl: Workload, seed: int = 0) -> Workload:
     return wl
 
 
+YI_TP2 = Dims(hidden=7168, n_q_heads=28, n_kv_heads=4, head_dim=128, ffn_dim=10240)
+
+
+def yi_tau2048_tp2(seed: int = 0) -> Workload:
+    """One GPU's share of the Yi-34B-shaped layer under 2-way tensor
+    parallelism: half the q and kv heads (28 / 4, g = 7) and half the FFN
+    (10240), full hidden size, over the batch of yi_tau2048 (its lengths and
+    block tables; the KV pool holds this GPU's 4 kv heads)."""
+    _, _, rl, _, _, _ = _streams(seed)
+    ctx = _lognormal_ctx(rl, 512, 2048, 16384)
+    return build_workload("yi_tau2048_tp2", YI_TP2, [768, 768], [0, 6144], ctx, seed, token_budget=2048)
+
+
 def small(seed: int = 0, n_q: int = 8, n_kv: int = 2, head_dim: int = 128,
           chunk_len=(77, 130), chunk_prefix=(45, 0), decode_ctx=(1, 15, 16, 17, 200, 333, 1000),
           hidden: int = 512, ffn: int = 1024) -> Workload:

@@ -287,6 +287,12 @@ def test_full_size_yi_tau2048():
     _full_size(W.yi_tau2048(0), 24, calibrate=True)
 
 
+def test_full_size_yi_tau2048_tp2_share():
+    """One GPU's share of Yi-34B under 2-way tensor parallelism (28 q / 4 kv
+    heads, g = 7, FFN 10240) over the tau=2048 batch."""
+    _full_size(W.yi_tau2048_tp2(0), 16, calibrate=True)
+
+
 # ---------------------------------------------------------------- FP8 e4m3 KV cache
 
 @pytest.mark.parametrize("head_dim,n_kv", [(128, 2), (64, 4)])
