@@ -126,6 +126,21 @@ def test_layer_parity_tiny_three_chunks():
     compare_cache(layer.cache_logical(), cache, b.num_pages, slots, "tiny")
 
 
+def test_layer_parity_max_hidden():
+    """The largest supported hidden size (16384: the norms and the split-K
+    reduce hold a whole row in registers) with a chunk and decodes."""
+    log("layer parity hidden 16384")
+    wl = W.small(5, n_q=4, n_kv=2, head_dim=128, hidden=16384, ffn=512, chunk_len=(40,), chunk_prefix=(17,),
+                 decode_ctx=(1, 300))
+    b = wl.batch
+    layer = _layer_for(wl)
+    layer.fill_prefixes(b.block_table, range(b.n_seq), wl.prefix_k, wl.prefix_v)
+    y, _ = _run(layer, wl)
+    r, cache = oracle_forward(wl)
+    assert_close(y, r.y, "hidden 16384 y")
+    compare_cache(layer.cache_logical(), cache, b.num_pages, _new_slots(b), "hidden 16384")
+
+
 def test_page_permutation_gives_identical_output():
     """Moving every sequence to other physical pages changes nothing: y is bit-identical."""
     log("page permutation")
