@@ -144,8 +144,9 @@ def cpu_baseline(wl, stride=4):
     dt = time.perf_counter() - t0
     return {"value": len(rows) / dt, "unit": "tokens/s", "cores": _oracle_threads(), "cpu_model": _cpu_model(),
             "kind": "oracle",
-            "sample": f"{len(rows)} of the {b.n_tokens} packed tokens (every {stride}th; K/V for all "
-                      f"{b.n_tokens}) of the same batch, float64 numpy oracle, {dt:.1f} s"}
+            "sample": (f"all {b.n_tokens} packed tokens" if stride == 1 else
+                       f"{len(rows)} of the {b.n_tokens} packed tokens (every {stride}th; K/V for all {b.n_tokens})") +
+                      f" of the same batch, float64 numpy oracle, {dt:.1f} s"}
 
 
 def _oracle_cache(O, wl):
@@ -431,7 +432,7 @@ def sweep_tau(args):
         out = bench_batch(wl, f"tau_sweep_{tau}{suffix}", args.steps, args.warmup, args.copies)
         out["metric"] = "hybrid-layer tokens/s, token-budget sweep (Mistral-7B-shaped layer)"
         if not args.no_cpu_baseline:
-            out["cpu_baseline"] = cpu_baseline(wl, stride=max(4, tau // 64))
+            out["cpu_baseline"] = cpu_baseline(wl, stride=max(1, tau // 512))
         print(json.dumps(out), flush=True)
         d = wl.dims
         psi = d.hidden * (d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim + d.n_q_heads * d.head_dim * d.hidden + \
@@ -720,7 +721,8 @@ def main():
         if args.workload == "tiny":
             out["cpu_baseline"] = cpu_baseline_whole(wl)
         else:
-            out["cpu_baseline"] = cpu_baseline(wl, stride=4 if wl.batch.n_tokens <= 1024 else 32)
+            # about 10 s of oracle work on a 16-core host
+            out["cpu_baseline"] = cpu_baseline(wl, stride=1 if wl.batch.n_tokens <= 1024 else 4)
     print(json.dumps(out), flush=True)
 
 
