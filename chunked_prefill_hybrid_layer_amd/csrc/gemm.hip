@@ -63,13 +63,13 @@ struct Tile {
   static constexpr int CPR = BK / 8;                          // 16-byte chunks per LDS row
   static constexpr int RPL = 64 / CPR;                        // rows per 1 KB wave load
   static constexpr int STAGE_ELEMS = (BM + BN) * BK;
-  static constexpr int TOTAL_LOADS = (BM + BN) / RPL;         // 1 KB loads per stage
-  static constexpr int LOADS = (TOTAL_LOADS + WAVES - 1) / WAVES;  // per wave (some waves one fewer)
   static constexpr int MAIN_LDS = NST * STAGE_ELEMS * 2;
   static constexpr int CS_LD = BN + 4;                        // fp32 staging row stride
   static constexpr int EPI_ROWS = BM * CS_LD * 4 <= 160 * 1024 - 4096 ? BM : BM / 2;
   static constexpr int EPI_LDS = EPI_ROWS * CS_LD * 4;
   static constexpr int LDS = MAIN_LDS > EPI_LDS ? MAIN_LDS : EPI_LDS;
+  static constexpr int TOTAL_LOADS = (BM + BN) / RPL;         // 1 KB loads per stage
+  static constexpr int LOADS = (TOTAL_LOADS + WAVES - 1) / WAVES;  // per wave (some waves one fewer)
   static_assert((BM + BN) % RPL == 0, "stage rows must split into whole wave loads");
   static_assert(EPI_ROWS % (BM / WM) == 0, "epilogue passes must hold whole waves");
 };
@@ -309,7 +309,7 @@ __global__ __launch_bounds__(TL::THREADS) void gemm_kernel(GemmArgs g) {
   __shared__ __align__(16) unsigned char smem[TL::LDS];
   uint16_t* lds = reinterpret_cast<uint16_t*>(smem);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / TL::WN, wn = wave % TL::WN;
   const int tiles_m = (g.M + BM - 1) / BM;
   int bid = blockIdx.x;
@@ -327,6 +327,12 @@ __global__ __launch_bounds__(TL::THREADS) void gemm_kernel(GemmArgs g) {
   // When the loads of a stage do not divide evenly over the waves, the waves
   // short of one repeat the stage's last load (same bytes to the same LDS
   // address), so that every wave counts the same number of loads per stage.
+  // bf16: waves 0-3 issue a stage's loads right after the barrier, waves 4-7
+  // after the stage's MFMAs: the two waves of a SIMD issue at different times,
+  // so one of them has MFMAs to issue while the other waits on its load queue.
+  // (FP8 keeps every wave issuing after the barrier: its fragment registers
+  // leave no room for the longer live ranges.)
+  const bool late = !F8 && wave >= 4;
   const uint16_t* gsrc[NL];
   int ldst[NL];
 #pragma unroll
@@ -444,7 +450,7 @@ __global__ __launch_bounds__(TL::THREADS) void gemm_kernel(GemmArgs g) {
     WAIT_LGKM0();                                                                                \
     __builtin_amdgcn_s_barrier();                                                                \
     asm volatile("" ::: "memory");                                                               \
-    if ((KT) + LEAD < nk) ISSUE_STAGE((KT) + LEAD);                                              \
+    if (!late && (KT) + LEAD < nk) ISSUE_STAGE((KT) + LEAD);                                   \
     if constexpr (F8) {                                                                          \
       MFMAS8(CUR, NXT, (KT) + 1, true);                                                          \
       _Pragma("unroll") for (int _j = 0; _j < FM; ++_j) {                                        \
@@ -468,6 +474,7 @@ __global__ __launch_bounds__(TL::THREADS) void gemm_kernel(GemmArgs g) {
         }                                                                                        \
       }                                                                                          \
     }                                                                                            \
+    if (late && (KT) + LEAD < nk) ISSUE_STAGE((KT) + LEAD);                                    \
   }
 
 #pragma unroll
@@ -534,13 +541,13 @@ __global__ __launch_bounds__(TL::THREADS) void gemm_kernel(GemmArgs g) {
 template <int MODE, class TL>
 __global__ __launch_bounds__(TL::THREADS) void gemm_sub_kernel(GemmArgs g) {
   constexpr int BM = TL::BM, BN = TL::BN, BK = TL::BK, SE = TL::STAGE_ELEMS;
-  constexpr int NL = TL::LOADS, FM = TL::FM, FN = TL::FN, CPR = TL::CPR, RPL = TL::RPL;
+  constexpr int FM = TL::FM, FN = TL::FN, CPR = TL::CPR, RPL = TL::RPL;
   constexpr int WROWS = BM / TL::WM, WCOLS = BN / TL::WN;
   static_assert(TL::NST == 2 && TL::KS == 2 && FN >= FM + 2, "sub-step pipeline layout");
   __shared__ __align__(16) unsigned char smem[TL::LDS];
   uint16_t* lds = reinterpret_cast<uint16_t*>(smem);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / TL::WN, wn = wave % TL::WN;
   const int tiles_m = (g.M + BM - 1) / BM;
   int bid = blockIdx.x;
@@ -551,13 +558,23 @@ __global__ __launch_bounds__(TL::THREADS) void gemm_sub_kernel(GemmArgs g) {
   const int nk = (g.K / BK) / gridDim.z;
   const int k_first = blockIdx.z * nk;
 
-  const uint16_t* gsrc[NL];
-  int ldst[NL];
-  // (the last load index exists only on the first TOTAL_LOADS % WAVES waves)
-  constexpr int TOT = TL::TOTAL_LOADS;
+  // Load split: the A rows' loads (activations, L2-resident) go to waves
+  // 4-7, the weight rows' loads (first touch from HBM) to waves 0-3.  Waves
+  // 0-3 issue right after the barrier, waves 4-7 after the MFMAs of the second
+  // sub-step, so the two waves of a SIMD issue at different times and one of
+  // them always has MFMAs to issue while the other waits on its load queue;
+  // the loads with the longer latency get the longer slack.
+  constexpr int LA = BM / RPL, LB = TL::BN / RPL;          // A and weight loads per stage
+  constexpr int NLA = LA / 4, NLB = (LB + 3) / 4;
+  constexpr int NLS = NLA > NLB ? NLA : NLB;
+  static_assert(LA % 4 == 0 && TL::WAVES == 8, "load split layout");
+  const bool a_side = wave >= 4;
+  const int nl = a_side ? NLA : (LB / 4 + ((wave & 3) < LB % 4 ? 1 : 0));
+  const uint16_t* gsrc[NLS];
+  int ldst[NLS];
 #pragma unroll
-  for (int i = 0; i < NL; ++i) {
-    const int q = min(wave + TL::WAVES * i, TOT - 1);
+  for (int i = 0; i < NLS; ++i) {
+    const int q = a_side ? (wave & 3) + 4 * i : LA + min((wave & 3) + 4 * i, LB - 1);
     const int r = RPL * q + lane / CPR;
     const int rr = r < BM ? r : r - BM;
     const int c = swz<CPR>(rr, lane % CPR);
@@ -565,12 +582,11 @@ __global__ __launch_bounds__(TL::THREADS) void gemm_sub_kernel(GemmArgs g) {
               (size_t)k_first * BK + c * 8;
     ldst[i] = RPL * q * BK;
   }
-  const bool last_load = wave + TL::WAVES * (NL - 1) < TOT;
 #define ISSUE_STAGE(KT)                                                                              \
   {                                                                                                  \
     uint16_t* _st = lds + ((KT) & 1) * SE;                                                           \
-    _Pragma("unroll") for (int i = 0; i < NL; ++i)                                                   \
-      if (i < NL - 1 || last_load)                                                                   \
+    _Pragma("unroll") for (int i = 0; i < NLS; ++i)                                                  \
+      if (i < nl)                                                                                    \
         __builtin_amdgcn_global_load_lds((const void*)(gsrc[i] + (size_t)(KT) * BK),                 \
                                          (lds_ptr_t)(_st + ldst[i]), 16, 0, 0);                      \
   }
@@ -639,8 +655,9 @@ __global__ __launch_bounds__(TL::THREADS) void gemm_sub_kernel(GemmArgs g) {
     WAIT_LGKM0();    // this wave's reads of the second half of stage st are done
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (st + 2 < nk) ISSUE_STAGE(st + 2);
+    if (!a_side && st + 2 < nk) ISSUE_STAGE(st + 2);
     SUBSTEP(1, 0, st + 1, 0, true);
+    if (a_side && st + 2 < nk) ISSUE_STAGE(st + 2);
   }
   SUBSTEP(0, 1, nk - 1, 1, true);
   SUBSTEP(1, 0, 0, 0, false);
@@ -650,6 +667,178 @@ __global__ __launch_bounds__(TL::THREADS) void gemm_sub_kernel(GemmArgs g) {
   WAIT_VMCNT(0);
   __syncthreads();
   gemm_epilogue<MODE, TL>(g, acc, smem, m0, n0, wm, wn, lane, tid);
+}
+
+// Wave-specialised pipeline.  Consumer waves 0-3 (one per SIMD) run every
+// MFMA of the tile, each a 64-row block across all BN columns; producer waves
+// 4-7 (the other wave of each SIMD) issue every direct-to-LDS load, into a
+// ring of NST stages.  A wave whose vector-memory queue is full stalls at its
+// next load; with the loads kept out of the MFMA waves' instruction streams,
+// that stall no longer holds up MFMA issue.  The consumers follow the
+// sub-step schedule (fragments of the next 32-deep sub-step read during the
+// MFMAs of the current one); the one barrier per stage, between its two
+// sub-steps, tells the producers that the buffer read last is free and the
+// consumers that the next stage has landed.
+template <int BM_, int BN_, int NST_>
+struct SpecTile {
+  static constexpr int BM = BM_, BN = BN_, BK = 64, NST = NST_;
+  static constexpr int WM = 4, WN = 1;                          // consumer blocks
+  static constexpr int CONSUMERS = 4, PRODUCERS = 4, WAVES = 8, THREADS = 512;
+  static constexpr int FM = BM / WM / 16, FN = BN / WN / 16;
+  static constexpr int KS = BK / 32, CPR = BK / 8, RPL = 64 / CPR;
+  static constexpr int STAGE_ELEMS = (BM + BN) * BK;
+  static constexpr int TOTAL_LOADS = (BM + BN) / RPL;
+  static constexpr int LOADS = TOTAL_LOADS / PRODUCERS;          // per producer wave and stage
+  static constexpr int MAIN_LDS = NST * STAGE_ELEMS * 2;
+  static constexpr int CS_LD = BN + 4;
+  static constexpr int EPI_ROWS = BM * CS_LD * 4 <= 160 * 1024 - 4096 ? BM : BM / 2;
+  static constexpr int EPI_LDS = EPI_ROWS * CS_LD * 4;
+  static constexpr int LDS = MAIN_LDS > EPI_LDS ? MAIN_LDS : EPI_LDS;
+  static_assert(TOTAL_LOADS % PRODUCERS == 0, "stage loads must split evenly over the producers");
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+using TileS256 = SpecTile<256, 128, 3>;
+
+template <int MODE, class TL>
+__global__ __launch_bounds__(TL::THREADS) void gemm_spec_kernel(GemmArgs g) {
+  constexpr int BM = TL::BM, BK = TL::BK, NST = TL::NST, SE = TL::STAGE_ELEMS;
+  constexpr int NL = TL::LOADS, FM = TL::FM, FN = TL::FN, CPR = TL::CPR, RPL = TL::RPL;
+  constexpr int WROWS = BM / TL::WM;
+  static_assert(TL::KS == 2 && FN >= FM + 2 && NST >= 2 && NST <= 3, "sub-step pipeline layout");
+  __shared__ __align__(16) unsigned char smem[TL::LDS];
+  uint16_t* lds = reinterpret_cast<uint16_t*>(smem);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tiles_m = (g.M + BM - 1) / BM;
+  int bid = blockIdx.x;
+  const int nblk = gridDim.x;
+  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  const int tm = bid % tiles_m, tn = bid / tiles_m;
+  const int m0 = tm * BM, n0 = tn * TL::BN;
+  const int nk = (g.K / BK) / gridDim.z;
+  const int k_first = blockIdx.z * nk;
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int wm = wave;   // consumer block row; producers stage nothing in the epilogue
+
+  if (wave >= TL::CONSUMERS) {
+    wm = 1 << 20;
+    // producer p issues loads q = p + PRODUCERS * i of every stage: rows
+    // [RPL q, RPL q + RPL) of the stage image (A rows, then weight rows), lane
+    // l at row RPL q + l / CPR, swizzled chunk (l % CPR) ^ f(row)
+    const int p = wave - TL::CONSUMERS;
+    const uint16_t* gsrc[NL];
+    int ldst[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int q = p + TL::PRODUCERS * i;
+      const int r = RPL * q + lane / CPR;
+      const int rr = r < BM ? r : r - BM;
+      const int c = swz<CPR>(rr, lane % CPR);
+      gsrc[i] = (r < BM ? g.a + (size_t)min(m0 + rr, g.M - 1) * g.lda : weight_row<MODE, TL::BN>(g, n0 + rr, n0)) +
+                (size_t)k_first * BK + c * 8;
+      ldst[i] = RPL * q * BK;
+    }
+    auto issue = [&](int kt) {
+      uint16_t* st = lds + (kt % NST) * SE;
+#pragma unroll
+      for (int i = 0; i < NL; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(gsrc[i] + (size_t)kt * BK), (lds_ptr_t)(st + ldst[i]), 16, 0,
+                                         0);
+    };
+#pragma unroll
+    for (int s = 0; s < NST; ++s)
+      if (s < nk) issue(s);
+    // stage 0 landed: the loads of the stages after it may still be in flight
+    {
+      const int later = min(NST, nk) - 1;
+      if (later >= 2) WAIT_VMCNT(2 * NL);
+      else if (later == 1) WAIT_VMCNT(NL);
+      else WAIT_VMCNT(0);
+    }
+    __builtin_amdgcn_s_barrier();
+    for (int st = 0; st + 1 < nk; ++st) {
+      // stage st + 1 landed (stages issued so far: up to st + NST - 1)
+      const int later = min(st + NST, nk) - (st + 2);
+      if (later >= 1) WAIT_VMCNT(NL);
+      else WAIT_VMCNT(0);
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      // every consumer has read stage st: refill its buffer
+      if (st + NST < nk) issue(st + NST);
+    }
+    WAIT_VMCNT(0);
+  } else {
+    bf16x8 fa[2][FM], fb[FN - 2], fbl[2][2];
+    const int arow = wave * WROWS + (lane & 15), brow = lane & 15;
+#define RD(BASE, R, KK) \
+  (*reinterpret_cast<const bf16x8*>((BASE) + (R) * BK + swz<CPR>((R), (KK) * 4 + (lane >> 4)) * 8))
+    // compute the sub-step held in fa[CUR], fb, fbl[CUR]; with NEXT, read the
+    // fragments of sub-step KK1 of the stage in buffer B1 in between.
+#define SUBSTEP(CUR, NXT, B1, KK1, NEXT)                                                          \
+  {                                                                                               \
+    const uint16_t* _as = lds + (B1) * SE;                                                        \
+    const uint16_t* _bs = _as + BM * BK;                                                          \
+    _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                              \
+      _Pragma("unroll") for (int i = 0; i < FM; ++i)                                              \
+        acc[i][j] = mfma16x16x32(fa[CUR][i], j < FN - 2 ? fb[j < FN - 2 ? j : 0] : fbl[CUR][j - (FN - 2) >= 0 ? j - (FN - 2) : 0], acc[i][j]); \
+      if (NEXT) {                                                                                 \
+        if (j == 0) {                                                                             \
+          fbl[NXT][0] = RD(_bs, brow + (FN - 2) * 16, KK1);                                      \
+          fbl[NXT][1] = RD(_bs, brow + (FN - 1) * 16, KK1);                                      \
+        }                                                                                         \
+        if (j < FN - 2) fb[j < FN - 2 ? j : 0] = RD(_bs, brow + j * 16, KK1);                     \
+        if (j >= 1 && j <= FM) fa[NXT][j >= 1 && j <= FM ? j - 1 : 0] = RD(_as, arow + (j - 1) * 16, KK1); \
+      }                                                                                           \
+    }                                                                                             \
+    if (NEXT) {                                                                                   \
+      __builtin_amdgcn_sched_group_barrier(0x008, FM, 0);                                         \
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);                                          \
+      _Pragma("unroll") for (int _j = 1; _j <= FM; ++_j) {                                        \
+        __builtin_amdgcn_sched_group_barrier(0x008, FM, 0);                                       \
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                                        \
+      }                                                                                           \
+      _Pragma("unroll") for (int _j = FM + 1; _j < FN - 2; ++_j) {                                \
+        __builtin_amdgcn_sched_group_barrier(0x008, FM, 0);                                       \
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                        \
+      }                                                                                           \
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * FM, 0);                                     \
+    }                                                                                             \
+  }
+    __builtin_amdgcn_s_barrier();   // stage 0 has landed
+    asm volatile("" ::: "memory");
+    {
+      const uint16_t* _as = lds;
+      const uint16_t* _bs = _as + BM * BK;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) fa[0][i] = RD(_as, arow + i * 16, 0);
+#pragma unroll
+      for (int j = 0; j < FN - 2; ++j) fb[j] = RD(_bs, brow + j * 16, 0);
+      fbl[0][0] = RD(_bs, brow + (FN - 2) * 16, 0);
+      fbl[0][1] = RD(_bs, brow + (FN - 1) * 16, 0);
+    }
+    int b0 = 0;   // buffer of stage st
+    for (int st = 0; st + 1 < nk; ++st) {
+      const int b1 = b0 + 1 == NST ? 0 : b0 + 1;
+      SUBSTEP(0, 1, b0, 1, true);
+      WAIT_LGKM0();   // this wave's reads of stage st are done
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      SUBSTEP(1, 0, b1, 0, true);
+      b0 = b1;
+    }
+    SUBSTEP(0, 1, b0, 1, true);
+    SUBSTEP(1, 0, 0, 0, false);
+#undef SUBSTEP
+#undef RD
+  }
+  __syncthreads();
+  gemm_epilogue<MODE, TL>(g, acc, smem, m0, n0, wm, 0, lane, tid);
 }
 
 // y[m][:] = res[m][:] + sum_z part[z][m][:] (z in order); with norm_out, also
@@ -726,7 +915,7 @@ __global__ __launch_bounds__(256) void qkv_reduce_kernel(GemmArgs g, int splits)
   qkv_store4(g, m, n, x0, x1);
 }
 
-enum { kTile256 = 1, kTileW256 = 2, kTileW224 = 3, kTile128W8 = 4, kTile128N96 = 5 };
+enum { kTile256 = 1, kTileW256 = 2, kTileW224 = 3, kTile128W8 = 4, kTile128N96 = 5, kTileS256 = 6 };
 
 // Estimated time of one GEMM under a tile choice, fitted (least squares, 37
 // measured tile/split choices on the Mistral-7B- and Yi-34B-shaped
@@ -762,21 +951,24 @@ static void plan_try(GemmPlan& best, double& best_cost, int tile, int mode, int 
   }
 }
 
-// Efficiencies: fraction of the MFMA peak per busy CU with every CU busy (fit;
-// 256x224 raised from 0.455 to 0.485 to match the layer, where it beats
-// 256x256 by 3-6 % on gate/up, O and down whenever both apply).
-// FP8 (f8): K counts codes; the plan is made for K / 2 units (same bytes and
-// the same MFMA cycles per stage as bf16), on the ring-pipeline tiles.
+// Efficiencies: fraction of the MFMA peak per busy CU with every CU busy (fit
+// to measured times of the bf16 kernels on the Mistral- and Yi-shaped
+// projections; 256x224 set so that it beats 256x256 where both apply, as
+// measured in the layer).  FP8 (f8): K counts codes; the plan is made for
+// K / 2 units (same bytes and the same MFMA cycles per stage as bf16), on the
+// ring-pipeline tiles; the FP8 ring kernel keeps the unskewed load issue, so
+// its 256x128 tile keeps the earlier fit.
 GemmPlan gemm_plan(int mode, int M, int N, int K, bool f8) {
   GemmPlan p{kTile128W8, 1};
   double cost = 1e30;
   if (f8) K /= 2;
   plan_try<Tile128W8>(p, cost, kTile128W8, mode, M, N, K, 0.344);
-  plan_try<Tile128N96>(p, cost, kTile128N96, mode, M, N, K, 0.291);
+  plan_try<Tile128N96>(p, cost, kTile128N96, mode, M, N, K, f8 ? 0.291 : 0.31);
   if (M < 256) return p;
-  plan_try<Tile256>(p, cost, kTile256, mode, M, N, K, 0.426);
+  plan_try<Tile256>(p, cost, kTile256, mode, M, N, K, f8 ? 0.426 : 0.445);
   if (f8) return p;
-  plan_try<TileW256>(p, cost, kTileW256, mode, M, N, K, 0.515);
+  plan_try<TileS256>(p, cost, kTileS256, mode, M, N, K, 0.49);
+  plan_try<TileW256>(p, cost, kTileW256, mode, M, N, K, 0.53);
   plan_try<TileW224>(p, cost, kTileW224, mode, M, N, K, 0.485);
   return p;
 }
@@ -788,6 +980,16 @@ static void launch_sub(const GemmArgs& g, int splits, hipStream_t s) {
     case kGemmQkvRope: hipLaunchKernelGGL((gemm_sub_kernel<kGemmQkvRope, TL>), grid, dim3(TL::THREADS), 0, s, g); break;
     case kGemmResidual: hipLaunchKernelGGL((gemm_sub_kernel<kGemmResidual, TL>), grid, dim3(TL::THREADS), 0, s, g); break;
     default: hipLaunchKernelGGL((gemm_sub_kernel<kGemmSwiglu, TL>), grid, dim3(TL::THREADS), 0, s, g); break;
+  }
+}
+
+template <class TL>
+static void launch_spec(const GemmArgs& g, int splits, hipStream_t s) {
+  const dim3 grid((unsigned)(((g.M + TL::BM - 1) / TL::BM) * (g.N / TL::BN)), 1, splits);
+  switch (g.mode) {
+    case kGemmQkvRope: hipLaunchKernelGGL((gemm_spec_kernel<kGemmQkvRope, TL>), grid, dim3(TL::THREADS), 0, s, g); break;
+    case kGemmResidual: hipLaunchKernelGGL((gemm_spec_kernel<kGemmResidual, TL>), grid, dim3(TL::THREADS), 0, s, g); break;
+    default: hipLaunchKernelGGL((gemm_spec_kernel<kGemmSwiglu, TL>), grid, dim3(TL::THREADS), 0, s, g); break;
   }
 }
 
@@ -818,7 +1020,8 @@ hb_status launch_gemm(const GemmArgs& ga, stream_t s) {
     if (p.tile == kTile256) launch_tile<Tile256, true>(g, p.splits, (hipStream_t)s);
     else if (p.tile == kTile128N96) launch_tile<Tile128N96, true>(g, p.splits, (hipStream_t)s);
     else launch_tile<Tile128W8, true>(g, p.splits, (hipStream_t)s);
-  } else if (p.tile == kTileW224) launch_sub<TileW224>(g, p.splits, (hipStream_t)s);
+  } else if (p.tile == kTileS256) launch_spec<TileS256>(g, p.splits, (hipStream_t)s);
+  else if (p.tile == kTileW224) launch_sub<TileW224>(g, p.splits, (hipStream_t)s);
   else if (p.tile == kTileW256) launch_sub<TileW256>(g, p.splits, (hipStream_t)s);
   else if (p.tile == kTile256) launch_tile<Tile256, false>(g, p.splits, (hipStream_t)s);
   else if (p.tile == kTile128W8) launch_tile<Tile128W8, false>(g, p.splits, (hipStream_t)s);
