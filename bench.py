@@ -389,16 +389,17 @@ def bench_batch(wl, name, steps, warmup, copies, calibrate_copy=False):
 
 
 def sclk_mhz():
-    """Current shader clock as reported by rocm-smi (None if unavailable)."""
-    import subprocess
+    """Current shader clock of cuda:0 from the driver's sysfs table (the entry
+    marked '*' in pp_dpm_sclk of the device's PCI function), or None.  Read as
+    a file: no helper program is started."""
+    import torch
     try:
-        out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
-                             timeout=20).stdout
-        rec = json.loads(out)
-        for card in rec.values():
-            for k, v in card.items():
-                if "sclk" in k.lower():
-                    return v
+        pr = torch.cuda.get_device_properties(0)
+        dev = "%04x:%02x:%02x.0" % (getattr(pr, "pci_domain_id", 0), pr.pci_bus_id, pr.pci_device_id)
+        with open(os.path.join("/sys/bus/pci/devices", dev, "pp_dpm_sclk")) as f:
+            for line in f:
+                if line.rstrip().endswith("*"):
+                    return line.split(":", 1)[1].replace("*", "").strip()
     except Exception:
         return None
     return None
