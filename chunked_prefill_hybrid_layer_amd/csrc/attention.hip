@@ -648,15 +648,16 @@ static hb_status launch_attention_d(const AttnArgs& a, stream_t s, void* const* 
   // FP8: keys are code * k_scale, so k_scale joins the score scale
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D) * (F8 ? a.k_scale : 1.0f);
   hipStream_t st = (hipStream_t)s;
-  if (ev) hipEventRecord((hipEvent_t)ev[0], st);
+  auto mark = [&](int i) -> bool { return !ev || hipEventRecord((hipEvent_t)ev[i], st) == hipSuccess; };
+  if (!mark(0)) return fail(HB_E_HIP, "attention: stage event record failed");
   if (a.n_chunk_items > 0)
     hipLaunchKernelGGL((attn_chunk_kernel<D, F8>), dim3((unsigned)a.n_chunk_items * a.n_kv_heads), dim3(256), 0, st, a,
                        scale_log2);
-  if (ev) hipEventRecord((hipEvent_t)ev[1], st);
+  if (!mark(1)) return fail(HB_E_HIP, "attention: stage event record failed");
   if (a.n_decode_items > 0)
     hipLaunchKernelGGL((attn_decode_kernel<D, F8>), dim3((a.n_decode_items + 3) / 4, a.n_kv_heads), dim3(256), 0, st, a,
                        scale_log2);
-  if (ev) hipEventRecord((hipEvent_t)ev[2], st);
+  if (!mark(2)) return fail(HB_E_HIP, "attention: stage event record failed");
   const int64_t pairs = (int64_t)a.n_tokens * a.n_q_heads, per_block = 256 / (D / 4);
   hipLaunchKernelGGL(attn_merge_kernel<D>, dim3((unsigned)((pairs + per_block - 1) / per_block)), dim3(256), 0, st,
                      a);

@@ -88,8 +88,10 @@ extern "C" hb_status hb_layer_forward(const hb_dims* dims, const hb_weights* w, 
 
   const stream_t s = (stream_t)stream;
   // optional per-stage timing events (see HB_STAGE_NAMES)
-  auto mark = [&](int i) {
-    if (stage_events) hipEventRecord((hipEvent_t)stage_events[i], (hipStream_t)stream);
+  auto mark = [&](int i) -> hb_status {
+    if (stage_events && hipEventRecord((hipEvent_t)stage_events[i], (hipStream_t)stream) != hipSuccess)
+      return fail(HB_E_HIP, "layer_forward: stage event record failed");
+    return HB_OK;
   };
   const DevMeta m = dev_meta(h, meta_dev);
   char* ws = (char*)workspace;
@@ -103,7 +105,7 @@ extern "C" hb_status hb_layer_forward(const hb_dims* dims, const hb_weights* w, 
   const int F = dims->ffn_dim;
 
   // a1: RMSNorm of the input
-  mark(0);
+  HB_TRY(mark(0));
   HB_TRY(launch_rmsnorm(x, w->g_attn, xn, T, H, dims->rms_eps, s, f8 ? 1.0f / dims->x_scale : 0.0f));
 
   // a2-a4: QKV projection, RoPE, KV append
@@ -137,7 +139,7 @@ extern "C" hb_status hb_layer_forward(const hb_dims* dims, const hb_weights* w, 
   g.n_kv_heads = nkv;
   g.head_dim = d;
   g.part = (float*)(ws + L.gemm_part);
-  mark(1);
+  HB_TRY(mark(1));
   HB_TRY(launch_gemm(g, s));
 
   // a5: hybrid attention over the paged cache
@@ -183,9 +185,9 @@ extern "C" hb_status hb_layer_forward(const hb_dims* dims, const hb_weights* w, 
   go.out_f = h1;
   go.ldo = H;
   go.part = gpart;
-  mark(5);
+  HB_TRY(mark(5));
   HB_TRY(launch_gemm(go, s));
-  mark(6);
+  HB_TRY(mark(6));
   const float h_inv = f8 ? 1.0f / dims->h_scale : 0.0f;
   if (po.splits > 1) {
     HB_TRY(launch_splitk_reduce(gpart, po.splits, x, h1, T, H, w->g_ffn, h1n, dims->rms_eps, s, h_inv));
@@ -210,7 +212,7 @@ extern "C" hb_status hb_layer_forward(const hb_dims* dims, const hb_weights* w, 
   gu.out_inv_scale = f8 ? 1.0f / dims->a_scale : 0.0f;
   gu.out_b = act;
   gu.ldo = F;
-  mark(7);
+  HB_TRY(mark(7));
   HB_TRY(launch_gemm(gu, s));
 
   // a9: down projection + residual
@@ -229,9 +231,9 @@ extern "C" hb_status hb_layer_forward(const hb_dims* dims, const hb_weights* w, 
   gd.out_f = y;
   gd.ldo = H;
   gd.part = gpart;
-  mark(8);
+  HB_TRY(mark(8));
   HB_TRY(launch_gemm(gd, s));
   if (pd.splits > 1) HB_TRY(launch_splitk_reduce(gpart, pd.splits, h1, y, T, H, nullptr, nullptr, 0.f, s));
-  mark(9);
+  HB_TRY(mark(9));
   return HB_OK;
 }

@@ -279,7 +279,8 @@ hb_status hb_kv_append(const hb_dims *dims, const void *meta_host, const void *m
  * stage_events: NULL, or HB_NUM_STAGES + 1 caller-created hipEvent_t handles;
  * event i is recorded on `stream` right before stage i is launched and event
  * HB_NUM_STAGES after the last stage, so elapsed(event i, event i+1) is the
- * device time of stage i.  Stages, in launch order: */
+ * device time of stage i.  A failing event record returns HB_E_HIP (the
+ * stages enqueued before it stay enqueued).  Stages, in launch order: */
 #define HB_NUM_STAGES 9
 #define HB_STAGE_NAMES                                                              \
   { "rmsnorm_attn", "qkv_rope_append", "attn_chunk", "attn_decode", "attn_merge", \

@@ -278,18 +278,22 @@ def test_full_size_mistral_tau512():
     _full_size(W.mistral_tau512(0), 64)
 
 
-@pytest.mark.parametrize("case", ["yi_T512", "mistral_T2048", "mistral_T200"])
+@pytest.mark.parametrize("case", ["yi_T512", "mistral_T2048", "mistral_T200", "mistral_T700"])
 def test_full_size_other_gemm_plans(case):
     """Token counts whose GEMM tile / K-split plans the two named
-    configurations do not reach: Yi at T = 512 (QKV on 256x256 tiles with a
-    2-way split and its reduce, O on 256x128 with a 2-way split, gate/up on
-    256x128, down on 256x224 with a 4-way split); Mistral at T = 2048 (QKV on
-    256x256 with the RoPE/append epilogue in the sub-step kernel, down with a
-    2-way split); Mistral at T = 200 (128-row tiles with 2- and 4-way splits)."""
+    configurations do not reach (plans as the planner picks them):
+    Yi at T = 512 (every projection on the wave-specialised 256x128 kernel:
+    QKV with the RoPE/append epilogue, O and down with 2-way splits, gate/up
+    with the SwiGLU epilogue); Mistral at T = 2048 (QKV on 256x256 with the
+    RoPE/append epilogue in the sub-step kernel, O, gate/up and down on the
+    specialised kernel without a split); Mistral at T = 200 (128-row tiles
+    with 2- and 4-way splits); Mistral at T = 700 (all four projections on
+    the specialised kernel with a ragged last row tile of 188 tokens)."""
     dims, cl, cp, n_dec = {
         "yi_T512": (W.YI, [448], [1000], 64),
         "mistral_T2048": (W.MISTRAL, [2000], [300], 48),
         "mistral_T200": (W.MISTRAL, [184], [700], 16),
+        "mistral_T700": (W.MISTRAL, [660], [900], 40),
     }[case]
     rng = np.random.default_rng(11)
     ctx = rng.integers(1, 1500, size=n_dec).astype(np.int32)
