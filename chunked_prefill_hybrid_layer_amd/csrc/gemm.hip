@@ -721,7 +721,8 @@ __global__ __launch_bounds__(TL::THREADS) void gemm_spec_kernel(GemmArgs g) {
   constexpr int BM = TL::BM, BK = TL::BK, NST = TL::NST, SE = TL::STAGE_ELEMS;
   constexpr int NL = TL::LOADS, FM = TL::FM, FN = TL::FN, CPR = TL::CPR, RPL = TL::RPL;
   constexpr int WROWS = BM / TL::WM;
-  static_assert(TL::KS == 2 && FN >= FM + 2 && NST >= 2 && NST <= 3, "sub-step pipeline layout");
+  static_assert(TL::KS == 2 && FN >= FM + 2 && NST >= 2 && NST <= 4, "sub-step pipeline layout");
+  static_assert(3 * NL <= 63, "vmcnt counts at most 63 loads");
   __shared__ __align__(16) unsigned char smem[TL::LDS];
   uint16_t* lds = reinterpret_cast<uint16_t*>(smem);
 
@@ -776,19 +777,19 @@ __global__ __launch_bounds__(TL::THREADS) void gemm_spec_kernel(GemmArgs g) {
 #pragma unroll
     for (int s = 0; s < NST; ++s)
       if (s < nk) issue(s);
-    // stage 0 landed: the loads of the stages after it may still be in flight
-    {
-      const int later = min(NST, nk) - 1;
-      if (later >= 2) WAIT_VMCNT(2 * NL);
-      else if (later == 1) WAIT_VMCNT(NL);
+    // wait until at most N stages of this wave's loads are in flight
+    auto wait_stages = [&](int n) {
+      if (n >= 3) WAIT_VMCNT(3 * NL);
+      else if (n == 2) WAIT_VMCNT(2 * NL);
+      else if (n == 1) WAIT_VMCNT(NL);
       else WAIT_VMCNT(0);
-    }
+    };
+    // stage 0 landed: the loads of the stages after it may still be in flight
+    wait_stages(min(NST, nk) - 1);
     __builtin_amdgcn_s_barrier();
     for (int st = 0; st + 1 < nk; ++st) {
       // stage st + 1 landed (stages issued so far: up to st + NST - 1)
-      const int later = min(st + NST, nk) - (st + 2);
-      if (later >= 1) WAIT_VMCNT(NL);
-      else WAIT_VMCNT(0);
+      wait_stages(min(st + NST, nk) - (st + 2));
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       // every consumer has read stage st: refill its buffer

@@ -71,11 +71,13 @@ WsLayout ws_layout(const hb_dims& d, int T, int n_partials) {
   w.act = take(t * d.ffn_dim * 2);
   w.part_o = take((size_t)n_partials * d.n_q_heads * d.head_dim * 4);
   w.part_ml = take((size_t)n_partials * d.n_q_heads * 2 * 4);
-  // split-K partials: the largest need among the QKV, O and down projections
+  // split-K partials: the largest need among the QKV, O and down projections,
+  // planned exactly as the layer plans them (the FP8 plans may split differently)
   const int nqkv = (d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim;
-  const GemmPlan pq = gemm_plan(kGemmQkvRope, T, nqkv, d.hidden);
-  const GemmPlan po = gemm_plan(kGemmResidual, T, d.hidden, d.n_q_heads * d.head_dim);
-  const GemmPlan pd = gemm_plan(kGemmResidual, T, d.hidden, d.ffn_dim);
+  const bool f8 = d.w8a8 != 0;
+  const GemmPlan pq = gemm_plan(kGemmQkvRope, T, nqkv, d.hidden, f8);
+  const GemmPlan po = gemm_plan(kGemmResidual, T, d.hidden, d.n_q_heads * d.head_dim, f8);
+  const GemmPlan pd = gemm_plan(kGemmResidual, T, d.hidden, d.ffn_dim, f8);
   size_t part = 0;
   if (pq.splits > 1) part = std::max(part, (size_t)pq.splits * t * nqkv);
   if (po.splits > 1) part = std::max(part, (size_t)po.splits * t * d.hidden);
