@@ -91,15 +91,19 @@ __device__ __forceinline__ int swz(int r, int c) {
 }
 
 // Cache policy of the weight rows' direct-to-LDS loads in the 256-row
-// sub-step and wave-specialised kernels: sc0 | nt (miss the CU's L1, stream
-// through L2).  The activation rows are re-read by every tile column;
-// streamed weights leave L2 to them, which lowers the average load latency
-// that bounds the stage loop.  Measured gains 3-11 % (gate/up, down, Yi
-// QKV/O), also with 8 row tiles sharing each weight tile.  The 128-row ring
+// sub-step and wave-specialised kernels when at most kStreamWeightsMaxRowTiles
+// row tiles share each weight tile: sc0 | nt (miss the CU's L1, stream through
+// L2).  The activation rows are re-read by every tile column; streamed
+// weights leave L2 to them, which lowers the average load latency that bounds
+// the stage loop (measured: 256x224 gate/up and specialised down at 512
+// tokens 3-7 % faster).  With more row tiles the weight tile itself is re-read
+// and streaming it costs: at 8 row tiles O lost 5 % while down gained 5 %, at
+// 128 row tiles (a 32768-token prefill) gate/up lost 6 %.  The 128-row ring
 // kernel keeps the default policy: streaming there lost 4-22 % (QKV, O, down;
 // it gained only on gate/up at 128 tokens).  Activation rows always load with
 // the default policy.
 constexpr int kWeightLoadPolicy = 3;
+constexpr int kStreamWeightsMaxRowTiles = 2;
 
 template <int MODE, int BN>
 __device__ __forceinline__ const uint16_t* weight_row(const GemmArgs& g, int n, int n0) {
@@ -581,6 +585,7 @@ __global__ __launch_bounds__(TL::THREADS) void gemm_sub_kernel(GemmArgs g) {
   static_assert(LA % 4 == 0 && TL::WAVES == 8, "load split layout");
   const bool a_side = wave >= 4;
   const int nl = a_side ? NLA : (LB / 4 + ((wave & 3) < LB % 4 ? 1 : 0));
+  const bool stream_w = tiles_m <= kStreamWeightsMaxRowTiles;
   const uint16_t* gsrc[NLS];
   int ldst[NLS];
 #pragma unroll
@@ -598,7 +603,7 @@ __global__ __launch_bounds__(TL::THREADS) void gemm_sub_kernel(GemmArgs g) {
     uint16_t* _st = lds + ((KT) & 1) * SE;                                                           \
     _Pragma("unroll") for (int i = 0; i < NLS; ++i)                                                  \
       if (i < nl) {                                                                                  \
-        if (a_side)                                                                                  \
+        if (a_side || !stream_w)                                                                     \
           __builtin_amdgcn_global_load_lds((const void*)(gsrc[i] + (size_t)(KT) * BK),               \
                                            (lds_ptr_t)(_st + ldst[i]), 16, 0, 0);                    \
         else                                                                                         \
@@ -750,6 +755,7 @@ __global__ __launch_bounds__(TL::THREADS) void gemm_spec_kernel(GemmArgs g) {
     // [RPL q, RPL q + RPL) of the stage image (A rows, then weight rows), lane
     // l at row RPL q + l / CPR, swizzled chunk (l % CPR) ^ f(row)
     const int p = wave - TL::CONSUMERS;
+    const bool stream_w = tiles_m <= kStreamWeightsMaxRowTiles;
     const uint16_t* gsrc[NL];
     int ldst[NL];
 #pragma unroll
@@ -766,7 +772,7 @@ __global__ __launch_bounds__(TL::THREADS) void gemm_spec_kernel(GemmArgs g) {
       uint16_t* st = lds + (kt % NST) * SE;
 #pragma unroll
       for (int i = 0; i < NL; ++i) {   // loads i < (BM / RPL) / PRODUCERS are A rows
-        if (i < (BM / RPL) / TL::PRODUCERS)
+        if (i < (BM / RPL) / TL::PRODUCERS || !stream_w)
           __builtin_amdgcn_global_load_lds((const void*)(gsrc[i] + (size_t)kt * BK), (lds_ptr_t)(st + ldst[i]), 16, 0,
                                            0);
         else
