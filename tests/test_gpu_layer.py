@@ -278,7 +278,7 @@ def test_full_size_mistral_tau512():
     _full_size(W.mistral_tau512(0), 64)
 
 
-@pytest.mark.parametrize("case", ["yi_T512", "mistral_T2048", "mistral_T200", "mistral_T700"])
+@pytest.mark.parametrize("case", ["yi_T512", "mistral_T2048", "mistral_T200", "mistral_T700", "yi_T256"])
 def test_full_size_other_gemm_plans(case):
     """Token counts whose GEMM tile / K-split plans the two named
     configurations do not reach (plans as the planner picks them):
@@ -288,12 +288,16 @@ def test_full_size_other_gemm_plans(case):
     RoPE/append epilogue in the sub-step kernel, O, gate/up and down on the
     specialised kernel without a split); Mistral at T = 200 (128-row tiles
     with 2- and 4-way splits); Mistral at T = 700 (all four projections on
-    the specialised kernel with a ragged last row tile of 188 tokens)."""
+    the specialised kernel with a ragged last row tile of 188 tokens); Yi at
+    T = 256 (QKV on the specialised kernel with a 2-way split, so its
+    partials go through the QKV reduce that applies RoPE and the KV append;
+    O and down on it with 4-way splits, gate/up on 256x256)."""
     dims, cl, cp, n_dec = {
         "yi_T512": (W.YI, [448], [1000], 64),
         "mistral_T2048": (W.MISTRAL, [2000], [300], 48),
         "mistral_T200": (W.MISTRAL, [184], [700], 16),
         "mistral_T700": (W.MISTRAL, [660], [900], 40),
+        "yi_T256": (W.YI, [224], [800], 32),
     }[case]
     rng = np.random.default_rng(11)
     ctx = rng.integers(1, 1500, size=n_dec).astype(np.int32)
