@@ -62,6 +62,23 @@ __device__ __forceinline__ void split_p(const float* p, bf16x8& hi, bf16x8& lo) 
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Four consecutive output dims starting at element oi of the [T][n_q * d]
+// attention output: (v0..v3) * inv as bf16, or as FP8 codes of that over the
+// O projection's input scale.  The merge writes its outputs the same way, so a
+// token written straight from its one attention item gets the arithmetic of a
+// one-partial merge.
+__device__ __forceinline__ void store_out4(const AttnArgs& a, size_t oi, float v0, float v1, float v2, float v3,
+                                           float inv) {
+  if (a.out_inv_scale > 0.0f) {
+    const float q = a.out_inv_scale;
+    *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(a.out) + oi) =
+        pack4fp8(v0 * inv * q, v1 * inv * q, v2 * inv * q, v3 * inv * q);
+  } else {
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + oi) =
+        make_uint2(pack2bf(v0 * inv, v1 * inv), pack2bf(v2 * inv, v3 * inv));
+  }
+}
+
 // ----------------------------------------------------------------------------
 // decode items
 //
@@ -232,16 +249,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
   l += __shfl_xor(l, 32, 64);
   if (r < g) {
     const int head = kvh * g + r;
-    const size_t pidx = (size_t)a.meta.part_off[t] + it.split;
-    float* po = a.part_o + (pidx * nq + head) * D;
     const float vsc = F8 ? a.v_scale : 1.0f;
+    if (it.n_split == 1) {
+      // the whole context in one item: normalise and write the output
+      const float inv = 1.0f / l;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      *reinterpret_cast<float4*>(po + j * 16 + qd * 4) =
-          make_float4(acc[j][0] * vsc, acc[j][1] * vsc, acc[j][2] * vsc, acc[j][3] * vsc);
-    if (qd == 0) {
-      a.part_ml[(pidx * nq + head) * 2 + 0] = m;
-      a.part_ml[(pidx * nq + head) * 2 + 1] = l;
+      for (int j = 0; j < NJ; ++j)
+        store_out4(a, ((size_t)t * nq + head) * D + j * 16 + qd * 4, acc[j][0] * vsc, acc[j][1] * vsc,
+                   acc[j][2] * vsc, acc[j][3] * vsc, inv);
+    } else {
+      const size_t pidx = (size_t)a.meta.part_off[t] + it.split;
+      float* po = a.part_o + (pidx * nq + head) * D;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        *reinterpret_cast<float4*>(po + j * 16 + qd * 4) =
+            make_float4(acc[j][0] * vsc, acc[j][1] * vsc, acc[j][2] * vsc, acc[j][3] * vsc);
+      if (qd == 0) {
+        a.part_ml[(pidx * nq + head) * 2 + 0] = m;
+        a.part_ml[(pidx * nq + head) * 2 + 1] = l;
+      }
     }
   }
 }
@@ -560,20 +586,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   l += __shfl_xor(l, 32, 64);
   if (valid) {
     const int head = kvh * g + hq;
-    const size_t pidx = (size_t)a.meta.part_off[t] + it.split;
-    float* po = a.part_o + (pidx * nq + head) * D + 4 * hh;
     const float vsc = F8 ? a.v_scale : 1.0f;
     // acc[db][v] is dim 32 db + 8 (v >> 2) + 4 hh + (v & 3)
+    if (it.n_split == 1) {
+      // all of the tile's keys in one item: normalise and write the output
+      const float inv = 1.0f / l;
+      const size_t ob = ((size_t)t * nq + head) * D + 4 * hh;
 #pragma unroll
-    for (int db = 0; db < NS; ++db)
+      for (int db = 0; db < NS; ++db)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<float4*>(po + 32 * db + 8 * j) =
-            make_float4(acc[db][4 * j] * vsc, acc[db][4 * j + 1] * vsc, acc[db][4 * j + 2] * vsc,
-                        acc[db][4 * j + 3] * vsc);
-    if (hh == 0) {
-      a.part_ml[(pidx * nq + head) * 2 + 0] = m;
-      a.part_ml[(pidx * nq + head) * 2 + 1] = l;
+        for (int j = 0; j < 4; ++j)
+          store_out4(a, ob + 32 * db + 8 * j, acc[db][4 * j] * vsc, acc[db][4 * j + 1] * vsc,
+                     acc[db][4 * j + 2] * vsc, acc[db][4 * j + 3] * vsc, inv);
+    } else {
+      const size_t pidx = (size_t)a.meta.part_off[t] + it.split;
+      float* po = a.part_o + (pidx * nq + head) * D + 4 * hh;
+#pragma unroll
+      for (int db = 0; db < NS; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<float4*>(po + 32 * db + 8 * j) =
+              make_float4(acc[db][4 * j] * vsc, acc[db][4 * j + 1] * vsc, acc[db][4 * j + 2] * vsc,
+                          acc[db][4 * j + 3] * vsc);
+      if (hh == 0) {
+        a.part_ml[(pidx * nq + head) * 2 + 0] = m;
+        a.part_ml[(pidx * nq + head) * 2 + 1] = l;
+      }
     }
   }
 }
@@ -594,6 +632,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   if (wid >= (int64_t)a.n_tokens * nq) return;
   const int t = (int)(wid / nq), h = (int)(wid % nq);
   const int p0 = a.meta.part_off[t], pc = a.meta.part_cnt[t];
+  if (pc <= 1) return;   // written by its one attention item
   const float2* ml = reinterpret_cast<const float2*>(a.part_ml) + (size_t)p0 * nq + h;
   const float* src = a.part_o + ((size_t)p0 * nq + h) * D + l4 * 4;
   float M = -INFINITY, L = 0.f;
@@ -629,18 +668,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
       M = mn;
     }
   }
-  const float inv = 1.0f / L;
-  const size_t oi = (size_t)t * nq * D + (size_t)h * D + l4 * 4;
-  if (a.out_inv_scale > 0.0f) {   // FP8 codes of o / o_scale (the O projection's input)
-    const float q = a.out_inv_scale;
-    *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(a.out) + oi) =
-        pack4fp8(o.x * inv * q, o.y * inv * q, o.z * inv * q, o.w * inv * q);
-  } else {
-    uint2 pk;
-    pk.x = pack2bf(o.x * inv, o.y * inv);
-    pk.y = pack2bf(o.z * inv, o.w * inv);
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + oi) = pk;
-  }
+  // FP8: codes of o / o_scale (the O projection's input)
+  store_out4(a, (size_t)t * nq * D + (size_t)h * D + l4 * 4, o.x, o.y, o.z, o.w, 1.0f / L);
 }
 
 template <int D, bool F8>
@@ -648,7 +677,7 @@ static hb_status launch_attention_d(const AttnArgs& a, stream_t s, void* const* 
   // FP8: keys are code * k_scale, so k_scale joins the score scale
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D) * (F8 ? a.k_scale : 1.0f);
   hipStream_t st = (hipStream_t)s;
-  auto mark = [&](int i) -> bool { return !ev || hipEventRecord((hipEvent_t)ev[i], st) == hipSuccess; };
+  auto mark = [&](int i) -> bool { return !ev || !ev[i] || hipEventRecord((hipEvent_t)ev[i], st) == hipSuccess; };
   if (!mark(0)) return fail(HB_E_HIP, "attention: stage event record failed");
   if (a.n_chunk_items > 0)
     hipLaunchKernelGGL((attn_chunk_kernel<D, F8>), dim3((unsigned)a.n_chunk_items * a.n_kv_heads), dim3(256), 0, st, a,
@@ -659,8 +688,9 @@ static hb_status launch_attention_d(const AttnArgs& a, stream_t s, void* const* 
                        scale_log2);
   if (!mark(2)) return fail(HB_E_HIP, "attention: stage event record failed");
   const int64_t pairs = (int64_t)a.n_tokens * a.n_q_heads, per_block = 256 / (D / 4);
-  hipLaunchKernelGGL(attn_merge_kernel<D>, dim3((unsigned)((pairs + per_block - 1) / per_block)), dim3(256), 0, st,
-                     a);
+  if (a.n_merge_tokens > 0)
+    hipLaunchKernelGGL(attn_merge_kernel<D>, dim3((unsigned)((pairs + per_block - 1) / per_block)), dim3(256), 0, st,
+                       a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(HB_E_HIP, std::string("attention launch: ") + hipGetErrorString(e));
   return HB_OK;

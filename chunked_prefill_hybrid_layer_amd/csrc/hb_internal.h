@@ -14,14 +14,14 @@ namespace hb {
 // --- attention tiling (fixed by the kernels; recorded in the metadata) -----
 constexpr int kChunkRows = 128;       // (token, head) rows per chunk attention tile
 constexpr int kChunkKeyTile = 64;     // keys staged per step (4 pages of 16)
-constexpr int kChunkKvSplit = 1024;   // keys per chunk attention item, at least (multiple of 64)
-constexpr int kChunkItemsTarget = 2048;  // chunk items beyond which the key split doubles
+constexpr int kChunkMinKeys = 768;    // keys per chunk attention item at least, where a tile is split
+constexpr int kChunkWgTarget = 1024;  // chunk workgroups (items x kv heads) the key split aims at
 constexpr int kDecodeKeyStep = 32;    // keys per decode step (2 pages)
 constexpr int kDecodeKvSplit = 256;   // keys per decode attention item, at least (multiple of 32)
 constexpr int kDecodeKvSplitMax = 1024;  // at most: the decode kernel holds an item's page ids one per lane
 constexpr int kDecodeWavesTarget = 16384;  // decode items x kv heads beyond which the decode split doubles
 constexpr int kPageSize = 16;
-constexpr uint32_t kMetaVersion = 2;
+constexpr uint32_t kMetaVersion = 3;
 constexpr int kMaxGroup = 16;         // decode path holds a kv group in one 16-row MFMA tile
 
 // --- GEMM -------------------------------------------------------------------
@@ -140,13 +140,15 @@ struct AttnArgs {
   int max_pages;
   int n_q_heads, n_kv_heads, head_dim, group;
   int n_chunk_items, n_decode_items, n_tokens;
+  int n_merge_tokens;      // tokens with more than one partial (0: no merge pass)
   float* part_o;           // [n_partials][n_q][d]
   float* part_ml;          // [n_partials][n_q][2]
   void* out;               // [T][n_q * d] bf16, or FP8 codes of o * out_inv_scale (> 0)
   float out_inv_scale;
 };
-// Attention in three launches (chunk items, decode items, merge); ev, if not
-// NULL, holds the events to record before each launch (3 entries).
+// Attention in up to three launches (chunk items, decode items, merge of the
+// tokens with more than one partial); ev, if not NULL, holds the events to
+// record before each launch (3 entries).
 hb_status launch_attention(const AttnArgs& a, stream_t s, void* const* ev);
 
 }  // namespace hb

@@ -89,7 +89,7 @@ extern "C" hb_status hb_layer_forward(const hb_dims* dims, const hb_weights* w, 
   const stream_t s = (stream_t)stream;
   // optional per-stage timing events (see HB_STAGE_NAMES)
   auto mark = [&](int i) -> hb_status {
-    if (stage_events && hipEventRecord((hipEvent_t)stage_events[i], (hipStream_t)stream) != hipSuccess)
+    if (stage_events && stage_events[i] && hipEventRecord((hipEvent_t)stage_events[i], (hipStream_t)stream) != hipSuccess)
       return fail(HB_E_HIP, "layer_forward: stage event record failed");
     return HB_OK;
   };
@@ -159,6 +159,7 @@ extern "C" hb_status hb_layer_forward(const hb_dims* dims, const hb_weights* w, 
   at.n_chunk_items = h->n_chunk_items;
   at.n_decode_items = h->n_decode_items;
   at.n_tokens = T;
+  at.n_merge_tokens = h->n_merge_tokens;
   at.part_o = (float*)(ws + L.part_o);
   at.part_ml = (float*)(ws + L.part_ml);
   at.out = ob;
@@ -185,13 +186,17 @@ extern "C" hb_status hb_layer_forward(const hb_dims* dims, const hb_weights* w, 
   go.out_f = h1;
   go.ldo = H;
   go.part = gpart;
+  // Stage events: a split O's reduce (which adds the residual) belongs to the
+  // O stage, as down's reduce belongs to the down stage; it also applies the
+  // FFN RMSNorm, whose own stage is then empty.
   HB_TRY(mark(5));
   HB_TRY(launch_gemm(go, s));
-  HB_TRY(mark(6));
   const float h_inv = f8 ? 1.0f / dims->h_scale : 0.0f;
   if (po.splits > 1) {
     HB_TRY(launch_splitk_reduce(gpart, po.splits, x, h1, T, H, w->g_ffn, h1n, dims->rms_eps, s, h_inv));
+    HB_TRY(mark(6));
   } else {
+    HB_TRY(mark(6));
     HB_TRY(launch_rmsnorm(h1, w->g_ffn, h1n, T, H, dims->rms_eps, s, h_inv));
   }
 

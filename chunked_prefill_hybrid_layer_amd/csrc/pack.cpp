@@ -127,7 +127,7 @@ size_t hb_meta_bytes(const hb_dims* dims, int32_t n_seq, int32_t n_tokens, int32
   size_t max_keys = P * kPageSize;
   int qt = chunk_q_tile(dims->n_q_heads / dims->n_kv_heads);
   size_t tiles = T / qt + S;                                     // chunk tiles (>= 1 token each)
-  size_t csplit = (max_keys + kChunkKvSplit - 1) / kChunkKvSplit;
+  size_t csplit = (max_keys + kChunkMinKeys - 1) / kChunkMinKeys + 1;
   size_t dsplit = (max_keys + kDecodeKvSplit - 1) / kDecodeKvSplit;
   size_t items = tiles * csplit + S * dsplit;
   size_t runs = T + S;                                           // a run per page a sequence touches
@@ -208,46 +208,62 @@ hb_status hb_pack_metadata(const hb_dims* dims, int32_t n_chunks, const int32_t*
       q_start[s + 1] = q_start[s] + newtok[s];
       kv_len[s] = cached[s] + newtok[s];
     }
-    // Keys per chunk item: kChunkKvSplit, doubled while the chunk tiles' keys
-    // would still make more than kChunkItemsTarget items, so that a long
-    // prompt does not multiply its partial results (and their merge).
-    int64_t chunk_keys = 0;
+    // Chunk items.  The keys [0, key_end) of a chunk query tile are cut into
+    // n runs of whole 64-key tiles, as equal as whole tiles allow (the last
+    // run ends at key_end), n = ceil(tiles / per).  per, the 64-key tiles an
+    // item takes at most, is the smallest that keeps the workgroups (items x
+    // kv heads) near kChunkWgTarget -- two rounds of the two workgroups each
+    // CU holds at a time -- and at least kChunkMinKeys / 64: more items buy
+    // no parallelism, only partial results to write and merge.  A tile that
+    // stays whole (n = 1) writes its output directly.
+    const int64_t nkv = dims->n_kv_heads;
+    int64_t chunk_steps = 0;
     for (int s = 0; s < n_chunks; ++s)
       for (int t0 = q_start[s]; t0 < q_start[s + 1]; t0 += qt)
-        chunk_keys += cached[s] + (t0 - q_start[s]) + std::min(qt, q_start[s + 1] - t0);
-    int csplit = kChunkKvSplit;
-    while ((int64_t)csplit * kChunkItemsTarget < chunk_keys && csplit < (1 << 20)) csplit *= 2;
+        chunk_steps += (cached[s] + (t0 - q_start[s]) + std::min(qt, q_start[s + 1] - t0) + 63) / 64;
+    const int64_t per = std::max<int64_t>(kChunkMinKeys / 64, (chunk_steps * nkv + kChunkWgTarget - 1) / kChunkWgTarget);
+    const int csplit = (int)std::min<int64_t>(per * 64, 1 << 30);
     std::vector<int32_t> part_off((size_t)T), part_cnt((size_t)T);
     std::vector<hb_attn_item> citems, ditems;
-    int64_t np = 0;
+    int64_t np = 0, n_merge = 0;
     for (int s = 0; s < n_chunks; ++s) {
       for (int t0 = q_start[s]; t0 < q_start[s + 1]; t0 += qt) {
         int n = std::min(qt, q_start[s + 1] - t0);
         int key_end = cached[s] + (t0 - q_start[s]) + n;  // last token's position + 1
-        int nsplit = (key_end + csplit - 1) / csplit;
+        const int64_t steps = (key_end + 63) / 64;
+        const int nsplit = (int)((steps + per - 1) / per);
         for (int j = 0; j < nsplit; ++j) {
           hb_attn_item it{};
           it.seq = s;
           it.tok0 = t0;
           it.n_tok = n;
-          it.key0 = j * csplit;
-          it.key1 = std::min(key_end, (j + 1) * csplit);
+          it.key0 = (int)(64 * (steps * j / nsplit));
+          it.key1 = std::min<int64_t>(key_end, 64 * (steps * (j + 1) / nsplit));
           it.split = j;
+          it.n_split = nsplit;
           citems.push_back(it);
         }
         for (int t = t0; t < t0 + n; ++t) {
-          part_off[t] = (int32_t)np;
           part_cnt[t] = nsplit;
-          np += nsplit;
+          part_off[t] = nsplit > 1 ? (int32_t)np : -1;
+          if (nsplit > 1) {
+            np += nsplit;
+            ++n_merge;
+          }
         }
       }
     }
-    // Longest key ranges first (chunk and decode lists alike): the kernels
-    // take items in list order, so the long ones start early and the short
-    // ones fill in behind them.  The output does not depend on the order
-    // (partials are indexed by split).
+    // Item order (the kernels take items in list order; the output does not
+    // depend on it, partials are indexed by split).  Longest key ranges
+    // first, so the long ones start early and the short ones fill in behind
+    // them -- compared in 256-key buckets, and within a bucket split-major:
+    // the items of the chunks' tiles that cover about the same key range run
+    // next to each other and share those keys' K/V in L2.
     std::stable_sort(citems.begin(), citems.end(), [](const hb_attn_item& x, const hb_attn_item& y) {
-      return x.key1 - x.key0 > y.key1 - y.key0;
+      return x.split < y.split;
+    });
+    std::stable_sort(citems.begin(), citems.end(), [](const hb_attn_item& x, const hb_attn_item& y) {
+      return (x.key1 - x.key0) / 256 > (y.key1 - y.key0) / 256;
     });
     // Keys per decode item: kDecodeKvSplit, doubled (up to kDecodeKvSplitMax)
     // while a large decode batch would still make more than
@@ -271,11 +287,15 @@ hb_status hb_pack_metadata(const hb_dims* dims, int32_t n_chunks, const int32_t*
         it.key0 = j * dsplit;
         it.key1 = std::min(kv_len[s], (j + 1) * dsplit);
         it.split = j;
+        it.n_split = nsplit;
         ditems.push_back(it);
       }
-      part_off[t] = (int32_t)np;
       part_cnt[t] = nsplit;
-      np += nsplit;
+      part_off[t] = nsplit > 1 ? (int32_t)np : -1;
+      if (nsplit > 1) {
+        np += nsplit;
+        ++n_merge;
+      }
     }
     std::stable_sort(ditems.begin(), ditems.end(), [](const hb_attn_item& x, const hb_attn_item& y) {
       return x.key1 - x.key0 > y.key1 - y.key0;
@@ -327,6 +347,7 @@ hb_status hb_pack_metadata(const hb_dims* dims, int32_t n_chunks, const int32_t*
     h.n_decode_items = (int32_t)ditems.size();
     h.n_partials = (int32_t)np;
     h.n_append_runs = (int32_t)runs.size();
+    h.n_merge_tokens = (int32_t)n_merge;
     h.off_q_start = take((S + 1) * 4);
     h.off_cached = take(S * 4);
     h.off_kv_len = take(S * 4);
@@ -440,6 +461,23 @@ size_t hb_workspace_bytes(const hb_dims* dims, const void* meta_host) {
   if (check_dims(dims) != HB_OK || check_meta(dims, meta_host) != HB_OK) return 0;
   const hb_meta_header* h = (const hb_meta_header*)meta_host;
   return ws_layout(*dims, h->n_tokens, h->n_partials).total;
+}
+
+hb_status hb_workspace_views_of(const hb_dims* dims, const void* meta_host, hb_workspace_views* out) {
+  if (!out) return fail(HB_E_NULL, "workspace_views: NULL out");
+  hb_status st = check_dims(dims);
+  if (st != HB_OK) return st;
+  st = check_meta(dims, meta_host);
+  if (st != HB_OK) return st;
+  const hb_meta_header* h = (const hb_meta_header*)meta_host;
+  const WsLayout L = ws_layout(*dims, h->n_tokens, h->n_partials);
+  out->xn = (int64_t)L.xn;
+  out->q = (int64_t)L.q;
+  out->o = (int64_t)L.o;
+  out->h1 = (int64_t)L.h1;
+  out->h1n = (int64_t)L.h1n;
+  out->act = (int64_t)L.act;
+  return HB_OK;
 }
 
 }  // extern "C"

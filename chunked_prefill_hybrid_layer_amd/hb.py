@@ -53,7 +53,7 @@ class Weights(ctypes.Structure):
 
 class AttnItem(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("seq", "tok0", "n_tok", "key0", "key1", "split", "reserved0", "reserved1")]
+                ("seq", "tok0", "n_tok", "key0", "key1", "split", "n_split", "reserved")]
 
 
 class MetaHeader(ctypes.Structure):
@@ -62,7 +62,7 @@ class MetaHeader(ctypes.Structure):
                  ("n_seq", "n_chunks", "n_decodes", "n_tokens", "page_size", "max_pages", "num_pages",
                   "max_kv_len", "n_kv_heads", "group", "head_dim", "n_q_heads", "chunk_q_tile",
                   "chunk_kv_split", "decode_kv_split", "n_chunk_items", "n_decode_items", "n_partials",
-                  "n_append_runs", "reserved")] +
+                  "n_append_runs", "n_merge_tokens")] +
                 [("bytes", ctypes.c_int64)] +
                 [(n, ctypes.c_int64) for n in
                  ("off_q_start", "off_cached", "off_kv_len", "off_tok_seq", "off_tok_pos", "off_slot",
@@ -70,12 +70,16 @@ class MetaHeader(ctypes.Structure):
                   "off_append_runs")])
 
 
+class WorkspaceViews(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("xn", "q", "o", "h1", "h1n", "act")]
+
+
 class Request(ctypes.Structure):
     _fields_ = [("prompt_len", ctypes.c_int32), ("cached", ctypes.c_int32)]
 
 
 EXPORTS = ["hb_meta_bytes", "hb_pack_metadata", "hb_schedule_iteration", "hb_rope_table", "hb_workspace_bytes",
-           "hb_kv_append", "hb_layer_forward", "hb_status_str", "hb_last_error_detail"]
+           "hb_workspace_views_of", "hb_kv_append", "hb_layer_forward", "hb_status_str", "hb_last_error_detail"]
 
 
 def _load() -> ctypes.CDLL:
@@ -97,6 +101,8 @@ def _load() -> ctypes.CDLL:
     lib.hb_rope_table.restype = ctypes.c_int
     lib.hb_workspace_bytes.argtypes = [ctypes.POINTER(Dims), P]
     lib.hb_workspace_bytes.restype = SZ
+    lib.hb_workspace_views_of.argtypes = [ctypes.POINTER(Dims), P, ctypes.POINTER(WorkspaceViews)]
+    lib.hb_workspace_views_of.restype = ctypes.c_int
     lib.hb_kv_append.argtypes = [ctypes.POINTER(Dims), P, P, P, P, I64, P, P, P]
     lib.hb_kv_append.restype = ctypes.c_int
     lib.hb_layer_forward.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Weights), P, P, P, I32, P, P, P, P,
@@ -224,6 +230,13 @@ def workspace_bytes(dims: Dims, blob: np.ndarray) -> int:
     return n
 
 
+def workspace_views(dims: Dims, blob: np.ndarray) -> dict:
+    """Byte offsets of the stored activations (xn, q, o, h1, h1n, act) in the workspace."""
+    v = WorkspaceViews()
+    _check(lib.hb_workspace_views_of(ctypes.byref(dims), blob.ctypes.data_as(ctypes.c_void_p), ctypes.byref(v)))
+    return {n: int(getattr(v, n)) for n, _ in WorkspaceViews._fields_}
+
+
 def kv_append(dims: Dims, blob: np.ndarray, meta_dev: int, k: int, v: int, row_stride: int,
               k_cache: int, v_cache: int, stream: int = 0):
     _check(lib.hb_kv_append(ctypes.byref(dims), blob.ctypes.data_as(ctypes.c_void_p), meta_dev, k, v,
@@ -286,8 +299,9 @@ class Forward:
         _check(lib.hb_layer_forward(*self.args, events))
 
 
-def make_events(handles: Sequence[int]):
-    """ctypes array of NUM_STAGES + 1 hipEvent_t handles for Forward.__call__."""
+def make_events(handles: Sequence[Optional[int]]):
+    """ctypes array of NUM_STAGES + 1 hipEvent_t handles for Forward.__call__
+    (None entries are not recorded)."""
     if len(handles) != NUM_STAGES + 1:
         raise ValueError(f"need {NUM_STAGES + 1} stage events")
     return (ctypes.c_void_p * len(handles))(*handles)

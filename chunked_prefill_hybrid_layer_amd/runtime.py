@@ -130,6 +130,29 @@ class DeviceLayer:
         torch.cuda.synchronize()
 
     # -- views for checking ---------------------------------------------------
+    def stored(self, prep: Prepared) -> dict:
+        """The activations the last forward of ``prep`` stored between its
+        steps (hb_workspace_views_of), copied to the host: xn, o, h1n, act as
+        bf16 bits (uint16), or with FP8 projections as e4m3 codes (uint8); q as
+        bf16 bits; h1 as float32.  Rows in packed-token order."""
+        d, T = self.dims, prep.n_tokens
+        offs = hb.workspace_views(self.hd, prep.blob)
+        f8 = bool(getattr(d, "w8a8", 0))
+        width = {"xn": d.hidden, "q": d.n_q_heads * d.head_dim, "o": d.n_q_heads * d.head_dim,
+                 "h1": d.hidden, "h1n": d.hidden, "act": d.ffn_dim}
+        out = {}
+        for name, n in width.items():
+            if name == "h1":
+                dt, nb = torch.float32, 4
+            elif name != "q" and f8:
+                dt, nb = torch.uint8, 1
+            else:
+                dt, nb = torch.int16, 2
+            raw = self.ws[offs[name]:offs[name] + T * n * nb]
+            a = raw.view(dt).reshape(T, n).cpu().numpy()
+            out[name] = a.view(np.uint16) if dt == torch.int16 else a
+        return out
+
     def cache_logical(self):
         """(K, V) in logical order [page][kv][slot][d]: bf16 bits as uint16, or
         FP8 e4m3 codes as uint8."""

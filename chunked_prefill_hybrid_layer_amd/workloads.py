@@ -226,10 +226,13 @@ def make_weights_fp8(dims: Dims, seed: np.random.SeedSequence, rms: float = 0.02
     return w
 
 
-# static projection-input scales of the synthetic FP8 workloads (powers of two:
-# N(0, 1)-sized xn and h1n, attention outputs within +-4, SwiGLU outputs within
-# +-50, all well inside e4m3's +-448 over the scale)
-FP8_ACT_SCALES = dict(x_scale=2.0 ** -4, o_scale=2.0 ** -5, h_scale=2.0 ** -4, a_scale=2.0 ** -3)
+# static projection-input scales of the synthetic FP8 workloads: N(0, 1)-sized
+# xn and h1n, attention outputs within +-4, SwiGLU outputs within +-50, all
+# inside e4m3's +-448 over the scale.  Distinct, none a power of two and no
+# ratio of two of them a power of two: e4m3 has a floating exponent, so a
+# value quantised and read back with a scale 2^k times the right one lands on
+# the same grid, and a swap of two such scales would be invisible
+FP8_ACT_SCALES = dict(x_scale=0.07, o_scale=0.03, h_scale=0.05, a_scale=0.13)
 
 
 def make_activations(n_tokens: int, hidden: int, rng: np.random.Generator, std: float) -> np.ndarray:

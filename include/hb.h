@@ -136,7 +136,9 @@ typedef struct {
   int32_t key0;     /* keys [key0, key1) of the sequence handled by this item */
   int32_t key1;
   int32_t split;    /* index of this key range among the tile's ranges */
-  int32_t reserved0, reserved1;
+  int32_t n_split;  /* number of key ranges of the tile (1: the item writes the
+                       attention output itself, no partial result) */
+  int32_t reserved;
 } hb_attn_item;
 
 /* A run of consecutive packed tokens of one sequence whose K/V land in one
@@ -158,12 +160,13 @@ typedef struct {
   int32_t max_kv_len;               /* max over sequences of cached + new */
   int32_t n_kv_heads, group, head_dim, n_q_heads;   /* dims the work lists were built for */
   int32_t chunk_q_tile;             /* tokens per chunk attention tile */
-  int32_t chunk_kv_split;           /* keys per chunk attention item */
+  int32_t chunk_kv_split;           /* keys per chunk attention item, at most */
   int32_t decode_kv_split;          /* keys per decode attention item */
   int32_t n_chunk_items, n_decode_items;
-  int32_t n_partials;               /* attention partial results (sum of part_cnt) */
+  int32_t n_partials;               /* attention partial results (part_cnt summed over the
+                                       tokens with more than one) */
   int32_t n_append_runs;            /* KV append runs (hb_append_run) */
-  int32_t reserved;
+  int32_t n_merge_tokens;           /* tokens whose attention has more than one partial */
   int64_t bytes;                    /* size of the whole blob */
   /* byte offsets from the start of the blob */
   int64_t off_q_start;     /* int32 [n_seq + 1]  first packed token of each sequence */
@@ -172,8 +175,9 @@ typedef struct {
   int64_t off_tok_seq;     /* int32 [n_tokens]   sequence of each token */
   int64_t off_tok_pos;     /* int32 [n_tokens]   position of each token in its sequence */
   int64_t off_slot;        /* int32 [n_tokens]   page * page_size + in-page slot */
-  int64_t off_part_off;    /* int32 [n_tokens]   first attention partial of each token */
-  int64_t off_part_cnt;    /* int32 [n_tokens]   number of attention partials of each token */
+  int64_t off_part_off;    /* int32 [n_tokens]   first attention partial of each token (-1: none) */
+  int64_t off_part_cnt;    /* int32 [n_tokens]   key ranges of each token's attention (1: its
+                              item writes the output directly, no partial) */
   int64_t off_block_table; /* int32 [n_seq][max_pages] copy of the caller's tables */
   int64_t off_chunk_items; /* hb_attn_item [n_chunk_items] */
   int64_t off_decode_items;/* hb_attn_item [n_decode_items] */
@@ -188,6 +192,15 @@ size_t hb_meta_bytes(const hb_dims *dims, int32_t n_seq, int32_t n_tokens,
 
 /* Validate one hybrid batch and build its packed-token metadata (host only;
  * makes no HIP call).
+ *
+ * The batch is the stall-free hybrid batch of the "Sarathi-Serve reading
+ * notes" §3.2: one token for each running decode plus prefill chunk pieces,
+ * together at most the token budget tau.  A chunk piece continues its
+ * prompt: the i-th chunk of size C covers prompt positions [(i-1)C, iC), and
+ * the (i-1)C tokens before it are already cached (§3.1; here any prefix
+ * length).  K/V live in fixed-size pages reached through per-sequence block
+ * tables (§3.5 paged KV; "Chunked Prefill", mechanism: each chunk's K/V go
+ * into the blocks the next chunk reads).
  *
  *   chunk_len[n_chunks], chunk_prefix_len[n_chunks]: new tokens and
  *     already-cached prefix of each chunk piece (chunk_len >= 1, prefix >= 0).
@@ -251,6 +264,28 @@ hb_status hb_rope_table(const hb_dims *dims, int32_t max_pos, float *host_out);
  * meta_host; 0 on bad arguments. */
 size_t hb_workspace_bytes(const hb_dims *dims, const void *meta_host);
 
+/* Where hb_layer_forward leaves the activations it stores between the layer's
+ * steps (the precision contract of the layer: each of these is what the next
+ * step reads), as byte offsets into the workspace.  T = the batch's packed
+ * tokens, rows in packed-token order:
+ *   xn   [T][hidden]  normed input (into QKV)
+ *   q    [T][n_q*d]   queries after RoPE, bf16, natural dim order
+ *   o    [T][n_q*d]   attention output (into O)
+ *   h1   [T][hidden]  x + o W_o^T, fp32
+ *   h1n  [T][hidden]  normed residual (into gate/up)
+ *   act  [T][ffn]     SwiGLU output (into down)
+ * xn, o, h1n and act are bf16, or with dims->w8a8 one-byte e4m3 codes of
+ * value / (x_scale, o_scale, h_scale, a_scale) with rows that many bytes
+ * apart.  The contents are valid once the forward has completed on its
+ * stream and until the workspace is used again.  For checking and debugging;
+ * nothing else reads them.  Errors as hb_workspace_bytes (HB_E_NULL for a
+ * NULL out). */
+typedef struct {
+  int64_t xn, q, o, h1, h1n, act;
+} hb_workspace_views;
+
+hb_status hb_workspace_views_of(const hb_dims *dims, const void *meta_host, hb_workspace_views *out);
+
 /* KV append ("Chunked Prefill", mechanism: each chunk writes its KV into the
  * paged blocks): for every packed token t, k[t] and v[t] ([n_kv][head_dim]
  * bf16, consecutive tokens `row_stride` elements apart) go to slot[t] of the
@@ -261,7 +296,15 @@ hb_status hb_kv_append(const hb_dims *dims, const void *meta_host, const void *m
                        const uint16_t *k, const uint16_t *v, int64_t row_stride,
                        void *k_cache, void *v_cache, void *stream);
 
-/* One decoder-layer forward over the hybrid batch (device):
+/* One decoder-layer forward over the hybrid batch (device): one layer of
+ * the iteration the "Sarathi-Serve reading notes" schedule in §3.4 (the whole
+ * batch passes through the model once), with every token of the batch in the
+ * same linear layers (§1.6: their cost depends on the token count, not on
+ * which request a token belongs to; "Chunked Prefill", hybrid-iteration
+ * roofline) and each token attending to its own sequence only: a chunk token
+ * at position p sees keys 0..p of its prompt, the cached prefix plus its own
+ * chunk causally (§3.1, §7.5b: query i of chunk k sees (k-1)C + i keys), a
+ * decode sees its whole context plus itself (§3.2).  Steps:
  *   xn  = RMSNorm(x) * g_attn                                  (bf16)
  *   q,k,v = xn W_q^T, xn W_k^T, xn W_v^T; RoPE(q, k) by position (bf16)
  *   k, v appended to the cache at the tokens' slots
@@ -279,8 +322,13 @@ hb_status hb_kv_append(const hb_dims *dims, const void *meta_host, const void *m
  * stage_events: NULL, or HB_NUM_STAGES + 1 caller-created hipEvent_t handles;
  * event i is recorded on `stream` right before stage i is launched and event
  * HB_NUM_STAGES after the last stage, so elapsed(event i, event i+1) is the
- * device time of stage i.  A failing event record returns HB_E_HIP (the
- * stages enqueued before it stay enqueued).  Stages, in launch order: */
+ * device time of stage i.  A NULL handle is skipped (each recorded event
+ * leaves a gap of a few microseconds between two kernels, so a caller timing
+ * one stage passes only its two events).  A failing event record returns HB_E_HIP (the
+ * stages enqueued before it stay enqueued).  Where a split O projection's
+ * reduce also applies the FFN RMSNorm, that reduce is timed with the O stage
+ * and the rmsnorm_ffn stage is empty; the merge stage is empty when no token
+ * has more than one attention partial.  Stages, in launch order: */
 #define HB_NUM_STAGES 9
 #define HB_STAGE_NAMES                                                              \
   { "rmsnorm_attn", "qkv_rope_append", "attn_chunk", "attn_decode", "attn_merge", \

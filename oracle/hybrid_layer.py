@@ -70,7 +70,7 @@ from __future__ import annotations
 
 import math
 from dataclasses import dataclass
-from typing import Dict, Optional, Sequence
+from typing import Callable, Dict, Optional, Sequence
 
 import numpy as np
 
@@ -443,12 +443,14 @@ class LayerResult:
     pairs: int               # (query, key) pairs attended by the computed rows
     linear_flops: int        # 2 n d_in d_out summed over the products actually run
     attn_out: Optional[np.ndarray] = None   # [len(rows)][n_q*d] (stored precision)
+    stored: Optional[Dict[str, np.ndarray]] = None   # every stored activation (keep_stored)
 
 
 def layer_forward(dims, w: Dict[str, np.ndarray], x: np.ndarray, chunk_len, chunk_prefix,
                   decode_ctx, block_table: np.ndarray, cache: PagedCache,
                   storage: str = "bf16", rows: Optional[Sequence[int]] = None,
-                  keep_attn: bool = False) -> LayerResult:
+                  keep_attn: bool = False, keep_stored: bool = False,
+                  perturb: Optional[Callable[[str, np.ndarray], np.ndarray]] = None) -> LayerResult:
     """One pre-norm decoder layer over the hybrid batch; writes the batch's new
     K/V into ``cache`` and returns y for ``rows`` (all tokens by default).
 
@@ -456,13 +458,23 @@ def layer_forward(dims, w: Dict[str, np.ndarray], x: np.ndarray, chunk_len, chun
     w_o [H][n_q d], w_g, w_u [F][H], w_d [H][F], g_attn, g_ffn [H].
     K/V are computed for every token (the cache needs them); steps after the
     projections run only for ``rows`` -- exact for those rows.
+
+    Test hooks (both off by default, leaving the arithmetic above untouched):
+    ``keep_stored`` returns every stored activation (xn, q, k, v, o, h1, h1n,
+    a; xn of the rows, and as xn_all of every token) in ``LayerResult.stored``; ``perturb(name, value)`` is applied to each
+    of those values, and to y, right before it is rounded to its storage type
+    -- how sensitive the result is to a change of size ulp(fp32) at one
+    storage point (the conditioning of the layer under its own roundings).
     """
+    hook = perturb if perturb is not None else (lambda name, a: a)
     if storage == "bf16":
-        act, res = round_bf16, round_f32
+        rb, rf = round_bf16, round_f32
     elif storage == "exact":
-        act = res = (lambda a: a)
+        rb = rf = (lambda a: a)
     else:
         raise ValueError(storage)
+    act = lambda a, name: rb(hook(name, a))
+    res = lambda a, name: rf(hook(name, a))
     lay = token_layout(chunk_len, chunk_prefix, decode_ctx)
     T = len(lay.seq)
     d = dims.head_dim
@@ -472,25 +484,27 @@ def layer_forward(dims, w: Dict[str, np.ndarray], x: np.ndarray, chunk_len, chun
     flops = 0
     # projection inputs: bf16 storage, or e4m3 codes with a static scale
     if getattr(dims, "w8a8", 0):
-        gin = lambda a, name: fp8_store(a, getattr(dims, name))
+        gin = lambda a, name, scale: fp8_store(hook(name, a), getattr(dims, scale))
     else:
-        gin = lambda a, name: act(a)
+        gin = lambda a, name, scale: act(a, name)
 
     # a1: RMSNorm of the input (all tokens: K/V need it)
-    xn = gin(rmsnorm(x, w["g_attn"], dims.rms_eps), "x_scale")
+    xn = gin(rmsnorm(x, w["g_attn"], dims.rms_eps), "xn", "x_scale")
     # a2 + a3: projections and rotary embedding
     k, f = linear(xn, w["w_k"]); flops += f
     v, f = linear(xn, w["w_v"]); flops += f
     q, f = linear(xn[rows], w["w_q"]); flops += f
     k = rope(k.reshape(T, nkv, d), lay.pos, dims.rope_theta)
     v = v.reshape(T, nkv, d)
-    q = act(rope(q.reshape(len(rows), nq, d), lay.pos[rows], dims.rope_theta))
+    q = act(rope(q.reshape(len(rows), nq, d), lay.pos[rows], dims.rope_theta), "q")
     # a bf16 cache stores bf16(k), bf16(v); an FP8 cache quantises the unrounded
     # values itself (e4m3(x / scale))
     if getattr(dims, "kv_fp8", 0) != cache.kv_fp8:
         raise ValueError("cache storage type does not match dims.kv_fp8")
-    if not cache.kv_fp8:
-        k, v = act(k), act(v)
+    if cache.kv_fp8:
+        k, v = hook("k", k), hook("v", v)
+    else:
+        k, v = act(k, "k"), act(v, "v")
 
     # a4: new K/V go into the paged cache at their sequence positions
     for t in range(T):
@@ -498,21 +512,22 @@ def layer_forward(dims, w: Dict[str, np.ndarray], x: np.ndarray, chunk_len, chun
 
     # a5: each token attends causally to positions 0..pos of its own sequence
     o, pairs = paged_attention(q, lay.seq[rows], lay.pos[rows], cache, block_table, nkv)
-    o = gin(o.reshape(len(rows), nq * d), "o_scale")
+    o = gin(o.reshape(len(rows), nq * d), "o", "o_scale")
 
     # a6: output projection + residual
     ao, f = linear(o, w["w_o"]); flops += f
-    h1 = res(x[rows] + ao)
+    h1 = res(x[rows] + ao, "h1")
     # a7 + a8: RMSNorm, gate/up projections and SwiGLU
-    h1n = gin(rmsnorm(h1, w["g_ffn"], dims.rms_eps), "h_scale")
+    h1n = gin(rmsnorm(h1, w["g_ffn"], dims.rms_eps), "h1n", "h_scale")
     gt, f1 = linear(h1n, w["w_g"])
     up, f2 = linear(h1n, w["w_u"])
-    a = gin(silu(gt) * up, "a_scale")
+    a = gin(silu(gt) * up, "a", "a_scale")
     # a9: down projection + residual
     dn, f3 = linear(a, w["w_d"])
     flops += f1 + f2 + f3
-    y = res(h1 + dn)
-    return LayerResult(y, rows, pairs, flops, o if keep_attn else None)
+    y = res(h1 + dn, "y")
+    stored = dict(xn=xn[rows], xn_all=xn, q=q, k=k, v=v, o=o, h1=h1, h1n=h1n, a=a) if keep_stored else None
+    return LayerResult(y, rows, pairs, flops, o if keep_attn else None, stored)
 
 
 def weights_to_float(wbits: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:

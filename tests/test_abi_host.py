@@ -75,17 +75,20 @@ def test_attention_work_lists_partition_keys(seed):
     pcnt = hb.meta_array(blob, "part_cnt")
     covered = {t: [] for t in range(T)}
     for kind in ("chunk", "decode"):
-        for seq, tok0, n_tok, k0, k1, split, _, _ in hb.attn_items(blob, kind):
-            assert k0 < k1 and n_tok >= 1
+        for seq, tok0, n_tok, k0, k1, split, n_split, _ in hb.attn_items(blob, kind):
+            assert k0 < k1 and n_tok >= 1 and 0 <= split < n_split and k0 % 16 == 0
             if kind == "decode":
                 assert n_tok == 1 and seq >= len(cl)
             else:
-                assert seq < len(cl) and n_tok <= h.chunk_q_tile
+                assert seq < len(cl) and n_tok <= h.chunk_q_tile and k0 % 64 == 0
             for t in range(tok0, tok0 + n_tok):
-                assert lay.seq[t] == seq
+                assert lay.seq[t] == seq and pcnt[t] == n_split
                 covered[t].append((split, k0, k1))
-    assert int(pcnt.sum()) == h.n_partials
-    assert np.array_equal(poff, np.concatenate([[0], np.cumsum(pcnt)[:-1]]))
+    # partial slots only for tokens with more than one key range, contiguous in token order
+    multi = pcnt > 1
+    assert int(pcnt[multi].sum()) == h.n_partials and int(multi.sum()) == h.n_merge_tokens
+    assert np.all(poff[~multi] == -1)
+    assert np.array_equal(poff[multi], np.concatenate([[0], np.cumsum(pcnt[multi])[:-1]]).astype(np.int64))
     for t in range(T):
         c = sorted(covered[t])
         assert [s for s, _, _ in c] == list(range(pcnt[t]))
@@ -111,36 +114,45 @@ def test_append_runs_cover_each_token_once_within_a_page(seed):
         assert np.array_equal(slot[tok0:tok0 + n], s0 + np.arange(n))
 
 
-def test_long_prompt_widens_the_chunk_key_split():
-    """A 32768-token prompt in one chunk: the keys per chunk item grow past
-    the 1024 minimum (bounding the partial results), the items still cover
-    every token's keys exactly once, and a 512-token chunk keeps 1024."""
+def test_chunk_key_split_follows_the_workgroup_target():
+    """Chunk items: a 32768-token prompt in one chunk already makes 8192
+    workgroups (1024 query tiles x 8 kv heads) unsplit, so no tile is split,
+    no partial result is allocated and nothing is merged; a 512-token chunk
+    over a 3000-token prefix makes too few workgroups for the machine, so its
+    tiles are split into items of at most 768 keys (the minimum), each tile's items as equal
+    as whole 64-key tiles allow, and they cover every token's keys once."""
     L = 32768
     bt, npg = W.deal_block_tables(np.array([L]), 16, np.random.default_rng(1))
     blob, T = _pack(W.MISTRAL, [L], [0], [], bt, npg)
     h = hb.header(blob)
-    assert h.chunk_kv_split > 1024 and h.chunk_kv_split % 1024 == 0
     items = hb.attn_items(blob, "chunk")
-    pcnt = hb.meta_array(blob, "part_cnt")
-    pos = hb.meta_array(blob, "tok_pos")
-    assert np.array_equal(pcnt, (pos + h.chunk_kv_split) // h.chunk_kv_split)
-    assert np.all(items[:, 4] - items[:, 3] <= h.chunk_kv_split)
-    # every (token, key) pair with key <= pos is covered exactly once: per tile, the
-    # split ranges tile [0, key_end) and each token masks keys beyond its position
-    for tok0 in np.unique(items[:, 1]):
-        r = items[items[:, 1] == tok0]
-        r = r[np.argsort(r[:, 5])]
-        assert r[0, 3] == 0 and np.all(r[1:, 3] == r[:-1, 4]) and r[-1, 4] == pos[tok0 + r[0, 2] - 1] + 1
+    assert h.n_partials == 0 and h.n_merge_tokens == 0 and np.all(items[:, 6] == 1)
+    assert np.all(hb.meta_array(blob, "part_cnt") == 1) and np.all(hb.meta_array(blob, "part_off") == -1)
+    assert np.all(items[:, 3] == 0) and h.n_chunk_items == L // h.chunk_q_tile
     bt2, npg2 = W.deal_block_tables(np.array([512 + 3000]), 16, np.random.default_rng(2))
     blob2, _ = _pack(W.MISTRAL, [512], [3000], [], bt2, npg2)
-    assert hb.header(blob2).chunk_kv_split == 1024
+    h2 = hb.header(blob2)
+    assert h2.chunk_kv_split == 768
+    items2 = hb.attn_items(blob2, "chunk")
+    pos = hb.meta_array(blob2, "tok_pos")
+    for tok0 in np.unique(items2[:, 1]):
+        r = items2[items2[:, 1] == tok0]
+        r = r[np.argsort(r[:, 5])]
+        key_end = pos[tok0 + r[0, 2] - 1] + 1
+        steps = (key_end + 63) // 64
+        n = int(r[0, 6])
+        assert len(r) == n == -(-steps // 12) and n > 1
+        assert r[0, 3] == 0 and np.all(r[1:, 3] == r[:-1, 4]) and r[-1, 4] == key_end
+        lens = (64 * np.ceil(np.minimum(r[:, 4], 64 * steps) / 64) - r[:, 3]) // 64
+        assert lens.max() - lens.min() <= 1 and lens.max() <= 12
 
 
 def test_large_decode_batch_widens_the_decode_key_split():
     """512 decodes of 1000-6000 context keys: the decode split grows past its
     256-key minimum (at most 1024, the page ids one decode wave can hold), the
     items still cover every decode's keys exactly once, and both item lists
-    run longest key range first.  32 decodes keep 256."""
+    run longest key range first (chunk items in 256-key buckets).  32 decodes
+    keep 256."""
     rng = np.random.default_rng(7)
     dc = rng.integers(1000, 6000, 512)
     cl, cp = np.array([64]), np.array([100])
@@ -153,9 +165,12 @@ def test_large_decode_batch_widens_the_decode_key_split():
     items = hb.attn_items(blob, "decode")
     pcnt = hb.meta_array(blob, "part_cnt")
     assert np.array_equal(pcnt[64:], (dc + 1 + h.decode_kv_split - 1) // h.decode_kv_split)
+    assert np.array_equal(items[:, 6], pcnt[items[:, 1]])
     for kind in ("chunk", "decode"):
         r = hb.attn_items(blob, kind)
         ln = r[:, 4] - r[:, 3]
+        if kind == "chunk":   # 256-key buckets, split-major within a bucket
+            ln = ln // 256
         assert np.all(ln[:-1] >= ln[1:]), kind
     for t in range(64, T):
         r = items[items[:, 1] == t]
@@ -258,6 +273,31 @@ def test_workspace_size_covers_buffers():
     # plus fp32 split-K partials of at most 8 slices of the widest split projection
     split_max = 8 * T * max(d.qkv_dim, d.hidden) * 4
     assert floor <= need <= floor + split_max + 16 * 256
+
+
+@pytest.mark.parametrize("w8a8", [0, 1])
+def test_workspace_views_are_disjoint_regions_of_the_workspace(w8a8):
+    """hb_workspace_views_of: the six stored activations sit in disjoint,
+    16-byte aligned regions inside hb_workspace_bytes, each large enough for
+    its [T][width] rows (one byte per element for the FP8 codes)."""
+    import dataclasses
+    wl = W.small(2, n_q=8, n_kv=2, head_dim=128)
+    d = dataclasses.replace(wl.dims, w8a8=w8a8, **(W.FP8_ACT_SCALES if w8a8 else {}))
+    b = wl.batch
+    dims = hb.make_dims(d)
+    blob, T = hb.pack_metadata(dims, b.chunk_len, b.chunk_prefix, b.decode_ctx, b.block_table, b.num_pages,
+                               b.token_budget)
+    v = hb.workspace_views(dims, blob)
+    need = hb.workspace_bytes(dims, blob)
+    el = 1 if w8a8 else 2
+    size = {"xn": d.hidden * el, "q": d.n_q_heads * d.head_dim * 2, "o": d.n_q_heads * d.head_dim * el,
+            "h1": d.hidden * 4, "h1n": d.hidden * el, "act": d.ffn_dim * el}
+    spans = sorted((v[n], v[n] + T * size[n], n) for n in size)
+    for (a0, a1, n), (b0, _, m) in zip(spans, spans[1:]):
+        assert a1 <= b0, (n, m)
+    assert all(s0 % 16 == 0 and s1 <= need for s0, s1, _ in spans)
+    with pytest.raises(hb.HbError):
+        hb.workspace_views(dims, np.zeros(64, np.uint8))
 
 
 def test_schedule_worked_example():

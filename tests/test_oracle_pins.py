@@ -576,3 +576,61 @@ def test_w8a8_layer_within_the_quantisation_error_of_the_exact_layer():
     d8, de = y8 - wl.x, ye - wl.x
     rel = np.linalg.norm(d8 - de) / np.linalg.norm(de)
     assert 1e-3 < rel < 0.1, rel
+
+
+def test_w8a8_each_projection_input_takes_its_own_scale():
+    """The four stored projection inputs are e4m3 codes times their own scale
+    (x_scale for the normed input, o_scale for the attention output, h_scale
+    for the normed residual, a_scale for the SwiGLU output), worked out from
+    the format definition and the layer's formulas on the stored values: each
+    lies on its own scale's grid and, with scales whose ratios are not powers
+    of two, not on the others'; the normed input, the normed residual and the
+    SwiGLU output equal their formulas quantised with their own scale."""
+    from chunked_prefill_hybrid_layer_amd import workloads as W
+    wl = W.with_w8a8(W.small(2, n_q=4, n_kv=2, head_dim=64, chunk_len=(20,), chunk_prefix=(5,),
+                             decode_ctx=(3, 17), hidden=128, ffn=256))
+    d, b = wl.dims, wl.batch
+    scales = {"xn": d.x_scale, "o": d.o_scale, "h1n": d.h_scale, "a": d.a_scale}
+    assert len({np.float32(s) for s in scales.values()}) == 4
+    w = O.weights_to_float(wl.weights)
+    cache = O.PagedCache(b.num_pages, d.n_kv_heads, d.page_size, d.head_dim)
+    for s in range(b.n_seq):
+        cache.load_prefix(b.block_table, s, O.bf16_bits_to_float(wl.prefix_k[s]), O.bf16_bits_to_float(wl.prefix_v[s]))
+    st = O.layer_forward(d, w, wl.x, b.chunk_len, b.chunk_prefix, b.decode_ctx, b.block_table, cache,
+                         keep_stored=True).stored
+
+    def on_grid(v, s):
+        q = v / np.float64(np.float32(s))
+        return O.e4m3_decode(O.e4m3_encode(q)) == q
+
+    for name, s in scales.items():
+        assert np.all(on_grid(st[name], s)), name
+        for other, s2 in scales.items():
+            if other != name:
+                assert np.mean(on_grid(st[name], s2)) < 0.5, (name, other)
+
+    def q8(v, s):   # e4m3 store of v with scale s: code of v * (1/s) in single precision, read back * s
+        s32 = np.float32(s)
+        code = O.e4m3_encode(np.asarray(v, np.float64).astype(np.float32) * (np.float32(1.0) / s32))
+        return O.e4m3_decode(code) * np.float64(s32)
+
+    x = wl.x.astype(np.float64)
+    for t in (0, 7, x.shape[0] - 1):
+        ms = sum(float(v) * float(v) for v in x[t]) / d.hidden
+        ref = [x[t, c] / math.sqrt(ms + d.rms_eps) * w["g_attn"][c] for c in range(d.hidden)]
+        assert np.array_equal(st["xn"][t], q8(ref, d.x_scale))
+        h1 = st["h1"][t]
+        ms = sum(float(v) * float(v) for v in h1) / d.hidden
+        ref = [h1[c] / math.sqrt(ms + d.rms_eps) * w["g_ffn"][c] for c in range(d.hidden)]
+        assert np.array_equal(st["h1n"][t], q8(ref, d.h_scale))
+        hn = st["h1n"][t]
+        ref = []
+        for f in range(d.ffn_dim):
+            gt = sum(hn[c] * w["w_g"][f, c] for c in range(d.hidden))
+            up = sum(hn[c] * w["w_u"][f, c] for c in range(d.hidden))
+            ref.append(gt / (1.0 + math.exp(-gt)) * up)
+        got, exp = st["a"][t], q8(ref, d.a_scale)
+        # the plain loops sum in another order than the matrix product: a value
+        # within rounding of a code midpoint may land one code away
+        assert np.mean(got == exp) > 0.99
+        assert np.all(np.abs(got - exp) <= np.abs(exp) * 2.0 ** -3 + 2.0 ** -9 * d.a_scale)
