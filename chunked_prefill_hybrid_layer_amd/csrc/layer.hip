@@ -9,6 +9,8 @@
 //   O projection (+residual) -> RMSNorm -> gate/up projection (+SwiGLU) ->
 //   down projection (+residual).
 
+#include <mutex>
+
 #include "device_common.h"
 
 namespace hb {
@@ -57,14 +59,51 @@ extern "C" hb_status hb_kv_append(const hb_dims* dims, const void* meta_host, co
                           (stream_t)stream);
 }
 
-extern "C" hb_status hb_layer_forward(const hb_dims* dims, const hb_weights* w, const void* meta_host,
-                                      const void* meta_dev, const float* rope_cs, int32_t rope_max_pos,
-                                      const float* x, float* y, void* k_cache, void* v_cache,
-                                      void* workspace, size_t workspace_bytes, void* stream,
-                                      void* const* stage_events) {
+// ---------------------------------------------------------------------------
+// Static scratch of hb_layer_forward_static_scratch, for callers that cannot
+// allocate: the workspace of one forward (stored activations, attention and
+// split-K partial results) in a file-scope device array, one per GPU the
+// library runs on, held until the process ends.  In host code `scratch` is a
+// host-side stand-in, not a device address: its device address is looked up
+// once per device (hipGetSymbolAddress, with the device current) and only
+// that address is handed to kernels.
+constexpr size_t kStaticScratchBytes = (size_t)128 << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+// Device address of the current device's scratch (looked up on the first
+// call on that device).
+static hb_status static_scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(HB_E_HIP, "static scratch: no current device (or device index >= 64)");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(HB_E_HIP, std::string("static scratch: hipGetSymbolAddress failed: ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return HB_OK;
+}
+
+// The forward of both entry points; static_ws: the workspace is the static
+// scratch (workspace and workspace_bytes are ignored).
+static hb_status layer_forward_impl(const hb_dims* dims, const hb_weights* w, const void* meta_host,
+                                    const void* meta_dev, const float* rope_cs, int32_t rope_max_pos,
+                                    const float* x, float* y, void* k_cache, void* v_cache, void* workspace,
+                                    size_t workspace_bytes, void* stream, void* const* stage_events,
+                                    bool static_ws) {
   HB_TRY(check_dims(dims));
   HB_TRY(check_meta(dims, meta_host));
-  if (!w || !meta_dev || !rope_cs || !x || !y || !k_cache || !v_cache || !workspace)
+  if (!w || !meta_dev || !rope_cs || !x || !y || !k_cache || !v_cache || (!static_ws && !workspace))
     return fail(HB_E_NULL, "layer_forward: NULL pointer");
   if (!w->w_q || !w->w_k || !w->w_v || !w->w_o || !w->w_g || !w->w_u || !w->w_d || !w->g_attn || !w->g_ffn)
     return fail(HB_E_NULL, "layer_forward: NULL weight");
@@ -78,13 +117,18 @@ extern "C" hb_status hb_layer_forward(const hb_dims* dims, const hb_weights* w, 
                                    std::to_string(h->max_kv_len));
   const int T = h->n_tokens;
   const WsLayout L = ws_layout(*dims, T, h->n_partials);
-  if (workspace_bytes < L.total)
+  if (static_ws && L.total > kStaticScratchBytes)
+    return fail(HB_E_CAPACITY, "layer_forward_static_scratch: the batch needs " + std::to_string(L.total) +
+                                   " bytes of workspace, the static scratch holds " +
+                                   std::to_string(kStaticScratchBytes));
+  if (!static_ws && workspace_bytes < L.total)
     return fail(HB_E_CAPACITY, "workspace needs " + std::to_string(L.total) + " bytes");
   const uintptr_t al = (uintptr_t)workspace | (uintptr_t)x | (uintptr_t)y | (uintptr_t)k_cache |
                        (uintptr_t)v_cache | (uintptr_t)rope_cs | (uintptr_t)w->w_q | (uintptr_t)w->w_k |
                        (uintptr_t)w->w_v | (uintptr_t)w->w_o | (uintptr_t)w->w_g | (uintptr_t)w->w_u |
                        (uintptr_t)w->w_d | (uintptr_t)w->g_attn | (uintptr_t)w->g_ffn;
   if (al & 15) return fail(HB_E_SHAPE, "layer_forward: device buffers must be 16-byte aligned");
+  if (static_ws) HB_TRY(static_scratch_ptr(&workspace));
 
   const stream_t s = (stream_t)stream;
   // optional per-stage timing events (see HB_STAGE_NAMES)
@@ -241,4 +285,21 @@ extern "C" hb_status hb_layer_forward(const hb_dims* dims, const hb_weights* w, 
   if (pd.splits > 1) HB_TRY(launch_splitk_reduce(gpart, pd.splits, h1, y, T, H, nullptr, nullptr, 0.f, s));
   HB_TRY(mark(9));
   return HB_OK;
+}
+
+extern "C" hb_status hb_layer_forward(const hb_dims* dims, const hb_weights* w, const void* meta_host,
+                                      const void* meta_dev, const float* rope_cs, int32_t rope_max_pos,
+                                      const float* x, float* y, void* k_cache, void* v_cache,
+                                      void* workspace, size_t workspace_bytes, void* stream,
+                                      void* const* stage_events) {
+  return layer_forward_impl(dims, w, meta_host, meta_dev, rope_cs, rope_max_pos, x, y, k_cache, v_cache, workspace,
+                            workspace_bytes, stream, stage_events, false);
+}
+
+extern "C" hb_status hb_layer_forward_static_scratch(const hb_dims* dims, const hb_weights* w, const void* meta_host,
+                                                     const void* meta_dev, const float* rope_cs,
+                                                     int32_t rope_max_pos, const float* x, float* y, void* k_cache,
+                                                     void* v_cache, void* stream) {
+  return layer_forward_impl(dims, w, meta_host, meta_dev, rope_cs, rope_max_pos, x, y, k_cache, v_cache, nullptr, 0,
+                            stream, nullptr, true);
 }

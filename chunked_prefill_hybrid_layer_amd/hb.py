@@ -79,7 +79,9 @@ class Request(ctypes.Structure):
 
 
 EXPORTS = ["hb_meta_bytes", "hb_pack_metadata", "hb_schedule_iteration", "hb_rope_table", "hb_workspace_bytes",
-           "hb_workspace_views_of", "hb_kv_append", "hb_layer_forward", "hb_status_str", "hb_last_error_detail"]
+           "hb_workspace_views_of", "hb_kv_append", "hb_layer_forward", "hb_layer_forward_static_scratch",
+           "hb_status_str", "hb_last_error_detail"]
+STATIC_SCRATCH_BYTES = 128 << 20
 
 
 def _load() -> ctypes.CDLL:
@@ -108,6 +110,9 @@ def _load() -> ctypes.CDLL:
     lib.hb_layer_forward.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Weights), P, P, P, I32, P, P, P, P,
                                      P, SZ, P, ctypes.POINTER(ctypes.c_void_p)]
     lib.hb_layer_forward.restype = ctypes.c_int
+    lib.hb_layer_forward_static_scratch.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Weights), P, P, P, I32, P,
+                                                    P, P, P, P]
+    lib.hb_layer_forward_static_scratch.restype = ctypes.c_int
     lib.hb_status_str.argtypes = [ctypes.c_int]
     lib.hb_status_str.restype = ctypes.c_char_p
     lib.hb_last_error_detail.argtypes = []
@@ -260,6 +265,14 @@ def layer_forward(dims: Dims, weights: Weights, blob: np.ndarray, meta_dev: int,
     _check(lib.hb_layer_forward(ctypes.byref(dims), ctypes.byref(weights), blob.ctypes.data_as(ctypes.c_void_p),
                                 meta_dev, rope_cs, int(rope_max_pos), x, y, k_cache, v_cache, workspace,
                                 int(workspace_bytes_), stream, ev))
+
+
+def layer_forward_static_scratch(dims: Dims, weights: Weights, blob: np.ndarray, meta_dev: int, rope_cs: int,
+                                 rope_max_pos: int, x: int, y: int, k_cache: int, v_cache: int, stream: int = 0):
+    """hb_layer_forward on the library's static scratch (no workspace argument)."""
+    _check(lib.hb_layer_forward_static_scratch(ctypes.byref(dims), ctypes.byref(weights),
+                                               blob.ctypes.data_as(ctypes.c_void_p), meta_dev, rope_cs,
+                                               int(rope_max_pos), x, y, k_cache, v_cache, stream))
 
 
 class Packer:

@@ -339,6 +339,26 @@ hb_status hb_layer_forward(const hb_dims *dims, const hb_weights *w, const void 
                            void *workspace, size_t workspace_bytes, void *stream,
                            void *const *stage_events);
 
+/* hb_layer_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The workspace is a static device array
+ * of HB_STATIC_SCRATCH_BYTES (128 MiB) inside the library: each GPU the
+ * library is loaded on holds one until the process ends, and its device
+ * address is looked up on the first call on that device (the device current
+ * at the call; `stream` must belong to it).  This call allocates nothing and
+ * calls no allocating routine; the caller still passes inputs, outputs,
+ * caches and metadata as for hb_layer_forward.  Every call on one GPU uses
+ * that GPU's one array, which keeps the last call's contents: calls that
+ * overlap on one GPU (other streams, other threads) race; serialise them.
+ * Nothing in the scratch needs to start at zero.  Errors: as hb_layer_forward;
+ * HB_E_CAPACITY, before anything is enqueued, when the batch needs more than
+ * HB_STATIC_SCRATCH_BYTES of workspace (hb_workspace_bytes gives the need). */
+#define HB_STATIC_SCRATCH_BYTES ((size_t)128 << 20)
+hb_status hb_layer_forward_static_scratch(const hb_dims *dims, const hb_weights *w, const void *meta_host,
+                                          const void *meta_dev, const float *rope_cs, int32_t rope_max_pos,
+                                          const float *x, float *y, void *k_cache, void *v_cache,
+                                          void *stream);
+
 const char *hb_status_str(hb_status s);
 const char *hb_last_error_detail(void);
 
