@@ -14,8 +14,8 @@ namespace hb {
 // --- attention tiling (fixed by the kernels; recorded in the metadata) -----
 constexpr int kChunkRows = 128;       // (token, head) rows per chunk attention tile
 constexpr int kChunkKeyTile = 64;     // keys staged per step (4 pages of 16)
-constexpr int kChunkMinKeys = 768;    // keys per chunk attention item at least, where a tile is split
-constexpr int kChunkWgTarget = 1024;  // chunk workgroups (items x kv heads) the key split aims at
+constexpr int kChunkMinKeys = 256;    // keys per chunk attention item at least, where a tile is split
+constexpr int kChunkSlots = 512;      // chunk workgroups the machine runs at once (2 per CU x 256 CUs)
 constexpr int kDecodeKeyStep = 32;    // keys per decode step (2 pages)
 constexpr int kDecodeKvSplit = 256;   // keys per decode attention item, at least (multiple of 32)
 constexpr int kDecodeKvSplitMax = 1024;  // at most: the decode kernel holds an item's page ids one per lane

@@ -211,17 +211,40 @@ hb_status hb_pack_metadata(const hb_dims* dims, int32_t n_chunks, const int32_t*
     // Chunk items.  The keys [0, key_end) of a chunk query tile are cut into
     // n runs of whole 64-key tiles, as equal as whole tiles allow (the last
     // run ends at key_end), n = ceil(tiles / per).  per, the 64-key tiles an
-    // item takes at most, is the smallest that keeps the workgroups (items x
-    // kv heads) near kChunkWgTarget -- two rounds of the two workgroups each
-    // CU holds at a time -- and at least kChunkMinKeys / 64: more items buy
-    // no parallelism, only partial results to write and merge.  A tile that
+    // item takes at most, is the smallest (and at least kChunkMinKeys / 64)
+    // for which the workgroups (items x kv heads) fit one round of the
+    // machine, kChunkSlots: every workgroup then starts at once and the
+    // nearly equal items end together.  Fewer, longer items would leave
+    // slots idle; more would put a second round on some CUs and add partial
+    // results to write and merge.  When no split fits one round, items take
+    // at most half of a slot's share of the work (per = total 64-key tiles
+    // x kv heads / (2 kChunkSlots)), so that longest-first ordering can
+    // balance the rounds; tiles shorter than that stay whole.  A tile that
     // stays whole (n = 1) writes its output directly.
     const int64_t nkv = dims->n_kv_heads;
-    int64_t chunk_steps = 0;
+    std::vector<int64_t> tile_steps;
     for (int s = 0; s < n_chunks; ++s)
       for (int t0 = q_start[s]; t0 < q_start[s + 1]; t0 += qt)
-        chunk_steps += (cached[s] + (t0 - q_start[s]) + std::min(qt, q_start[s + 1] - t0) + 63) / 64;
-    const int64_t per = std::max<int64_t>(kChunkMinKeys / 64, (chunk_steps * nkv + kChunkWgTarget - 1) / kChunkWgTarget);
+        tile_steps.push_back((cached[s] + (t0 - q_start[s]) + std::min(qt, q_start[s + 1] - t0) + 63) / 64);
+    int64_t max_steps = 1;
+    for (int64_t x : tile_steps) max_steps = std::max(max_steps, x);
+    auto workgroups = [&](int64_t per) {
+      int64_t n = 0;
+      for (int64_t x : tile_steps) n += (x + per - 1) / per;
+      return n * nkv;
+    };
+    int64_t total_steps = 0;
+    for (int64_t x : tile_steps) total_steps += x;
+    int64_t per = std::max<int64_t>(kChunkMinKeys / 64, (total_steps * nkv + 2 * kChunkSlots - 1) / (2 * kChunkSlots));
+    if (workgroups(max_steps) <= kChunkSlots) {   // non-increasing in per: bisect
+      int64_t lo = std::min<int64_t>(kChunkMinKeys / 64, max_steps), hi = max_steps;
+      while (lo < hi) {
+        const int64_t mid = (lo + hi) / 2;
+        if (workgroups(mid) <= kChunkSlots) hi = mid;
+        else lo = mid + 1;
+      }
+      per = lo;
+    }
     const int csplit = (int)std::min<int64_t>(per * 64, 1 << 30);
     std::vector<int32_t> part_off((size_t)T), part_cnt((size_t)T);
     std::vector<hb_attn_item> citems, ditems;

@@ -114,37 +114,64 @@ def test_append_runs_cover_each_token_once_within_a_page(seed):
         assert np.array_equal(slot[tok0:tok0 + n], s0 + np.arange(n))
 
 
-def test_chunk_key_split_follows_the_workgroup_target():
-    """Chunk items: a 32768-token prompt in one chunk already makes 8192
-    workgroups (1024 query tiles x 8 kv heads) unsplit, so no tile is split,
-    no partial result is allocated and nothing is merged; a 512-token chunk
-    over a 3000-token prefix makes too few workgroups for the machine, so its
-    tiles are split into items of at most 768 keys (the minimum), each tile's items as equal
-    as whole 64-key tiles allow, and they cover every token's keys once."""
-    L = 32768
-    bt, npg = W.deal_block_tables(np.array([L]), 16, np.random.default_rng(1))
-    blob, T = _pack(W.MISTRAL, [L], [0], [], bt, npg)
+def _expected_chunk_split(dims, cl, cp, slots=512, min_steps=4):
+    """The rule for the keys per chunk item, restated: the smallest number of
+    64-key tiles per item (at least min_steps) whose workgroups (items x kv
+    heads) fit one round of `slots`; when none does, half a slot's share of
+    the work (total tiles x kv heads / (2 slots))."""
+    qt = 128 // (dims.n_q_heads // dims.n_kv_heads)
+    steps = []
+    for n, p in zip(cl, cp):
+        for t0 in range(0, n, qt):
+            steps.append(-(-(p + t0 + min(qt, n - t0)) // 64))
+    wgs = lambda per: sum(-(-x // per) for x in steps) * dims.n_kv_heads
+    if wgs(max(steps)) <= slots:
+        per = next(p for p in range(min(min_steps, max(steps)), max(steps) + 1) if wgs(p) <= slots)
+    else:
+        per = max(min_steps, -(-sum(steps) * dims.n_kv_heads // (2 * slots)))
+    return 64 * per, steps
+
+
+@pytest.mark.parametrize("case", ["prompt_32768", "chunk_512_over_3000", "yi_tau2048_chunks", "small_chunk"])
+def test_chunk_key_split_follows_the_workgroup_rule(case):
+    """Chunk items: the keys per item follow the stated rule (one round of
+    512 workgroups where a split fits it, else half a slot's share of the
+    work); each tile's items are as equal as whole 64-key tiles allow and
+    cover its keys once; tiles left whole have no partial result.  A
+    32768-token prompt is unsplit (8192 workgroups already), so nothing is
+    merged."""
+    dims, cl, cp = {
+        "prompt_32768": (W.MISTRAL, [32768], [0]),
+        "chunk_512_over_3000": (W.MISTRAL, [512], [3000]),
+        "yi_tau2048_chunks": (W.YI, [768, 768], [0, 6144]),
+        "small_chunk": (W.MISTRAL, [64], [1792]),
+    }[case]
+    kv = np.array(cl) + np.array(cp)
+    bt, npg = W.deal_block_tables(kv, 16, np.random.default_rng(2))
+    blob, _ = _pack(dims, cl, cp, [], bt, npg)
     h = hb.header(blob)
+    want, _ = _expected_chunk_split(dims, cl, cp)
     items = hb.attn_items(blob, "chunk")
-    assert h.n_partials == 0 and h.n_merge_tokens == 0 and np.all(items[:, 6] == 1)
-    assert np.all(hb.meta_array(blob, "part_cnt") == 1) and np.all(hb.meta_array(blob, "part_off") == -1)
-    assert np.all(items[:, 3] == 0) and h.n_chunk_items == L // h.chunk_q_tile
-    bt2, npg2 = W.deal_block_tables(np.array([512 + 3000]), 16, np.random.default_rng(2))
-    blob2, _ = _pack(W.MISTRAL, [512], [3000], [], bt2, npg2)
-    h2 = hb.header(blob2)
-    assert h2.chunk_kv_split == 768
-    items2 = hb.attn_items(blob2, "chunk")
-    pos = hb.meta_array(blob2, "tok_pos")
-    for tok0 in np.unique(items2[:, 1]):
-        r = items2[items2[:, 1] == tok0]
+    pos = hb.meta_array(blob, "tok_pos")
+    pcnt = hb.meta_array(blob, "part_cnt")
+    assert h.chunk_kv_split == min(want, 1 << 30)
+    per = h.chunk_kv_split // 64
+    for tok0 in np.unique(items[:, 1]):
+        r = items[items[:, 1] == tok0]
         r = r[np.argsort(r[:, 5])]
         key_end = pos[tok0 + r[0, 2] - 1] + 1
         steps = (key_end + 63) // 64
         n = int(r[0, 6])
-        assert len(r) == n == -(-steps // 12) and n > 1
+        assert len(r) == n == -(-steps // per)
         assert r[0, 3] == 0 and np.all(r[1:, 3] == r[:-1, 4]) and r[-1, 4] == key_end
-        lens = (64 * np.ceil(np.minimum(r[:, 4], 64 * steps) / 64) - r[:, 3]) // 64
-        assert lens.max() - lens.min() <= 1 and lens.max() <= 12
+        lens = (64 * np.ceil(r[:, 4] / 64) - r[:, 3]) // 64
+        assert lens.max() - lens.min() <= 1 and lens.max() <= per
+        assert np.all(pcnt[tok0:tok0 + r[0, 2]] == n)
+    if case == "prompt_32768":
+        assert h.n_partials == 0 and h.n_merge_tokens == 0 and np.all(items[:, 6] == 1)
+        assert h.n_chunk_items == 32768 // h.chunk_q_tile
+    if case == "chunk_512_over_3000":
+        assert h.n_chunk_items * dims.n_kv_heads <= 512 and h.chunk_kv_split == 896
 
 
 def test_large_decode_batch_widens_the_decode_key_split():
