@@ -48,6 +48,8 @@ def workload_by_name(name):
         return W.yi_tau2048_tp2(0)
     if name == "tiny":
         return W.tiny(0)
+    if name == "spec_verify":
+        return W.spec_verify(0)
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -59,15 +61,26 @@ def stage_model(wl):
     H, nq, nkv, D, F = d.hidden, d.n_q_heads, d.n_kv_heads, d.head_dim, d.ffn_dim
     cached = b.cached_lengths()
     new = b.new_lengths()
-    # attention (query, key) pairs: chunk token at position p sees p+1 keys
-    chunk_pairs = 0
-    for c, n in zip(b.chunk_prefix, b.chunk_len):
-        chunk_pairs += int(n) * int(c) + int(n) * (int(n) + 1) // 2
-    dec_pairs = int(np.sum(b.decode_ctx.astype(np.int64) + 1))
+    # attention (query, key) pairs: a token at position p sees p+1 keys.  Chunk
+    # pieces whose (token, head) rows fit the decode kernel's 16-row tile
+    # (new tokens x group <= 16) run on the decode kernel; their keys are read
+    # once for all their rows.
+    g = nq // nkv
+    on_dec = b.chunk_len * g <= 16
+    chunk_pairs, dec_pairs, chunk_kv_keys, dec_kv_keys = 0, 0, 0, 0
+    for c, n, dp in zip(b.chunk_prefix, b.chunk_len, on_dec):
+        pairs = int(n) * int(c) + int(n) * (int(n) + 1) // 2
+        if dp:
+            dec_pairs += pairs
+            dec_kv_keys += int(c) + int(n)
+        else:
+            chunk_pairs += pairs
+            chunk_kv_keys += int(c) + int(n)
+    dec_pairs += int(np.sum(b.decode_ctx.astype(np.int64) + 1))
+    dec_kv_keys += int(np.sum(b.decode_ctx.astype(np.int64) + 1))
     kv_elem = 1 if getattr(d, "kv_fp8", 0) else 2            # bytes per cached K/V element
     kv_bytes_per_key = nkv * D * 2 * kv_elem                # K and V
     we = 1 if getattr(d, "w8a8", 0) else 2                   # bytes per weight / projection-input element
-    chunk_kv_keys = int(np.sum(cached[:b.n_chunks] + new[:b.n_chunks]))
     blob, _ = hb.pack_metadata(hb.make_dims(d), b.chunk_len, b.chunk_prefix, b.decode_ctx, b.block_table,
                                b.num_pages, b.token_budget)
     npart = hb.header(blob).n_partials
@@ -78,7 +91,7 @@ def stage_model(wl):
                             (nq + 2 * nkv) * D * H * we + T * H * we + T * nq * D * 2 + T * 2 * nkv * D * kv_elem,
                             "mfma"),
         "attn_chunk": (4 * chunk_pairs * nq * D, chunk_kv_keys * kv_bytes_per_key, "mfma"),
-        "attn_decode": (4 * dec_pairs * nq * D, dec_pairs * kv_bytes_per_key, "hbm"),
+        "attn_decode": (4 * dec_pairs * nq * D, dec_kv_keys * kv_bytes_per_key, "hbm"),
         "attn_merge": (0, part_bytes + T * nq * D * we, "hbm"),
         "o_proj_residual": (2 * T * nq * D * H, nq * D * H * we + T * nq * D * we + 2 * T * H * 4, "mfma"),
         "rmsnorm_ffn": (0, T * H * 4 + T * H * we + H * 2, "hbm"),

@@ -11,7 +11,9 @@
 // a merge pass combines a token's partials.  The two item kinds run on
 // different kernels:
 //   decode: one wave per (item, kv head).  The g query heads of the kv group
-//     form one 16-row MFMA tile.  S^T = K Q^T and O^T = V^T P^T, so that K
+//     form one 16-row MFMA tile -- for a chunk piece of a few tokens (n x g
+//     <= 16: a speculative-verify step) the n tokens' g heads, each row
+//     masking the keys past its own position.  S^T = K Q^T and O^T = V^T P^T, so that K
 //     rows and V^T rows (the V cache is dim-major inside a page) are MFMA
 //     fragments loaded straight from HBM as 16- and 8-byte vectors, and the
 //     probabilities never leave the lanes that computed them.  The path is a
@@ -157,23 +159,27 @@ __device__ __forceinline__ void store_out4(const AttnArgs& a, size_t oi, float v
       s0 = mfma16x16x32(as_bf16x8(k0[kk]), qf[kk], s0);                                       \
       s1 = mfma16x16x32(as_bf16x8(k1[kk]), qf[kk], s1);                                       \
     }                                                                                         \
-    /* raw scores of keys KB + 8 qd + e; keys past the item's end are masked */               \
+    /* raw scores of keys KB + 8 qd + e for this lane's row; keys past the  */                \
+    /* item's end or past the row's own position are masked                 */                \
     float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};                   \
-    const int _nv = it.key1 - ((KB) + 8 * qd); /* valid keys among this lane's 8 */           \
-    if ((KB) + 32 > it.key1) {                                                                \
+    const int _nv = it.key1 - ((KB) + 8 * qd); /* keys of the item among this lane's 8 */     \
+    if ((KB) + 32 > lim0) {                                                                   \
+      const int _ns = lim - ((KB) + 8 * qd);   /* ... and at or before the row's position */  \
       _Pragma("unroll") for (int e = 0; e < 8; ++e)                                           \
-        if (e >= _nv) sv[e] = -INFINITY;                                                      \
+        if (e >= _ns) sv[e] = -INFINITY;                                                      \
     }                                                                                         \
     float mb = sv[0];                                                                         \
     _Pragma("unroll") for (int e = 1; e < 8; ++e) mb = fmaxf(mb, sv[e]);                      \
     mb = fmaxf(mb, __shfl_xor(mb, 16, 64));                                                   \
     mb = fmaxf(mb, __shfl_xor(mb, 32, 64));                                                   \
-    /* running max in log2 units; the first step always has a valid key */                    \
+    /* running max in log2 units (-inf while the row has seen no key: a     */                \
+    /* multi-token row may see none in a step, or in a whole item)          */                \
     const float mn = fmaxf(m, mb * scale_log2);                                               \
-    const float alpha = fast_exp2(m - mn);                                                    \
+    const float ms = (mn == -INFINITY) ? 0.f : mn;                                            \
+    const float alpha = fast_exp2(m - ms);                                                    \
     float ps[8], lsum = 0.f;                                                                  \
     _Pragma("unroll") for (int e = 0; e < 8; ++e) {                                           \
-      ps[e] = fast_exp2(fmaf(sv[e], scale_log2, -mn));                                        \
+      ps[e] = fast_exp2(fmaf(sv[e], scale_log2, -ms));                                        \
       lsum += ps[e];                                                                          \
     }                                                                                         \
     l = l * alpha + lsum;                                                                     \
@@ -204,6 +210,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
   const hb_attn_item it = a.meta.decode_items[item_idx];
   const int g = a.group, nq = a.n_q_heads, nkv = a.n_kv_heads;
   const int r = lane & 15, qd = lane >> 4;
+  // MFMA row r is (token tl, head hq) of the item's n_tok tokens (n_tok x g <=
+  // 16; a decode is one token).  Row r sees keys < lim: the item's end, or
+  // its own position + 1 if that is earlier; lim0 (the first token's) is the
+  // smallest over the rows, so steps ending at or before it need no mask.
+  const int tl = r / g, hq = r - tl * g;
+  const bool valid = tl < it.n_tok;
+  const int lim = valid ? min(it.key1, a.meta.tok_pos[it.tok0 + tl] + 1) : it.key1;
+  const int lim0 = min(it.key1, a.meta.tok_pos[it.tok0] + 1);
   const int kslot = 8 * ((r >> 2) & 1) + (r & 3);   // K slot of MFMA 0's row r (MFMA 1: + 4)
   const int t = it.tok0;
   const int32_t* bt = a.meta.block_table + (size_t)it.seq * a.max_pages;
@@ -212,10 +226,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
 
   bf16x8 qf[KK];
   {
-    const uint16_t* qrow = a.q + (size_t)t * nq * D + (size_t)(kvh * g + r) * D + qd * 8;
+    const uint16_t* qrow = a.q + (size_t)(t + (valid ? tl : 0)) * nq * D + (size_t)(kvh * g + hq) * D + qd * 8;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      qf[kk] = (r < g) ? as_bf16x8(*reinterpret_cast<const uint4*>(qrow + kk * 32)) : as_bf16x8(make_uint4(0, 0, 0, 0));
+      qf[kk] = valid ? as_bf16x8(*reinterpret_cast<const uint4*>(qrow + kk * 32)) : as_bf16x8(make_uint4(0, 0, 0, 0));
   }
   f32x4 acc[NJ];
 #pragma unroll
@@ -247,18 +261,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
   }
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
-  if (r < g) {
-    const int head = kvh * g + r;
+  if (valid) {
+    const int head = kvh * g + hq, tok = t + tl;
     const float vsc = F8 ? a.v_scale : 1.0f;
     if (it.n_split == 1) {
       // the whole context in one item: normalise and write the output
       const float inv = 1.0f / l;
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
-        store_out4(a, ((size_t)t * nq + head) * D + j * 16 + qd * 4, acc[j][0] * vsc, acc[j][1] * vsc,
+        store_out4(a, ((size_t)tok * nq + head) * D + j * 16 + qd * 4, acc[j][0] * vsc, acc[j][1] * vsc,
                    acc[j][2] * vsc, acc[j][3] * vsc, inv);
     } else {
-      const size_t pidx = (size_t)a.meta.part_off[t] + it.split;
+      const size_t pidx = (size_t)a.meta.part_off[tok] + it.split;
       float* po = a.part_o + (pidx * nq + head) * D;
 #pragma unroll
       for (int j = 0; j < NJ; ++j)

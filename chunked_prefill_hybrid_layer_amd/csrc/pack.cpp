@@ -208,6 +208,13 @@ hb_status hb_pack_metadata(const hb_dims* dims, int32_t n_chunks, const int32_t*
       q_start[s + 1] = q_start[s] + newtok[s];
       kv_len[s] = cached[s] + newtok[s];
     }
+    // Which sequences take the decode kernel: every decode, and every chunk
+    // piece short enough that its (token, head) rows fit the decode kernel's
+    // 16-row tile (new tokens x group <= 16: a speculative-verify step of E
+    // drafted tokens is a piece of E + 1 tokens over its context, "Sarathi-
+    // Serve reading notes" §7.4).  Each row masks the keys past its own
+    // position.  The other chunk pieces go to the chunk kernel's 128-row tiles.
+    auto decode_path = [&](int s) { return s >= n_chunks || newtok[s] * g <= kMaxGroup; };
     // Chunk items.  The keys [0, key_end) of a chunk query tile are cut into
     // n runs of whole 64-key tiles, as equal as whole tiles allow (the last
     // run ends at key_end), n = ceil(tiles / per).  per, the 64-key tiles an
@@ -224,7 +231,8 @@ hb_status hb_pack_metadata(const hb_dims* dims, int32_t n_chunks, const int32_t*
     const int64_t nkv = dims->n_kv_heads;
     std::vector<int64_t> tile_steps;
     for (int s = 0; s < n_chunks; ++s)
-      for (int t0 = q_start[s]; t0 < q_start[s + 1]; t0 += qt)
+      if (!decode_path(s))
+        for (int t0 = q_start[s]; t0 < q_start[s + 1]; t0 += qt)
         tile_steps.push_back((cached[s] + (t0 - q_start[s]) + std::min(qt, q_start[s + 1] - t0) + 63) / 64);
     int64_t max_steps = 1;
     for (int64_t x : tile_steps) max_steps = std::max(max_steps, x);
@@ -250,6 +258,7 @@ hb_status hb_pack_metadata(const hb_dims* dims, int32_t n_chunks, const int32_t*
     std::vector<hb_attn_item> citems, ditems;
     int64_t np = 0, n_merge = 0;
     for (int s = 0; s < n_chunks; ++s) {
+      if (decode_path(s)) continue;
       for (int t0 = q_start[s]; t0 < q_start[s + 1]; t0 += qt) {
         int n = std::min(qt, q_start[s + 1] - t0);
         int key_end = cached[s] + (t0 - q_start[s]) + n;  // last token's position + 1
@@ -295,29 +304,33 @@ hb_status hb_pack_metadata(const hb_dims* dims, int32_t n_chunks, const int32_t*
     int dsplit = kDecodeKvSplit;
     auto decode_items = [&](int split) {
       int64_t n = 0;
-      for (int s = n_chunks; s < S; ++s) n += (kv_len[s] + split - 1) / split;
+      for (int s = 0; s < S; ++s)
+        if (decode_path(s)) n += (kv_len[s] + split - 1) / split;
       return n;
     };
     while (dsplit < kDecodeKvSplitMax && decode_items(dsplit) * dims->n_kv_heads > kDecodeWavesTarget) dsplit *= 2;
-    for (int s = n_chunks; s < S; ++s) {
-      int t = q_start[s];
-      int nsplit = (kv_len[s] + dsplit - 1) / dsplit;
+    for (int s = 0; s < S; ++s) {
+      if (!decode_path(s)) continue;
+      const int t = q_start[s], n = newtok[s];
+      const int nsplit = (kv_len[s] + dsplit - 1) / dsplit;
       for (int j = 0; j < nsplit; ++j) {
         hb_attn_item it{};
         it.seq = s;
         it.tok0 = t;
-        it.n_tok = 1;
+        it.n_tok = n;
         it.key0 = j * dsplit;
         it.key1 = std::min(kv_len[s], (j + 1) * dsplit);
         it.split = j;
         it.n_split = nsplit;
         ditems.push_back(it);
       }
-      part_cnt[t] = nsplit;
-      part_off[t] = nsplit > 1 ? (int32_t)np : -1;
-      if (nsplit > 1) {
-        np += nsplit;
-        ++n_merge;
+      for (int u = t; u < t + n; ++u) {
+        part_cnt[u] = nsplit;
+        part_off[u] = nsplit > 1 ? (int32_t)np : -1;
+        if (nsplit > 1) {
+          np += nsplit;
+          ++n_merge;
+        }
       }
     }
     std::stable_sort(ditems.begin(), ditems.end(), [](const hb_attn_item& x, const hb_attn_item& y) {

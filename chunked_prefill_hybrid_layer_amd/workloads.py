@@ -349,6 +349,17 @@ def yi_tau2048(seed: int = 0) -> Workload:
     return build_workload("yi_tau2048", YI, [768, 768], [0, 6144], ctx, seed, token_budget=2048)
 
 
+def spec_verify(seed: int = 0, n_req: int = 128, q_len: int = 4) -> Workload:
+    """Speculative-decoding verify batch on the Mistral-7B-shaped layer: 128
+    requests each checking 3 drafted tokens at once ("Sarathi-Serve reading
+    notes" §7.4), i.e. pieces of 4 new tokens whose prefix is the request's
+    whole context; contexts lognormal(median 1024, sigma 1) capped at 8192;
+    512 tokens."""
+    _, _, rl, _, _, _ = _streams(seed)
+    ctx = _lognormal_ctx(rl, n_req, 1024, 8192)
+    return build_workload("spec_verify", MISTRAL, [q_len] * n_req, ctx, [], seed, token_budget=n_req * q_len)
+
+
 # FP8 KV cache scales of the synthetic workloads (powers of two, K and V
 # different): N(0, 1)-sized K/V over the scale stay far inside e4m3's +-448
 # and far above its subnormals (2^-6)

@@ -77,10 +77,11 @@ def test_attention_work_lists_partition_keys(seed):
     for kind in ("chunk", "decode"):
         for seq, tok0, n_tok, k0, k1, split, n_split, _ in hb.attn_items(blob, kind):
             assert k0 < k1 and n_tok >= 1 and 0 <= split < n_split and k0 % 16 == 0
-            if kind == "decode":
-                assert n_tok == 1 and seq >= len(cl)
+            g = dims.n_q_heads // dims.n_kv_heads
+            if kind == "decode":   # decodes, and chunk pieces whose rows fit the 16-row decode tile
+                assert n_tok == (1 if seq >= len(cl) else cl[seq]) and n_tok * g <= 16
             else:
-                assert seq < len(cl) and n_tok <= h.chunk_q_tile and k0 % 64 == 0
+                assert seq < len(cl) and cl[seq] * g > 16 and n_tok <= h.chunk_q_tile and k0 % 64 == 0
             for t in range(tok0, tok0 + n_tok):
                 assert lay.seq[t] == seq and pcnt[t] == n_split
                 covered[t].append((split, k0, k1))

@@ -234,12 +234,16 @@ def test_chunked_prefill_matches_unchunked_on_gpu():
 
 
 @pytest.mark.parametrize("case", ["decodes_only", "one_token_chunk", "ctx0_only", "page_edge_chunks",
-                                  "multi_token_decodes"])
+                                  "multi_token_decodes", "verify_rows_g1"])
 def test_layer_edge_cases(case):
     """Edge cases of the batch layout.  multi_token_decodes: requests that
     verify E drafted tokens at once ("Sarathi-Serve reading notes" §7.4,
     speculative decoding) are chunks of E + 1 tokens whose prefix is the whole
-    context, next to plain decodes."""
+    context, next to plain decodes; pieces whose (token, head) rows fit 16
+    (2 and 4 tokens at g = 4) run on the decode kernel with a causal mask per
+    row, the 8-token one on the chunk kernel.  verify_rows_g1: g = 1, pieces
+    of 16, 3 and 1 tokens on the decode kernel (16 rows = 16 tokens), one of
+    them at context 0 and one ending on a page edge."""
     log(f"edge case {case}")
     kw = {
         "decodes_only": dict(chunk_len=(), chunk_prefix=(), decode_ctx=(1, 16, 17, 255, 256, 257, 999)),
@@ -248,8 +252,11 @@ def test_layer_edge_cases(case):
         "page_edge_chunks": dict(chunk_len=(16, 17, 15, 129), chunk_prefix=(16, 15, 1, 1023), decode_ctx=()),
         "multi_token_decodes": dict(chunk_len=(2, 4, 8, 4), chunk_prefix=(1000, 333, 17, 2045),
                                     decode_ctx=(5, 1000, 2047)),
+        "verify_rows_g1": dict(chunk_len=(16, 3, 1), chunk_prefix=(300, 0, 1023), decode_ctx=(7,),
+                               n_q=4, n_kv=4, head_dim=64, hidden=256, ffn=512),
     }[case]
-    wl = W.small(7, n_q=8, n_kv=2, head_dim=128, **kw)
+    kw = dict(dict(n_q=8, n_kv=2, head_dim=128), **kw)
+    wl = W.small(7, **kw)
     b = wl.batch
     layer = _layer_for(wl)
     layer.fill_prefixes(b.block_table, range(b.n_seq), wl.prefix_k, wl.prefix_v)
