@@ -3,6 +3,12 @@
     # per-kernel durations (from --kernel-trace --stats CSV output)
     python -m chunked_prefill_hybrid_layer_amd.profiling stats <dir>/<run>_kernel_stats.csv
 
+    # per-phase kernel time of a run made of several batches (bench.py
+    # --long-prompt / --chunk-sweep): the trace is cut into layer forwards
+    # (each starts with the RMSNorm that feeds the QKV projection); a phase
+    # NAME:NxP is P passes of N forwards, of which the middle one is summed
+    python -m chunked_prefill_hybrid_layer_amd.profiling phases <dir>/<run>_kernel_trace.csv NAME:NxP ...
+
     # HBM bytes per launch from two --pmc runs (FETCH_SIZE, then WRITE_SIZE),
     # scaled by what the same counters read for the plain 256 MiB copy that
     # `bench.py --calibrate-copy` issues
@@ -59,6 +65,48 @@ def kernel_stats(path: str) -> str:
         pct = float(r.get("Percentage", 0.0))
         out.append(f"| {short_name(name)} (`{name[:70]}`) | {calls} | {avg:.2f} | {tot:.1f} | {pct:.2f} |")
     return "\n".join(out)
+
+
+def forwards(trace_csv: str):
+    """Layer forwards of a kernel trace, in time order: lists of (short
+    name, duration us, start ns).  A forward starts at an RMSNorm launch
+    directly followed by a QKV projection launch; launches of other kernels
+    (copies, fills) are left out."""
+    rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Start_Timestamp"]))
+    ks = [(short_name(r["Kernel_Name"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3,
+           int(r["Start_Timestamp"])) for r in rows]
+    ks = [k for k in ks if k[0] in set(LAYER_KERNELS.values())]
+    out = []
+    for i, k in enumerate(ks):
+        if k[0] == "rmsnorm" and i + 1 < len(ks) and ks[i + 1][0] == "qkv_rope_append":
+            out.append([])
+        if out:
+            out[-1].append(k)
+    return out
+
+
+def phases(trace_csv: str, specs):
+    fw = forwards(trace_csv)
+    need = sum(n * p for _, n, p in specs)
+    if need != len(fw):
+        raise SystemExit(f"trace holds {len(fw)} forwards, the phases describe {need}")
+    lines = ["| phase | forwards | span ms | " + " | ".join(sorted(set(LAYER_KERNELS.values()))) + " |",
+             "|---|---:|---:|" + "---:|" * len(set(LAYER_KERNELS.values()))]
+    names = sorted(set(LAYER_KERNELS.values()))
+    i = 0
+    res = {}
+    for name, n, p in specs:
+        passes = [fw[i + j * n:i + (j + 1) * n] for j in range(p)]
+        i += n * p
+        mid = passes[p // 2]
+        tot = collections.defaultdict(float)
+        for f in mid:
+            for k, d, _ in f:
+                tot[k] += d
+        span = (mid[-1][-1][2] + mid[-1][-1][1] * 1e3 - mid[0][0][2]) / 1e6
+        res[name] = dict(tot)
+        lines.append(f"| {name} | {n} | {span:.3f} | " + " | ".join(f"{tot.get(k, 0.0) / 1e3:.3f}" for k in names) + " |")
+    return "\n".join(lines), res
 
 
 def _per_kernel(path: str, counter: str):
@@ -122,6 +170,14 @@ def write_traffic_json(res, cal, workload: str, path: str, root: str):
 def main(argv):
     if len(argv) >= 2 and argv[0] == "stats":
         print(kernel_stats(argv[1]))
+    elif len(argv) >= 3 and argv[0] == "phases":
+        specs = []
+        for a in argv[2:]:
+            name, np_ = a.split(":")
+            n, p = np_.split("x")
+            specs.append((name, int(n), int(p)))
+        print("kernel time summed per phase (ms), middle pass of each phase")
+        print(phases(argv[1], specs)[0])
     elif len(argv) >= 3 and argv[0] == "traffic":
         res, cal = traffic(argv[1], argv[2])
         if len(argv) >= 5:   # ... --json-for WORKLOAD: update profiles/traffic.json
