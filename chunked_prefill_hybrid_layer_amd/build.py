@@ -20,31 +20,41 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
 SOURCES = ["pack.cpp", "elementwise.hip", "gemm.hip", "attention.hip", "layer.hip"]
 
 
-def _compile(src: str, obj_dir: str) -> str:
+# host-side AddressSanitizer + UndefinedBehaviorSanitizer (device code is not
+# instrumented: each -fsanitize= applies to the host compilation only)
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def _compile(src: str, obj_dir: str, extra=()) -> str:
     obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, f"--offload-arch={ARCH}", *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, f"--offload-arch={ARCH}", *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
-        cmd = [HIPCC, *COMMON[:5], "-c", "-x", "c++", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *COMMON[:5], *extra, "-c", "-x", "c++", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compiling {src} failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    obj_dir = os.path.join(HERE, "_build")
+def build(verbose: bool = False, sanitize: bool = False, out: str = None) -> str:
+    """Compile libhb.so in place (or, with sanitize, a host-sanitized copy at
+    `out`, for the host tests run under libasan)."""
+    extra = SANITIZE if sanitize else []
+    obj_dir = os.path.join(HERE, "_build_san" if sanitize else "_build")
+    out = out or OUT
     os.makedirs(obj_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, obj_dir), SOURCES))
-    tmp = OUT + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+        objs = list(ex.map(lambda s: _compile(s, obj_dir, extra), SOURCES))
+    tmp = out + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *extra, *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"linking failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
     if verbose:
-        print("built", OUT)
-    return OUT
+        print("built", out)
+    return out
 
 
 if __name__ == "__main__":

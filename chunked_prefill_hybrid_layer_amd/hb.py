@@ -21,7 +21,9 @@ except ImportError:  # host-only use (metadata packing) works without torch
     torch = None
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libhb.so")
+# HB_LIB_PATH: another build of the same library (the host tests use it for a
+# host-sanitized build)
+LIB_PATH = os.environ.get("HB_LIB_PATH") or os.path.join(_HERE, "libhb.so")
 
 HB_OK = 0
 STATUS_NAMES = ["HB_OK", "HB_E_NULL", "HB_E_SHAPE", "HB_E_LENGTH", "HB_E_BUDGET", "HB_E_PAGE",
