@@ -871,31 +871,42 @@ __global__ __launch_bounds__(TL::THREADS) void gemm_spec_kernel(GemmArgs g) {
 }
 
 // y[m][:] = res[m][:] + sum_z part[z][m][:] (z in order); with norm_out, also
-// norm_out[m][:] = bf16(y / sqrt(mean(y^2) + eps) * gain).  One workgroup per
-// row; the row stays in registers (N <= 256 * 4 * kReduceMaxChunks).
-constexpr int kReduceMaxChunks = 16;
+// norm_out[m][:] = bf16(y / sqrt(mean(y^2) + eps) * gain).  One workgroup of
+// NT threads per row; the row stays in registers (N <= NT * 4 * MAXCH).  All
+// slices of a chunk are loaded before any is added (up to kMaxSplits), so a
+// thread waits on memory once per chunk, not once per slice; the sum keeps the
+// slice order.
+constexpr int kMaxSplits = 8;   // the planner splits K at most 8 ways
 
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int splits,
-                                                            const float* __restrict__ res, float* __restrict__ out,
-                                                            int M, int N, const uint16_t* __restrict__ gain,
-                                                            void* __restrict__ norm_out, float eps,
-                                                            float norm_inv_scale) {
-  __shared__ float red[4];
+template <int NT, int MAXCH>
+__global__ __launch_bounds__(NT) void splitk_reduce_kernel(const float* __restrict__ part, int splits,
+                                                           const float* __restrict__ res, float* __restrict__ out,
+                                                           int M, int N, const uint16_t* __restrict__ gain,
+                                                           void* __restrict__ norm_out, float eps,
+                                                           float norm_inv_scale) {
+  constexpr int NW = NT / 64;
+  __shared__ float red[NW];
   const int m = blockIdx.x;
   const int n4 = N >> 2;
-  float4 v[kReduceMaxChunks];
+  float4 v[MAXCH];
   float ss = 0.f;
 #pragma unroll
-  for (int k = 0; k < kReduceMaxChunks; ++k) {
-    const int i = threadIdx.x + 256 * k;
+  for (int k = 0; k < MAXCH; ++k) {
+    const int i = threadIdx.x + NT * k;
     if (i < n4) {
+      float4 p[kMaxSplits];
+#pragma unroll
+      for (int z = 0; z < kMaxSplits; ++z)
+        if (z < splits) p[z] = reinterpret_cast<const float4*>(part + ((size_t)z * M + m) * N)[i];
       v[k] = reinterpret_cast<const float4*>(res + (size_t)m * N)[i];
-      for (int z = 0; z < splits; ++z) {
-        const float4 p = reinterpret_cast<const float4*>(part + ((size_t)z * M + m) * N)[i];
-        v[k].x += p.x;
-        v[k].y += p.y;
-        v[k].z += p.z;
-        v[k].w += p.w;
+#pragma unroll
+      for (int z = 0; z < kMaxSplits; ++z) {
+        if (z < splits) {
+          v[k].x += p[z].x;
+          v[k].y += p[z].y;
+          v[k].z += p[z].z;
+          v[k].w += p[z].w;
+        }
       }
       reinterpret_cast<float4*>(out + (size_t)m * N)[i] = v[k];
       ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
@@ -905,11 +916,13 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
-  const float total = (red[0] + red[1]) + (red[2] + red[3]);
+  float total = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; w += 2) total += red[w] + red[w + 1];
   const float rs = 1.0f / sqrtf(total / (float)N + eps);
 #pragma unroll
-  for (int k = 0; k < kReduceMaxChunks; ++k) {
-    const int i = threadIdx.x + 256 * k;
+  for (int k = 0; k < MAXCH; ++k) {
+    const int i = threadIdx.x + NT * k;
     if (i < n4) {
       const uint2 gg = reinterpret_cast<const uint2*>(gain)[i];
       const float y0 = v[k].x * rs * bf2f((uint16_t)(gg.x & 0xffff)), y1 = v[k].y * rs * bf2f((uint16_t)(gg.x >> 16));
@@ -933,12 +946,22 @@ __global__ __launch_bounds__(256) void qkv_reduce_kernel(GemmArgs g, int splits)
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (int64_t)g.M * groups) return;
   const int m = (int)(idx / groups), n = (int)(idx % groups) * 8;
+  float4 u[kMaxSplits], v[kMaxSplits];   // every slice loaded before any is added
+#pragma unroll
+  for (int z = 0; z < kMaxSplits; ++z) {
+    if (z < splits) {
+      const float4* row = reinterpret_cast<const float4*>(g.part + ((size_t)z * g.M + m) * g.N + n);
+      u[z] = row[0];
+      v[z] = row[1];
+    }
+  }
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-  for (int z = 0; z < splits; ++z) {
-    const float4* row = reinterpret_cast<const float4*>(g.part + ((size_t)z * g.M + m) * g.N + n);
-    const float4 u = row[0], v = row[1];
-    a.x += u.x; a.y += u.y; a.z += u.z; a.w += u.w;
-    b.x += v.x; b.y += v.y; b.z += v.z; b.w += v.w;
+#pragma unroll
+  for (int z = 0; z < kMaxSplits; ++z) {
+    if (z < splits) {
+      a.x += u[z].x; a.y += u[z].y; a.z += u[z].z; a.w += u[z].w;
+      b.x += v[z].x; b.y += v[z].y; b.z += v[z].z; b.w += v[z].w;
+    }
   }
   const float x0[4] = {a.x, a.z, b.x, b.z}, x1[4] = {a.y, a.w, b.y, b.w};
   qkv_store4(g, m, n, x0, x1);
@@ -1071,9 +1094,16 @@ hb_status launch_gemm(const GemmArgs& ga, stream_t s) {
 hb_status launch_splitk_reduce(const float* part, int splits, const float* res, float* out, int M, int N,
                                const uint16_t* gain, void* norm_out, float eps, stream_t s, float norm_inv_scale) {
   if (M <= 0) return HB_OK;
-  if (N > 256 * 4 * kReduceMaxChunks) return fail(HB_E_SHAPE, "split-K reduce: row above 16384");
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(M), dim3(256), 0, (hipStream_t)s, part, splits, res, out, M, N, gain,
-                     norm_out, eps, norm_inv_scale);
+  if (N > 16384) return fail(HB_E_SHAPE, "split-K reduce: row above 16384");
+  if (splits < 1 || splits > kMaxSplits) return fail(HB_E_SHAPE, "split-K reduce: 1..8 slices");
+  // A row per workgroup; with fewer rows than the machine has CUs, 1024
+  // threads a row (more loads in flight per row), else 256.
+  if (M < kNumCU)
+    hipLaunchKernelGGL((splitk_reduce_kernel<1024, 4>), dim3(M), dim3(1024), 0, (hipStream_t)s, part, splits, res, out,
+                       M, N, gain, norm_out, eps, norm_inv_scale);
+  else
+    hipLaunchKernelGGL((splitk_reduce_kernel<256, 16>), dim3(M), dim3(256), 0, (hipStream_t)s, part, splits, res, out,
+                       M, N, gain, norm_out, eps, norm_inv_scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(HB_E_HIP, std::string("split-K reduce launch: ") + hipGetErrorString(e));
   return HB_OK;
