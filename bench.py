@@ -693,13 +693,14 @@ def chunk_sweep_bench(args):
     ms_u, st_u, y_full = _run_unchunked(base)
     attn_u = float(st_u[ia])
     pts = []
-    for C in CHUNK_SWEEP:
+    for C in (args.chunk_sizes or CHUNK_SWEEP):
         lp = W.long_prompt(0, chunk=C, n_dec=0)
         ms_c, st_c, y = _run_chunked(lp)
         rel = float(np.linalg.norm(y.astype(np.float64) - y_full) / np.linalg.norm(y_full.astype(np.float64)))
         pts.append({"chunk": C, "iterations": lp.n_iter, "prompt_ms": round(ms_c, 3),
                     "attn_chunk_ms": round(float(st_c[ia]), 3),
                     "recompute_overhead": round(float(st_c[ia]) / attn_u - 1.0, 4),
+                    "attn_merge_ms": round(float(st_c[names.index("attn_merge")]), 3),
                     "gemm_ms": round(float(sum(st_c[names.index(n)] for n in
                                              ("qkv_rope_append", "o_proj_residual", "gate_up_swiglu",
                                               "down_residual"))), 3),
@@ -728,6 +729,8 @@ def main():
     ap.add_argument("--kv-append", action="store_true", help="hb_kv_append GB/s on a 32768-token prompt")
     ap.add_argument("--long-prompt", action="store_true",
                     help="32768-token prompt: 64 chunks of 512 with 64 decodes vs unchunked")
+    ap.add_argument("--chunk-sizes", type=lambda v: [int(c) for c in v.split(",")], default=None,
+                    help="chunk sizes of --chunk-sweep (comma-separated; default 128,256,512,1024,2048)")
     ap.add_argument("--chunk-sweep", action="store_true",
                     help="32768-token prompt alone at chunk sizes 128 .. 2048 vs unchunked")
     args = ap.parse_args()

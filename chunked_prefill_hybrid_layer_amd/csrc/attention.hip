@@ -364,18 +364,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   const int npg = (it.key1 - it.key0 + 15) >> 4;
   const int ntiles = (it.key1 - it.key0 + 63) >> 6;
 
+  // Page ids of this wave's pages (page 4 j + wave of the item for tile j),
+  // one per lane for a window of 64 tiles, broadcast with readlane.  The
+  // first window is requested before Q, so the first tile's loads wait only
+  // for it and Q's loads overlap them.  Window w + 1 (if the item has one) is
+  // requested at the first tile of window w into pnext and taken over when
+  // its first tile is issued, 63 tiles later.
+  // The loads are unconditional (indexes clamped into the item, results
+  // selected afterwards): a load under a branch makes every later wait a
+  // wait for all loads.
+  auto fetch_window = [&](int w) {
+    const int pi = 4 * (64 * w + lane) + wave;
+    const int v = bt[max(0, min(pi, npg - 1))];
+    return pi < npg ? v : 0;
+  };
+  int pcur = fetch_window(0), pnext = 0;
+
   // this lane's query row and its Q^T fragments (dims 16 ks + 8 hh .. +7)
   const int row = wave * 32 + col;
   const int tl = row / g, hq = row - tl * g;
   const bool valid = tl < it.n_tok;
   const int t = it.tok0 + tl;
-  const int rpos = valid ? a.meta.tok_pos[t] : -1;
+  const int tq = valid ? t : it.tok0;   // rows past the item's tokens read its first row
+  const int rpos_l = a.meta.tok_pos[tq];
+  const int rpos = valid ? rpos_l : -1;
   bf16x8 qf[KS];
   {
-    const uint16_t* qrow = a.q + ((size_t)t * nq + kvh * g + hq) * D + hh * 8;
+    const uint16_t* qrow = a.q + ((size_t)tq * nq + kvh * g + hq) * D + hh * 8;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qf[ks] = valid ? as_bf16x8(*reinterpret_cast<const uint4*>(qrow + ks * 16)) : as_bf16x8(make_uint4(0, 0, 0, 0));
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 u = *reinterpret_cast<const uint4*>(qrow + ks * 16);
+      qf[ks] = as_bf16x8(valid ? u : make_uint4(0, 0, 0, 0));
+    }
   }
 
   // LDS fragment offsets (elements, stage 0).  K: MFMA row col of key block kb
@@ -402,20 +422,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   }
   const int vdma = (lane >> 1) * 16 + (((lane & 1) ^ ((lane >> 4) & 1)) * 8);
 
-  // Page ids of this wave's pages (page 4 j + wave of the item for tile j),
-  // one per lane for a window of 64 tiles, double-buffered over windows and
-  // broadcast with readlane.  Window w + 1 is fetched at the first tile of
-  // window w.
-  auto fetch_window = [&](int w) {
-    const int pi = 4 * (64 * w + lane) + wave;
-    return pi < npg ? bt[pi] : 0;
-  };
-  int pw0 = fetch_window(0), pw1 = 0;
-
   auto issue_tile = [&](int tile, int st) {
     // wave-uniform: does the tile have this wave's page?
     if (4 * tile + wave < npg) {
-      const int page = __builtin_amdgcn_readlane(((tile >> 6) & 1) ? pw1 : pw0, tile & 63);
+      const int page = __builtin_amdgcn_readlane(pcur, tile & 63);
       const size_t base = ((size_t)page * nkv + kvh) * PAGE;
       const uint16_t* kg = static_cast<const uint16_t*>(a.k_cache) + base;
       const uint16_t* vg = static_cast<const uint16_t*>(a.v_cache) + base + vdma;
@@ -440,7 +450,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   uint4 kr8[NL8], vr8[NL8];
   auto load_tile8 = [&](int tile) {
     if (4 * tile + wave < npg) {
-      const int page = __builtin_amdgcn_readlane(((tile >> 6) & 1) ? pw1 : pw0, tile & 63);
+      const int page = __builtin_amdgcn_readlane(pcur, tile & 63);
       const size_t base = ((size_t)page * nkv + kvh) * PAGE + lane * 16;
 #pragma unroll
       for (int u = 0; u < NL8; ++u) {
@@ -485,13 +495,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   for (int ti = 0; ti < ntiles; ++ti) {
     const int kt = it.key0 + ti * 64;
     const int cur = ti & 1;
-    // tile ti has landed for every wave, and every wave is done with tile ti - 1
+    // tile ti has landed for every wave (each wave's own direct-to-LDS loads
+    // are complete before it reaches the barrier), and every wave is done
+    // with tile ti - 1
+    WAIT_VMCNT(0);
     __syncthreads();
-    if ((ti & 63) == 0) {
-      const int nw = fetch_window((ti >> 6) + 1);
-      if ((ti >> 6) & 1) pw0 = nw; else pw1 = nw;
-    }
+    if ((ti & 63) == 0 && ti + 64 < ntiles) pnext = fetch_window((ti >> 6) + 1);
     if (ti + 1 < ntiles) {
+      if (((ti + 1) & 63) == 0) pcur = pnext;
       if (F8) load_tile8(ti + 1);
       else issue_tile(ti + 1, cur ^ 1);
     }

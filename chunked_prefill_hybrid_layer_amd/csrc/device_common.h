@@ -9,6 +9,15 @@
 
 namespace hb {
 
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).  Direct-to-LDS
+// loads (global_load_lds) count in vmcnt; the compiler does not reliably wait
+// for them before a barrier, so kernels that stage tiles that way wait
+// explicitly before the barrier that publishes a tile.
+#define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+// s_waitcnt with only the LDS/scalar counter constrained (lgkmcnt = 0)
+#define WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4))
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));

@@ -212,11 +212,6 @@ __device__ __forceinline__ void qkv_store4(const GemmArgs& g, int m, int n, cons
   }
 }
 
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
-#define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
-// s_waitcnt with only the LDS/scalar counter constrained (lgkmcnt = 0)
-#define WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4))
 
 // Epilogue, in passes of EPI_ROWS tile rows staged through LDS as fp32:
 // acc[i][j][e] is C[wm*WROWS + i*16 + 4*(lane>>4) + e][wn*WCOLS + j*16 + (lane&15)].

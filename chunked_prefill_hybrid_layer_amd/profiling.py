@@ -9,6 +9,11 @@
     # NAME:NxP is P passes of N forwards, of which the middle one is summed
     python -m chunked_prefill_hybrid_layer_amd.profiling phases <dir>/<run>_kernel_trace.csv NAME:NxP ...
 
+    # the launches of one forward in order, each with its median duration over
+    # the forwards of the trace that run the same launch sequence (the
+    # projections O and down share a kernel; their order tells them apart)
+    python -m chunked_prefill_hybrid_layer_amd.profiling sequence <dir>/<run>_kernel_trace.csv
+
     # HBM bytes per launch from two --pmc runs (FETCH_SIZE, then WRITE_SIZE),
     # scaled by what the same counters read for the plain 256 MiB copy that
     # `bench.py --calibrate-copy` issues
@@ -109,6 +114,23 @@ def phases(trace_csv: str, specs):
     return "\n".join(lines), res
 
 
+def sequence(trace_csv: str) -> str:
+    fw = forwards(trace_csv)
+    seqs = collections.Counter(tuple(k for k, _, _ in f) for f in fw)
+    common, n = seqs.most_common(1)[0]
+    same = [f for f in fw if tuple(k for k, _, _ in f) == common]
+    lines = [f"{n} of {len(fw)} forwards run this launch sequence; median over them (us)", "",
+             "| # | kernel | median us |", "|---:|---|---:|"]
+    total = 0.0
+    for i, k in enumerate(common):
+        d = sorted(f[i][1] for f in same)
+        med = d[len(d) // 2]
+        total += med
+        lines.append(f"| {i} | {k} | {med:.2f} |")
+    lines.append(f"| | sum | {total:.2f} |")
+    return "\n".join(lines)
+
+
 def _per_kernel(path: str, counter: str):
     vals = collections.defaultdict(list)
     for r in csv.DictReader(open(path)):
@@ -170,6 +192,8 @@ def write_traffic_json(res, cal, workload: str, path: str, root: str):
 def main(argv):
     if len(argv) >= 2 and argv[0] == "stats":
         print(kernel_stats(argv[1]))
+    elif len(argv) >= 2 and argv[0] == "sequence":
+        print(sequence(argv[1]))
     elif len(argv) >= 3 and argv[0] == "phases":
         specs = []
         for a in argv[2:]:
