@@ -685,6 +685,114 @@ __global__ __launch_bounds__(TL::THREADS) void gemm_sub_kernel(GemmArgs g) {
   gemm_epilogue<MODE, TL>(g, acc, smem, m0, n0, wm, wn, lane, tid);
 }
 
+// FP8 wide tiles (256 x 224, 256 x 256).  A 64-unit stage row is 128 codes,
+// so one 16x16x128 MFMA per (i, j) covers a stage and the bf16 sub-step split
+// has no FP8 counterpart; with the fragments of the next stage held in
+// registers as the ring kernel does, these tiles spill.  Here two LDS stages
+// and one barrier per stage: after the barrier every wave is done with the
+// stage before (its buffer is refilled with the next stage at once) and the
+// current stage has landed; the stage's A fragments are read first, the B
+// fragments one column block ahead of its MFMAs.  The next stage's loads
+// have one stage of MFMAs to land.  The loads and LDS images are the ring
+// kernel's (K counted in 16-bit units), the weight rows stream through L2
+// under the same rule as the bf16 wide tiles.  (A schedule that gave the
+// weight rows two stages of slack -- all B fragments read first, a second
+// barrier, then the B rows of the stage after next -- measured the same:
+// 65-66 us on the 512-token gate/up, 242 us at 2048 tokens.)
+template <int MODE, class TL>
+__global__ __launch_bounds__(TL::THREADS) void gemm_f8w_kernel(GemmArgs g) {
+  constexpr int BM = TL::BM, BN = TL::BN, BK = TL::BK, SE = TL::STAGE_ELEMS;
+  constexpr int NL = TL::LOADS, FM = TL::FM, FN = TL::FN, CPR = TL::CPR, RPL = TL::RPL;
+  constexpr int WROWS = BM / TL::WM, WCOLS = BN / TL::WN;
+  static_assert(TL::NST == 2, "two LDS stages");
+  __shared__ __align__(16) unsigned char smem[TL::LDS];
+  uint16_t* lds = reinterpret_cast<uint16_t*>(smem);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / TL::WN, wn = wave % TL::WN;
+  const int tiles_m = (g.M + BM - 1) / BM;
+  int bid = blockIdx.x;
+  const int nblk = gridDim.x;
+  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  const int tm = bid % tiles_m, tn = bid / tiles_m;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int nk = (g.K / BK) / gridDim.z;
+  const int k_first = blockIdx.z * nk;
+
+  // DMA mapping of the ring kernel: load q = wave + WAVES * i covers rows
+  // [RPL q, RPL q + RPL) of the stage image; waves short of a load repeat the
+  // stage's last one.
+  const bool stream_w = tiles_m <= kStreamWeightsMaxRowTiles;
+  const uint16_t* gsrc[NL];
+  int ldst[NL];
+  bool wrow[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int q = min(wave + TL::WAVES * i, TL::TOTAL_LOADS - 1);
+    const int r = RPL * q + lane / CPR;
+    const int rr = r < BM ? r : r - BM;
+    const int c = swz<CPR>(rr, lane % CPR);
+    gsrc[i] = (r < BM ? g.a + (size_t)min(m0 + rr, g.M - 1) * g.lda : weight_row<MODE, BN>(g, n0 + rr, n0)) +
+              (size_t)k_first * BK + c * 8;
+    ldst[i] = RPL * q * BK;
+    wrow[i] = stream_w && RPL * q >= BM;   // wave-uniform: a load's rows are all A or all weights
+  }
+#define ISSUE_STAGE(KT)                                                                              \
+  {                                                                                                  \
+    uint16_t* _st = lds + ((KT) & 1) * SE;                                                           \
+    _Pragma("unroll") for (int i = 0; i < NL; ++i) {                                                 \
+      if (wrow[i])                                                                                   \
+        __builtin_amdgcn_global_load_lds((const void*)(gsrc[i] + (size_t)(KT) * BK),                 \
+                                         (lds_ptr_t)(_st + ldst[i]), 16, 0, kWeightLoadPolicy);      \
+      else                                                                                           \
+        __builtin_amdgcn_global_load_lds((const void*)(gsrc[i] + (size_t)(KT) * BK),                 \
+                                         (lds_ptr_t)(_st + ldst[i]), 16, 0, 0);                      \
+    }                                                                                                \
+  }
+  // 32 codes per lane: 16-byte chunks qd and 4 + qd of the row (read as
+  // bf16x8, the type the bf16 path reads)
+#define FRAG8(DST, BASE, R)                                                                      \
+  {                                                                                              \
+    const int _r = (R);                                                                          \
+    const bf16x8 _lo = *reinterpret_cast<const bf16x8*>((BASE) + _r * BK + swz<CPR>(_r, (lane >> 4)) * 8); \
+    const bf16x8 _hi = *reinterpret_cast<const bf16x8*>((BASE) + _r * BK + swz<CPR>(_r, 4 + (lane >> 4)) * 8); \
+    DST = cat_i32x8(__builtin_bit_cast(uint4, _lo), __builtin_bit_cast(uint4, _hi));             \
+  }
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  i32x8 fa[FM], fb[2];
+  const int arow = wm * WROWS + (lane & 15), brow = wn * WCOLS + (lane & 15);
+
+  ISSUE_STAGE(0);
+  for (int kt = 0; kt < nk; ++kt) {
+    WAIT_VMCNT(0);   // stage kt (the only one in flight) has landed
+    WAIT_LGKM0();    // this wave's reads of stage kt - 1 are done
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kt + 1 < nk) ISSUE_STAGE(kt + 1);
+    const uint16_t* as = lds + (kt & 1) * SE;
+    const uint16_t* bs = as + BM * BK;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) FRAG8(fa[i], as, arow + i * 16);
+    FRAG8(fb[0], bs, brow);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      if (j + 1 < FN) FRAG8(fb[(j + 1) & 1], bs, brow + (j + 1) * 16);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) acc[i][j] = mfma16x16x128_f8(fa[i], fb[j & 1], acc[i][j]);
+    }
+  }
+#undef FRAG8
+#undef ISSUE_STAGE
+  WAIT_VMCNT(0);
+  __syncthreads();
+  gemm_epilogue<MODE, TL>(g, acc, smem, m0, n0, wm, wn, lane, tid);
+}
+
 // Wave-specialised pipeline.  Consumer waves 0-3 (one per SIMD) run every
 // MFMA of the tile, each a 64-row block across all BN columns; producer waves
 // 4-7 (the other wave of each SIMD) issue every direct-to-LDS load, into a
@@ -1003,8 +1111,11 @@ static void plan_try(GemmPlan& best, double& best_cost, int tile, int mode, int 
 // projections; 256x224 set so that it beats 256x256 where both apply, as
 // measured in the layer).  FP8 (f8): K counts codes; the plan is made for
 // K / 2 units (same bytes and the same MFMA cycles per stage as bf16), on the
-// ring-pipeline tiles; the FP8 ring kernel keeps the unskewed load issue, so
-// its 256x128 tile keeps the earlier fit.
+// ring-pipeline tiles and the FP8 wide tiles; the FP8 ring kernel keeps the
+// unskewed load issue, so its 256x128 tile keeps the earlier fit.  FP8
+// 256x224 measured 66 us on the 512-token gate/up (0.46) and 236 us at 2048
+// tokens (0.52); 256x256 93 us on the 2048-token QKV (0.35, where the
+// 256x128 ring tile takes 86 us).
 GemmPlan gemm_plan(int mode, int M, int N, int K, bool f8) {
   GemmPlan p{kTile128W8, 1};
   double cost = 1e30;
@@ -1013,7 +1124,11 @@ GemmPlan gemm_plan(int mode, int M, int N, int K, bool f8) {
   plan_try<Tile128N96>(p, cost, kTile128N96, mode, M, N, K, f8 ? 0.291 : 0.31);
   if (M < 256) return p;
   plan_try<Tile256>(p, cost, kTile256, mode, M, N, K, f8 ? 0.426 : 0.445);
-  if (f8) return p;
+  if (f8) {   // the FP8 wide-tile kernel (gemm_f8w_kernel), fit to its layer timings
+    plan_try<TileW256>(p, cost, kTileW256, mode, M, N, K, 0.35);
+    plan_try<TileW224>(p, cost, kTileW224, mode, M, N, K, 0.47);
+    return p;
+  }
   plan_try<TileS256>(p, cost, kTileS256, mode, M, N, K, 0.49);
   plan_try<TileW256>(p, cost, kTileW256, mode, M, N, K, 0.53);
   plan_try<TileW224>(p, cost, kTileW224, mode, M, N, K, 0.485);
@@ -1037,6 +1152,16 @@ static void launch_spec(const GemmArgs& g, int splits, hipStream_t s) {
     case kGemmQkvRope: hipLaunchKernelGGL((gemm_spec_kernel<kGemmQkvRope, TL>), grid, dim3(TL::THREADS), 0, s, g); break;
     case kGemmResidual: hipLaunchKernelGGL((gemm_spec_kernel<kGemmResidual, TL>), grid, dim3(TL::THREADS), 0, s, g); break;
     default: hipLaunchKernelGGL((gemm_spec_kernel<kGemmSwiglu, TL>), grid, dim3(TL::THREADS), 0, s, g); break;
+  }
+}
+
+template <class TL>
+static void launch_f8w(const GemmArgs& g, int splits, hipStream_t s) {
+  const dim3 grid((unsigned)(((g.M + TL::BM - 1) / TL::BM) * (g.N / TL::BN)), 1, splits);
+  switch (g.mode) {
+    case kGemmQkvRope: hipLaunchKernelGGL((gemm_f8w_kernel<kGemmQkvRope, TL>), grid, dim3(TL::THREADS), 0, s, g); break;
+    case kGemmResidual: hipLaunchKernelGGL((gemm_f8w_kernel<kGemmResidual, TL>), grid, dim3(TL::THREADS), 0, s, g); break;
+    default: hipLaunchKernelGGL((gemm_f8w_kernel<kGemmSwiglu, TL>), grid, dim3(TL::THREADS), 0, s, g); break;
   }
 }
 
@@ -1065,6 +1190,8 @@ hb_status launch_gemm(const GemmArgs& ga, stream_t s) {
   if (p.splits > 1 && !g.part) return fail(HB_E_NULL, "gemm split-K needs a partial buffer");
   if (g.f8) {
     if (p.tile == kTile256) launch_tile<Tile256, true>(g, p.splits, (hipStream_t)s);
+    else if (p.tile == kTileW224) launch_f8w<TileW224>(g, p.splits, (hipStream_t)s);
+    else if (p.tile == kTileW256) launch_f8w<TileW256>(g, p.splits, (hipStream_t)s);
     else if (p.tile == kTile128N96) launch_tile<Tile128N96, true>(g, p.splits, (hipStream_t)s);
     else launch_tile<Tile128W8, true>(g, p.splits, (hipStream_t)s);
   } else if (p.tile == kTileS256) launch_spec<TileS256>(g, p.splits, (hipStream_t)s);

@@ -120,6 +120,7 @@ DERIVED_BAR_CASES = {
     "yi_T256": (lambda: gemm_plan_workload("yi_T256"), 16, 1e-7, False),
     "mistral_tau512_w8a8": (lambda: W.with_w8a8(W.mistral_tau512(0)), 48, FP8_MFMA_REL_ERR, True),
     "mistral_T2048_w8a8": (lambda: W.with_w8a8(gemm_plan_workload("mistral_T2048")), 16, FP8_MFMA_REL_ERR, True),
+    "yi_T512_w8a8": (lambda: W.with_w8a8(gemm_plan_workload("yi_T512")), 16, FP8_MFMA_REL_ERR, True),
     "small_g7_d128_w8a8": (lambda: W.with_w8a8(W.small(2, **SMALL["g7_d128"])), None, FP8_MFMA_REL_ERR, True),
 }
 FLOOR_ROWS = 96          # the floor is measured on the first 96 of the sampled rows
