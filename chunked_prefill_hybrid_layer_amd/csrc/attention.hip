@@ -17,7 +17,11 @@
 //     rows and V^T rows (the V cache is dim-major inside a page) are MFMA
 //     fragments loaded straight from HBM as 16- and 8-byte vectors, and the
 //     probabilities never leave the lanes that computed them.  The path is a
-//     bandwidth-bound stream over the cached context.
+//     bandwidth-bound stream over the cached context.  A workgroup is one
+//     wave, and the grid runs kv head fastest: the kv heads of an item start
+//     together and read the same pages, whose blocks for all kv heads are
+//     adjacent in memory (Yi tau=2048 decode 1.20 -> 1.16 ms, 64 decodes at
+//     tau=128 86 -> 80 us, against four items per workgroup item-fastest).
 //   chunk: one 256-thread workgroup per (item, kv head) holds up to 128
 //     (token, head) rows, 32 per wave; 64-key tiles (4 pages) of K and V are
 //     staged through double-buffered, swizzled LDS and shared by the 4 waves.
@@ -203,10 +207,10 @@ template <int D, bool F8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void attn_decode_kernel(AttnArgs a, float scale_log2) {
   constexpr int KK = D / 32;  // MFMA k-steps over the head dim
   constexpr int NJ = D / 16;  // 16-dim output blocks
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int item_idx = blockIdx.x * 4 + wave;
+  const int lane = threadIdx.x & 63;
+  const int kvh = blockIdx.x % a.n_kv_heads;
+  const int item_idx = blockIdx.x / a.n_kv_heads;
   if (item_idx >= a.n_decode_items) return;
-  const int kvh = blockIdx.y;
   const hb_attn_item it = a.meta.decode_items[item_idx];
   const int g = a.group, nq = a.n_q_heads, nkv = a.n_kv_heads;
   const int r = lane & 15, qd = lane >> 4;
@@ -709,8 +713,8 @@ static hb_status launch_attention_d(const AttnArgs& a, stream_t s, void* const* 
                        scale_log2);
   if (!mark(1)) return fail(HB_E_HIP, "attention: stage event record failed");
   if (a.n_decode_items > 0)
-    hipLaunchKernelGGL((attn_decode_kernel<D, F8>), dim3((a.n_decode_items + 3) / 4, a.n_kv_heads), dim3(256), 0, st, a,
-                       scale_log2);
+    hipLaunchKernelGGL((attn_decode_kernel<D, F8>), dim3((unsigned)a.n_decode_items * a.n_kv_heads), dim3(64), 0, st,
+                       a, scale_log2);
   if (!mark(2)) return fail(HB_E_HIP, "attention: stage event record failed");
   const int64_t pairs = (int64_t)a.n_tokens * a.n_q_heads, per_block = 256 / (D / 4);
   if (a.n_merge_tokens > 0)
