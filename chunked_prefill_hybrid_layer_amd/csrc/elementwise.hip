@@ -24,13 +24,16 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
   const int row = blockIdx.x;
   const float4* xr = reinterpret_cast<const float4*>(x + (size_t)row * hidden);
   const int n4 = hidden >> 2;
+  const uint2* g2 = reinterpret_cast<const uint2*>(gain);
   float4 v[kNormMaxChunks];
+  uint2 gg[kNormMaxChunks];   // gains requested with the row, not after its sum
   float ss = 0.f;
 #pragma unroll
   for (int k = 0; k < kNormMaxChunks; ++k) {
     const int i = threadIdx.x + 256 * k;
     if (i < n4) {
       v[k] = xr[i];
+      gg[k] = g2[i];
       ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
     }
   }
@@ -39,7 +42,6 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
   __syncthreads();
   const float total = (red[0] + red[1]) + (red[2] + red[3]);
   const float r = 1.0f / sqrtf(total / (float)hidden + eps);
-  const uint2* g2 = reinterpret_cast<const uint2*>(gain);
   const bool f8 = out_inv_scale > 0.0f;   // FP8 codes of the normed row / scale
   uint2* orow = reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + (size_t)row * hidden);
   uint32_t* crow = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(out) + (size_t)row * hidden);
@@ -47,9 +49,8 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
   for (int k = 0; k < kNormMaxChunks; ++k) {
     const int i = threadIdx.x + 256 * k;
     if (i < n4) {
-      const uint2 gg = g2[i];
-      const float y0 = v[k].x * r * bf2f((uint16_t)(gg.x & 0xffff)), y1 = v[k].y * r * bf2f((uint16_t)(gg.x >> 16));
-      const float y2 = v[k].z * r * bf2f((uint16_t)(gg.y & 0xffff)), y3 = v[k].w * r * bf2f((uint16_t)(gg.y >> 16));
+      const float y0 = v[k].x * r * bf2f((uint16_t)(gg[k].x & 0xffff)), y1 = v[k].y * r * bf2f((uint16_t)(gg[k].x >> 16));
+      const float y2 = v[k].z * r * bf2f((uint16_t)(gg[k].y & 0xffff)), y3 = v[k].w * r * bf2f((uint16_t)(gg[k].y >> 16));
       if (f8) {
         crow[i] = pack4fp8(y0 * out_inv_scale, y1 * out_inv_scale, y2 * out_inv_scale, y3 * out_inv_scale);
       } else {

@@ -993,6 +993,15 @@ __global__ __launch_bounds__(NT) void splitk_reduce_kernel(const float* __restri
   const int n4 = N >> 2;
   float4 v[MAXCH];
   float ss = 0.f;
+  // the norm's gains are requested with the row, not after the row sum
+  uint2 gg[MAXCH];
+  if (norm_out) {
+#pragma unroll
+    for (int k = 0; k < MAXCH; ++k) {
+      const int i = threadIdx.x + NT * k;
+      if (i < n4) gg[k] = reinterpret_cast<const uint2*>(gain)[i];
+    }
+  }
 #pragma unroll
   for (int k = 0; k < MAXCH; ++k) {
     const int i = threadIdx.x + NT * k;
@@ -1027,9 +1036,8 @@ __global__ __launch_bounds__(NT) void splitk_reduce_kernel(const float* __restri
   for (int k = 0; k < MAXCH; ++k) {
     const int i = threadIdx.x + NT * k;
     if (i < n4) {
-      const uint2 gg = reinterpret_cast<const uint2*>(gain)[i];
-      const float y0 = v[k].x * rs * bf2f((uint16_t)(gg.x & 0xffff)), y1 = v[k].y * rs * bf2f((uint16_t)(gg.x >> 16));
-      const float y2 = v[k].z * rs * bf2f((uint16_t)(gg.y & 0xffff)), y3 = v[k].w * rs * bf2f((uint16_t)(gg.y >> 16));
+      const float y0 = v[k].x * rs * bf2f((uint16_t)(gg[k].x & 0xffff)), y1 = v[k].y * rs * bf2f((uint16_t)(gg[k].x >> 16));
+      const float y2 = v[k].z * rs * bf2f((uint16_t)(gg[k].y & 0xffff)), y3 = v[k].w * rs * bf2f((uint16_t)(gg[k].y >> 16));
       if (norm_inv_scale > 0.0f) {   // FP8 codes of the normed row / scale
         const float q = norm_inv_scale;
         reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(norm_out) + (size_t)m * N)[i] =
