@@ -707,6 +707,9 @@ static hb_status launch_attention_d(const AttnArgs& a, stream_t s, void* const* 
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D) * (F8 ? a.k_scale : 1.0f);
   hipStream_t st = (hipStream_t)s;
   auto mark = [&](int i) -> bool { return !ev || !ev[i] || hipEventRecord((hipEvent_t)ev[i], st) == hipSuccess; };
+  // one workgroup per (item, kv head): the grid's x extent holds at most 2^31 - 1
+  if ((int64_t)a.n_chunk_items * a.n_kv_heads > INT32_MAX || (int64_t)a.n_decode_items * a.n_kv_heads > INT32_MAX)
+    return fail(HB_E_SHAPE, "attention: more (item, kv head) pairs than one grid holds");
   if (!mark(0)) return fail(HB_E_HIP, "attention: stage event record failed");
   if (a.n_chunk_items > 0)
     hipLaunchKernelGGL((attn_chunk_kernel<D, F8>), dim3((unsigned)a.n_chunk_items * a.n_kv_heads), dim3(256), 0, st, a,
