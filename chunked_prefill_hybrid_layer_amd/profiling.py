@@ -119,6 +119,8 @@ def phases(trace_csv: str, specs):
 
 def sequence(trace_csv: str) -> str:
     fw = forwards(trace_csv)
+    if not fw:
+        return "no layer forward found in the trace (an RMSNorm launch followed by a QKV projection)"
     seqs = collections.Counter(tuple(k for k, _, _ in f) for f in fw)
     common, n = seqs.most_common(1)[0]
     same = [f for f in fw if tuple(k for k, _, _ in f) == common]
