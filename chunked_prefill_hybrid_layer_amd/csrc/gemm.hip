@@ -215,14 +215,14 @@ __device__ __forceinline__ void qkv_store4(const GemmArgs& g, int m, int n, cons
 
 // Epilogue, in passes of EPI_ROWS tile rows staged through LDS as fp32:
 // acc[i][j][e] is C[wm*WROWS + i*16 + 4*(lane>>4) + e][wn*WCOLS + j*16 + (lane&15)].
-template <int MODE, class TL>
+template <int MODE, class TL, bool F8 = true>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x4 (&acc)[TL::FM][TL::FN], unsigned char* smem,
                                               int m0, int n0, int wm, int wn, int lane, int tid) {
   constexpr int BM = TL::BM, BN = TL::BN, NT = TL::THREADS, FM = TL::FM, FN = TL::FN;
   constexpr int WROWS = BM / TL::WM, WCOLS = BN / TL::WN, CS_LD = TL::CS_LD;
   float* Cs = reinterpret_cast<float*>(smem);
   constexpr int ER = TL::EPI_ROWS;
-  if (g.f8) {   // codes -> values: input scale times the weight row's scale, per column
+  if (F8 && g.f8) {   // codes -> values: input scale times the weight row's scale, per column
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int n = n0 + wn * WCOLS + j * 16 + (lane & 15);
@@ -973,6 +973,149 @@ __global__ __launch_bounds__(TL::THREADS) void gemm_spec_kernel(GemmArgs g) {
   gemm_epilogue<MODE, TL>(g, acc, smem, m0, n0, wm, 0, lane, tid);
 }
 
+// Wide wave-specialised pipeline (256 x 224): 12 waves, three per SIMD.
+// Consumer waves 0-7 (two per SIMD) each hold a 64 x 112 accumulator block
+// (112 VGPRs) and run its MFMAs; producer waves 8-11 issue every
+// direct-to-LDS load of a stage (15 each) into two 60 KB stages.  Three waves
+// per SIMD leave 168 VGPRs a wave, so a consumer reads the A fragments of a
+// 32-deep sub-step when it starts and each B fragment one column block ahead
+// of its MFMAs, and the other consumer of its SIMD hides those reads.  One
+// barrier per stage: after it every consumer is done with the stage before
+// (its buffer takes the stage after next) and the next stage has landed.
+template <int BM_, int BN_>
+struct SpecWTile {
+  static constexpr int BM = BM_, BN = BN_, BK = 64, NST = 2;
+  static constexpr int WM = 4, WN = 2;                          // consumer blocks
+  static constexpr int CONSUMERS = WM * WN, PRODUCERS = 4, WAVES = CONSUMERS + PRODUCERS, THREADS = 64 * WAVES;
+  static constexpr int FM = BM / WM / 16, FN = BN / WN / 16;
+  static constexpr int KS = BK / 32, CPR = BK / 8, RPL = 64 / CPR;
+  static constexpr int STAGE_ELEMS = (BM + BN) * BK;
+  static constexpr int TOTAL_LOADS = (BM + BN) / RPL;
+  static constexpr int LOADS = TOTAL_LOADS / PRODUCERS;
+  static constexpr int MAIN_LDS = NST * STAGE_ELEMS * 2;
+  static constexpr int CS_LD = BN + 4;
+  static constexpr int EPI_ROWS = BM * CS_LD * 4 <= 160 * 1024 - 4096 ? BM : BM / 2;
+  static constexpr int EPI_LDS = EPI_ROWS * CS_LD * 4;
+  static constexpr int LDS = MAIN_LDS > EPI_LDS ? MAIN_LDS : EPI_LDS;
+  static_assert(TOTAL_LOADS % PRODUCERS == 0, "stage loads must split evenly over the producers");
+  static_assert((BM / RPL) % PRODUCERS == 0, "A rows fill whole load indices of every producer");
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+  static_assert(EPI_ROWS % (BM / WM) == 0, "epilogue passes must hold whole consumer blocks");
+};
+using TileSW224 = SpecWTile<256, 224>;
+
+template <int MODE, class TL>
+__global__ __launch_bounds__(TL::THREADS) __attribute__((amdgpu_waves_per_eu(3))) void gemm_specw_kernel(GemmArgs g) {
+  constexpr int BM = TL::BM, BK = TL::BK, SE = TL::STAGE_ELEMS;
+  constexpr int NL = TL::LOADS, FM = TL::FM, FN = TL::FN, CPR = TL::CPR, RPL = TL::RPL;
+  constexpr int WROWS = BM / TL::WM, WCOLS = TL::BN / TL::WN;
+  static_assert(TL::KS == 2 && TL::NST == 2, "two 64-deep stages of two sub-steps");
+  static_assert(NL <= 31, "vmcnt counts at most 63 loads");
+  __shared__ __align__(16) unsigned char smem[TL::LDS];
+  uint16_t* lds = reinterpret_cast<uint16_t*>(smem);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tiles_m = (g.M + BM - 1) / BM;
+  int bid = blockIdx.x;
+  const int nblk = gridDim.x;
+  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  const int tm = bid % tiles_m, tn = bid / tiles_m;
+  const int m0 = tm * BM, n0 = tn * TL::BN;
+  const int nk = (g.K / BK) / gridDim.z;
+  const int k_first = blockIdx.z * nk;
+
+  // accumulators: set in each branch, so they are not live through the
+  // producers' loop
+  f32x4 acc[FM][FN];
+  // consumer block (wm, wn); producers stage nothing in the epilogue
+  int wm = wave % TL::WM, wn = wave / TL::WM;
+
+  if (wave >= TL::CONSUMERS) {
+    wm = 1 << 20;
+    wn = 0;
+    const int p = wave - TL::CONSUMERS;
+    const bool stream_w = tiles_m <= kStreamWeightsMaxRowTiles;
+    const uint16_t* gsrc[NL];
+    int ldst[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int q = p + TL::PRODUCERS * i;   // row group: A rows, then B rows
+      const int r = RPL * q + lane / CPR;
+      const int rr = r < BM ? r : r - BM;
+      const int c = swz<CPR>(rr, lane % CPR);
+      gsrc[i] = (r < BM ? g.a + (size_t)min(m0 + rr, g.M - 1) * g.lda : weight_row<MODE, TL::BN>(g, n0 + rr, n0)) +
+                (size_t)k_first * BK + c * 8;
+      ldst[i] = RPL * q * BK;
+    }
+    auto issue = [&](int kt) {
+      uint16_t* st = lds + (kt & 1) * SE;
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {   // loads i < (BM / RPL) / PRODUCERS are A rows
+        if (i < (BM / RPL) / TL::PRODUCERS || !stream_w)
+          __builtin_amdgcn_global_load_lds((const void*)(gsrc[i] + (size_t)kt * BK), (lds_ptr_t)(st + ldst[i]), 16, 0,
+                                           0);
+        else
+          __builtin_amdgcn_global_load_lds((const void*)(gsrc[i] + (size_t)kt * BK), (lds_ptr_t)(st + ldst[i]), 16, 0,
+                                           kWeightLoadPolicy);
+      }
+    };
+    issue(0);
+    if (nk > 1) issue(1);
+    // stage 0 landed (stage 1 may still be in flight)
+    if (nk > 1) WAIT_VMCNT(NL);
+    else WAIT_VMCNT(0);
+    __builtin_amdgcn_s_barrier();
+    for (int st = 0; st + 1 < nk; ++st) {
+      WAIT_VMCNT(0);   // stage st + 1 (the only one in flight) has landed
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      // every consumer is done with stage st: refill its buffer
+      if (st + 2 < nk) issue(st + 2);
+    }
+    WAIT_VMCNT(0);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  } else {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 fa[FM], fb[2];
+    const int arow = wm * WROWS + (lane & 15), brow = wn * WCOLS + (lane & 15);
+#define RD(BASE, R, KK) \
+  (*reinterpret_cast<const bf16x8*>((BASE) + (R) * BK + swz<CPR>((R), (KK) * 4 + (lane >> 4)) * 8))
+    __builtin_amdgcn_s_barrier();   // stage 0 has landed
+    asm volatile("" ::: "memory");
+    for (int st = 0; st < nk; ++st) {
+      const uint16_t* as = lds + (st & 1) * SE;
+      const uint16_t* bs = as + BM * BK;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa[i] = RD(as, arow + i * 16, kk);
+        fb[0] = RD(bs, brow, kk);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          if (j + 1 < FN) fb[(j + 1) & 1] = RD(bs, brow + (j + 1) * 16, kk);
+#pragma unroll
+          for (int i = 0; i < FM; ++i) acc[i][j] = mfma16x16x32(fa[i], fb[j & 1], acc[i][j]);
+        }
+      }
+      if (st + 1 < nk) {
+        WAIT_LGKM0();   // this wave's reads of stage st are done
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+      }
+    }
+#undef RD
+  }
+  __syncthreads();
+  gemm_epilogue<MODE, TL, false>(g, acc, smem, m0, n0, wm, wn, lane, tid);
+}
+
 // y[m][:] = res[m][:] + sum_z part[z][m][:] (z in order); with norm_out, also
 // norm_out[m][:] = bf16(y / sqrt(mean(y^2) + eps) * gain).  One workgroup of
 // NT threads per row; the row stays in registers (N <= NT * 4 * MAXCH).  All
@@ -1078,7 +1221,7 @@ __global__ __launch_bounds__(256) void qkv_reduce_kernel(GemmArgs g, int splits)
   qkv_store4(g, m, n, x0, x1);
 }
 
-enum { kTile256 = 1, kTileW256 = 2, kTileW224 = 3, kTile128W8 = 4, kTile128N96 = 5, kTileS256 = 6 };
+enum { kTile256 = 1, kTileW256 = 2, kTileW224 = 3, kTile128W8 = 4, kTile128N96 = 5, kTileS256 = 6, kTileSW224 = 7 };
 
 // Estimated time of one GEMM under a tile choice, fitted (least squares, 37
 // measured tile/split choices on the Mistral-7B- and Yi-34B-shaped
@@ -1087,12 +1230,14 @@ enum { kTile256 = 1, kTileW256 = 2, kTileW224 = 3, kTile128W8 = 4, kTile128N96 =
 //   + split-K partials written and read once at 6.5 TB/s,
 // where rounds = ceil(tiles / 256 CUs), f = tiles / (rounds * 256) is how full
 // the rounds are (a part-filled machine runs each busy CU faster), and 545
-// K columns stand for a tile's pipeline fill and epilogue.
+// K columns stand for a tile's pipeline fill and epilogue.  The wide
+// wave-specialised kernel gains nothing from a part-filled machine (its four
+// producer waves set its load rate, not the memory system): it takes f = 1.
 template <class TL>
-static double plan_cost(int M, int N, int K, int splits, double eff) {
+static double plan_cost(int M, int N, int K, int splits, double eff, bool fill_gain) {
   const double tiles = (double)((M + TL::BM - 1) / TL::BM) * (N / TL::BN) * splits;
   const double rounds = std::ceil(tiles / kNumCU);
-  const double fill = tiles / (rounds * kNumCU);
+  const double fill = fill_gain ? tiles / (rounds * kNumCU) : 1.0;
   const double per_cu = 2.5e15 / kNumCU * eff;   // flop/s
   const double t_tile = 2.0 * TL::BM * TL::BN * ((double)K / splits + 545.0) / per_cu;
   const double t_part = splits > 1 ? 2.0 * splits * (double)M * N * 4 / 6.5e12 : 0.0;
@@ -1100,12 +1245,13 @@ static double plan_cost(int M, int N, int K, int splits, double eff) {
 }
 
 template <class TL>
-static void plan_try(GemmPlan& best, double& best_cost, int tile, int mode, int M, int N, int K, double eff) {
+static void plan_try(GemmPlan& best, double& best_cost, int tile, int mode, int M, int N, int K, double eff,
+                     bool fill_gain = true) {
   if (N % TL::BN || K % TL::BK) return;
   const int nk = K / TL::BK;
   for (int splits = 1; splits <= 8; splits *= 2) {
     if (splits > 1 && (mode == kGemmSwiglu || nk % splits || nk / splits < 2 * TL::NST)) break;
-    const double c = plan_cost<TL>(M, N, K, splits, eff);
+    const double c = plan_cost<TL>(M, N, K, splits, eff, fill_gain);
     if (c < best_cost) {
       best_cost = c;
       best.tile = tile;
@@ -1123,7 +1269,12 @@ static void plan_try(GemmPlan& best, double& best_cost, int tile, int mode, int 
 // unskewed load issue, so its 256x128 tile keeps the earlier fit.  FP8
 // 256x224 measured 66 us on the 512-token gate/up (0.46) and 236 us at 2048
 // tokens (0.52); 256x256 93 us on the 2048-token QKV (0.35, where the
-// 256x128 ring tile takes 86 us).
+// 256x128 ring tile takes 86 us).  The wide wave-specialised 256x224 kernel
+// (bf16 only) measured 100-102 us on the Mistral-shaped 512-token gate/up
+// against 103-105 on the sub-step kernel, 193 vs 196 at 1024 tokens and 376
+// vs 406 (256x128 specialised) at 2048, but 170 vs 158 us at 576 tokens (1.5
+// rounds) and 7.45 vs 6.21 ms at 32768 (256x256 sub-step), where the
+// activation rows no longer stay in L2: it is tried up to 2048 rows only.
 GemmPlan gemm_plan(int mode, int M, int N, int K, bool f8) {
   GemmPlan p{kTile128W8, 1};
   double cost = 1e30;
@@ -1140,6 +1291,7 @@ GemmPlan gemm_plan(int mode, int M, int N, int K, bool f8) {
   plan_try<TileS256>(p, cost, kTileS256, mode, M, N, K, 0.49);
   plan_try<TileW256>(p, cost, kTileW256, mode, M, N, K, 0.53);
   plan_try<TileW224>(p, cost, kTileW224, mode, M, N, K, 0.485);
+  if (M <= 2048) plan_try<TileSW224>(p, cost, kTileSW224, mode, M, N, K, 0.55, false);
   return p;
 }
 
@@ -1160,6 +1312,16 @@ static void launch_spec(const GemmArgs& g, int splits, hipStream_t s) {
     case kGemmQkvRope: hipLaunchKernelGGL((gemm_spec_kernel<kGemmQkvRope, TL>), grid, dim3(TL::THREADS), 0, s, g); break;
     case kGemmResidual: hipLaunchKernelGGL((gemm_spec_kernel<kGemmResidual, TL>), grid, dim3(TL::THREADS), 0, s, g); break;
     default: hipLaunchKernelGGL((gemm_spec_kernel<kGemmSwiglu, TL>), grid, dim3(TL::THREADS), 0, s, g); break;
+  }
+}
+
+template <class TL>
+static void launch_specw(const GemmArgs& g, int splits, hipStream_t s) {
+  const dim3 grid((unsigned)(((g.M + TL::BM - 1) / TL::BM) * (g.N / TL::BN)), 1, splits);
+  switch (g.mode) {
+    case kGemmQkvRope: hipLaunchKernelGGL((gemm_specw_kernel<kGemmQkvRope, TL>), grid, dim3(TL::THREADS), 0, s, g); break;
+    case kGemmResidual: hipLaunchKernelGGL((gemm_specw_kernel<kGemmResidual, TL>), grid, dim3(TL::THREADS), 0, s, g); break;
+    default: hipLaunchKernelGGL((gemm_specw_kernel<kGemmSwiglu, TL>), grid, dim3(TL::THREADS), 0, s, g); break;
   }
 }
 
@@ -1204,6 +1366,7 @@ hb_status launch_gemm(const GemmArgs& ga, stream_t s) {
     else launch_tile<Tile128W8, true>(g, p.splits, (hipStream_t)s);
   } else if (p.tile == kTileS256) launch_spec<TileS256>(g, p.splits, (hipStream_t)s);
   else if (p.tile == kTileW224) launch_sub<TileW224>(g, p.splits, (hipStream_t)s);
+  else if (p.tile == kTileSW224) launch_specw<TileSW224>(g, p.splits, (hipStream_t)s);
   else if (p.tile == kTileW256) launch_sub<TileW256>(g, p.splits, (hipStream_t)s);
   else if (p.tile == kTile256) launch_tile<Tile256, false>(g, p.splits, (hipStream_t)s);
   else if (p.tile == kTile128W8) launch_tile<Tile128W8, false>(g, p.splits, (hipStream_t)s);

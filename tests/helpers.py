@@ -100,6 +100,7 @@ def gemm_plan_workload(case):
         "mistral_T200": (W.MISTRAL, [184], [700], 16),
         "mistral_T700": (W.MISTRAL, [660], [900], 40),
         "yi_T256": (W.YI, [224], [800], 32),
+        "mistral_T1000": (W.MISTRAL, [960], [500], 40),
     }[case]
     rng = np.random.default_rng(11)
     ctx = rng.integers(1, 1500, size=n_dec).astype(np.int32)

@@ -320,20 +320,24 @@ def test_full_size_tau_sweep(tau):
     _full_size(W.tau_sweep(tau, 0), 32)
 
 
-@pytest.mark.parametrize("case", ["yi_T512", "mistral_T2048", "mistral_T200", "mistral_T700", "yi_T256"])
+@pytest.mark.parametrize("case", ["yi_T512", "mistral_T2048", "mistral_T200", "mistral_T700", "yi_T256",
+                                  "mistral_T1000"])
 def test_full_size_other_gemm_plans(case):
     """Token counts whose GEMM tile / K-split plans the two named
     configurations do not reach (plans as the planner picks them):
     Yi at T = 512 (every projection on the wave-specialised 256x128 kernel:
     QKV with the RoPE/append epilogue, O and down with 2-way splits, gate/up
     with the SwiGLU epilogue); Mistral at T = 2048 (QKV on 256x256 with the
-    RoPE/append epilogue in the sub-step kernel, O, gate/up and down on the
-    specialised kernel without a split); Mistral at T = 200 (128-row tiles
+    RoPE/append epilogue in the sub-step kernel, O and down on the
+    specialised kernel without a split, gate/up on the wide specialised
+    256x224 kernel); Mistral at T = 200 (128-row tiles
     with 2- and 4-way splits); Mistral at T = 700 (all four projections on
     the specialised kernel with a ragged last row tile of 188 tokens); Yi at
     T = 256 (QKV on the specialised kernel with a 2-way split, so its
     partials go through the QKV reduce that applies RoPE and the KV append;
-    O and down on it with 4-way splits, gate/up on 256x256)."""
+    O and down on it with 4-way splits, gate/up on 256x256); Mistral at
+    T = 1000 (gate/up on the wide specialised kernel with a ragged last row
+    tile of 232 tokens)."""
     # Yi-shaped outputs: the literal max-abs bar lies below the layer's own
     # conditioning floor on this shape (CPU pin: tests/test_oracle_floor.py);
     # the bar is twice the stored oracle floor of these rows
