@@ -37,6 +37,7 @@ LAYER_KERNELS = {
     "gemm_kernel<0": "qkv_rope_append",
     "gemm_sub_kernel<0": "qkv_rope_append",
     "gemm_spec_kernel<0": "qkv_rope_append",
+    "gemm_specw_kernel<0": "qkv_rope_append",
     "gemm_f8w_kernel<0": "qkv_rope_append",
     "qkv_reduce_kernel": "qkv_split_reduce",
     "attn_chunk_kernel": "attn_chunk",
@@ -45,11 +46,13 @@ LAYER_KERNELS = {
     "gemm_kernel<1": "o_proj / down (residual)",
     "gemm_sub_kernel<1": "o_proj / down (residual)",
     "gemm_spec_kernel<1": "o_proj / down (residual)",
+    "gemm_specw_kernel<1": "o_proj / down (residual)",
     "gemm_f8w_kernel<1": "o_proj / down (residual)",
     "splitk_reduce_kernel": "split-K reduce (+rmsnorm)",
     "gemm_kernel<2": "gate_up_swiglu",
     "gemm_sub_kernel<2": "gate_up_swiglu",
     "gemm_spec_kernel<2": "gate_up_swiglu",
+    "gemm_specw_kernel<2": "gate_up_swiglu",
     "gemm_f8w_kernel<2": "gate_up_swiglu",
     "kv_append_kernel": "kv_append",
 }
@@ -168,10 +171,12 @@ STAGE_OF_KERNEL = {
     "gemm_kernel<2": ("gate_up_swiglu", "chunked_prefill_hybrid_layer_amd/csrc/gemm.hip"),
     "gemm_sub_kernel<2": ("gate_up_swiglu", "chunked_prefill_hybrid_layer_amd/csrc/gemm.hip"),
     "gemm_spec_kernel<2": ("gate_up_swiglu", "chunked_prefill_hybrid_layer_amd/csrc/gemm.hip"),
+    "gemm_specw_kernel<2": ("gate_up_swiglu", "chunked_prefill_hybrid_layer_amd/csrc/gemm.hip"),
     "gemm_f8w_kernel<2": ("gate_up_swiglu", "chunked_prefill_hybrid_layer_amd/csrc/gemm.hip"),
     "gemm_kernel<0": ("qkv_rope_append", "chunked_prefill_hybrid_layer_amd/csrc/gemm.hip"),
     "gemm_sub_kernel<0": ("qkv_rope_append", "chunked_prefill_hybrid_layer_amd/csrc/gemm.hip"),
     "gemm_spec_kernel<0": ("qkv_rope_append", "chunked_prefill_hybrid_layer_amd/csrc/gemm.hip"),
+    "gemm_specw_kernel<0": ("qkv_rope_append", "chunked_prefill_hybrid_layer_amd/csrc/gemm.hip"),
     "gemm_f8w_kernel<0": ("qkv_rope_append", "chunked_prefill_hybrid_layer_amd/csrc/gemm.hip"),
     "attn_chunk_kernel": ("attn_chunk", "chunked_prefill_hybrid_layer_amd/csrc/attention.hip"),
     "attn_decode_kernel": ("attn_decode", "chunked_prefill_hybrid_layer_amd/csrc/attention.hip"),

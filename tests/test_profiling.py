@@ -11,6 +11,7 @@ QKV = "void hb::gemm_kernel<0, hb::Tile<128, 96, 64, 4, 2, 4>, false>(hb::GemmAr
 NORM = "hb::rmsnorm_kernel(float const*, unsigned short const*, void*, int, float, float)"
 ATTN = "void hb::attn_chunk_kernel<128, false>(hb::AttnArgs, float)"
 O_PROJ = "void hb::gemm_kernel<1, hb::Tile<128, 128, 64, 4, 2, 4>, false>(hb::GemmArgs)"
+GATE_UP = "void hb::gemm_specw_kernel<2, hb::SpecWTile<256, 224> >(hb::GemmArgs)"
 DOWN = "void hb::gemm_spec_kernel<1, hb::SpecTile<256, 128, 3> >(hb::GemmArgs)"
 FILL = "void at::native::vectorized_elementwise_kernel<8, at::native::FillFunctor<float> >"
 
@@ -28,7 +29,7 @@ def _trace(path, launches):
 
 def _forward(scale=1):
     return [(NORM, 5000 * scale), (QKV, 40000 * scale), (ATTN, 30000 * scale), (O_PROJ, 25000 * scale),
-            (DOWN, 57000 * scale)]
+            (GATE_UP, 100000 * scale), (DOWN, 57000 * scale)]
 
 
 def test_forwards_are_cut_at_norm_then_qkv_and_foreign_kernels_are_dropped(tmp_path):
@@ -37,8 +38,8 @@ def test_forwards_are_cut_at_norm_then_qkv_and_foreign_kernels_are_dropped(tmp_p
     fw = P.forwards(str(p))
     assert len(fw) == 2
     assert [k for k, _, _ in fw[0]] == ["rmsnorm", "qkv_rope_append", "attn_chunk", "o_proj / down (residual)",
-                                        "o_proj / down (residual)"]
-    assert [d for _, d, _ in fw[1]] == [10.0, 80.0, 60.0, 50.0, 114.0]
+                                        "gate_up_swiglu", "o_proj / down (residual)"]
+    assert [d for _, d, _ in fw[1]] == [10.0, 80.0, 60.0, 50.0, 200.0, 114.0]
 
 
 def test_sequence_lists_launches_in_order_with_their_medians(tmp_path):
@@ -48,8 +49,8 @@ def test_sequence_lists_launches_in_order_with_their_medians(tmp_path):
     assert out.startswith("3 of 3 forwards")
     rows = [ln for ln in out.splitlines() if ln.startswith("| ") and ln[2].isdigit()]
     # the median of 1x, 3x, 2x is 2x; O comes before down (same short name, order tells them apart)
-    assert [r.split("|")[3].strip() for r in rows] == ["10.00", "80.00", "60.00", "50.00", "114.00"]
-    assert out.splitlines()[-1].split("|")[3].strip() == "314.00"
+    assert [r.split("|")[3].strip() for r in rows] == ["10.00", "80.00", "60.00", "50.00", "200.00", "114.00"]
+    assert out.splitlines()[-1].split("|")[3].strip() == "514.00"
 
 
 def test_sequence_without_a_forward_says_so(tmp_path):
