@@ -174,8 +174,8 @@ __device__ __forceinline__ void store_out4(const AttnArgs& a, size_t oi, float v
     }                                                                                         \
     float mb = sv[0];                                                                         \
     _Pragma("unroll") for (int e = 1; e < 8; ++e) mb = fmaxf(mb, sv[e]);                      \
-    mb = fmaxf(mb, __shfl_xor(mb, 16, 64));                                                   \
-    mb = fmaxf(mb, __shfl_xor(mb, 32, 64));                                                   \
+    mb = fmaxf(mb, xor16(mb));                                                                \
+    mb = fmaxf(mb, xor32(mb));                                                                \
     /* running max in log2 units (-inf while the row has seen no key: a     */                \
     /* multi-token row may see none in a step, or in a whole item)          */                \
     const float mn = fmaxf(m, mb * scale_log2);                                               \
@@ -263,8 +263,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
       DEC_COMPUTE(kb);
     }
   }
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
+  l += xor16(l);
+  l += xor32(l);
   if (valid) {
     const int head = kvh * g + hq, tok = t + tl;
     const float vsc = F8 ? a.v_scale : 1.0f;
@@ -570,7 +570,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = kb ? 0 : 1; v < 16; ++v) mb = __builtin_elementwise_maximum(mb, s[kb][v]);
-    mb = __builtin_elementwise_maximum(mb, __shfl_xor(mb, 32, 64)) * scale_log2;
+    mb = __builtin_elementwise_maximum(mb, xor32(mb)) * scale_log2;
     // The reference maximum m of a row (log2 units; -inf while the row saw no
     // key) moves only when a tile exceeds it by more than kLazyMax: the
     // probabilities then stay below 2^kLazyMax, and the accumulator rescale
@@ -612,7 +612,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     if (F8 && ti + 1 < ntiles) store_tile8(ti + 1, cur ^ 1);
   }
 
-  l += __shfl_xor(l, 32, 64);
+  l += xor32(l);
   if (valid) {
     const int head = kvh * g + hq;
     const float vsc = F8 ? a.v_scale : 1.0f;

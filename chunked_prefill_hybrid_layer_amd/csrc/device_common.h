@@ -108,15 +108,37 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) {
   return r;
 }
 
+// The value of lane l ^ 32 (xor32) or l ^ 16 (xor16), through gfx950's
+// v_permlane32_swap / v_permlane16_swap: two VALU instructions and a select,
+// where a shuffle goes through the LDS crossbar (ds_bpermute) and its latency.
+// Each swap takes two copies of x and returns them with the upper half (of
+// the wave, or of each 32-lane row pair) of the first exchanged with the
+// lower half of the second; the partner's value is in the copy the lane's
+// own half did not keep.
+__device__ __forceinline__ float xor32(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (threadIdx.x & 32) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float xor16(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (threadIdx.x & 16) ? r[0] : r[1]);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
+  v += xor32(v);
+  v += xor16(v);
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
 
 __device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, xor32(v));
+  v = fmaxf(v, xor16(v));
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  for (int o = 8; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
 }
 
