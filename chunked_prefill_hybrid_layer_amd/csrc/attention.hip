@@ -524,6 +524,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
       __syncthreads();
     }
     const uint16_t* kimg = &lds[cur][0];
+    // The QK and PV MFMAs run at raised wave priority, the softmax at the
+    // normal one: of the two waves of a SIMD (from two co-resident items),
+    // the one in an MFMA phase then issues each MFMA as soon as the pipe
+    // frees, and the other's softmax fills the issue slots in between.
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
 
     // QK: the two key blocks' accumulation chains alternate, and the fragment
     // reads run four ahead of the MFMAs that use them
@@ -552,6 +558,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
     // causal / end-of-range masks matter only on tiles reaching past the first
     // row's position or past the item's last key (wave-uniform test)
     if ((kt + 64 > it.key1) || (kt + 63 > first_pos)) {
@@ -599,6 +607,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
       for (int db = 0; db < NS; ++db) acc[db] *= alpha;
     }
     // key step q = 2 kb + h covers the tile's page q: keys 16 q + 8 hh .. +7 in this lane
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const bf16x8 pb = as_bf16x8(make_uint4(pk[q >> 1][4 * (q & 1)], pk[q >> 1][4 * (q & 1) + 1],
@@ -606,6 +616,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 #pragma unroll
       for (int db = 0; db < NS; ++db) acc[db] = mfma32x32x16(vf[q * NS + db], pb, acc[db]);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
     // FP8: the next tile's codes, loaded before this tile's compute, go into
     // the other LDS images (every wave finished reading them before this
     // iteration's barrier)
