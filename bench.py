@@ -227,7 +227,7 @@ def bench_batch(wl, name, steps, warmup, copies, calibrate_copy=False):
     x = torch.from_numpy(wl.x).cuda()
     y = torch.empty_like(x)
     # metadata: a ring of pinned host blobs and device blobs
-    RING, REC = 8, 4
+    RING, REC = 32, 16
     blob0 = hb.pack_metadata(hd, b.chunk_len, b.chunk_prefix, b.decode_ctx, b.block_table, b.num_pages,
                              b.token_budget)[0]
     size = blob0.nbytes
@@ -249,7 +249,8 @@ def bench_batch(wl, name, steps, warmup, copies, calibrate_copy=False):
     # refilled only after the forward that read it RING steps earlier has
     # finished: the compute stream records an event after every REC-th forward
     # (each packet between two kernels leaves a bubble of about 6-8 us, so not
-    # after every one), and the copy waits for the first one at or after it.
+    # after every one: every 16th costs about 0.4 us a step), and the copy
+    # waits for the first one at or after it.
     compute = torch.cuda.current_stream()
     upload = torch.cuda.Stream()
     copied = [torch.cuda.Event() for _ in range(RING)]

@@ -44,6 +44,8 @@
 //   residual: out = res + acc (fp32).
 //   SwiGLU:   the first half of the tile's columns are gate rows, the second
 //             half the up rows of the same FFN units; out = silu(gate) * up (bf16).
+//             The wide wave-specialised kernel interleaves them per 16-column
+//             MFMA block instead and applies SwiGLU in registers.
 
 #include <cmath>
 
@@ -982,6 +984,10 @@ __global__ __launch_bounds__(TL::THREADS) void gemm_spec_kernel(GemmArgs g) {
 // of its MFMAs, and the other consumer of its SIMD hides those reads.  One
 // barrier per stage: after it every consumer is done with the stage before
 // (its buffer takes the stage after next) and the next stage has landed.
+// For SwiGLU the tile interleaves gate and up rows within each 16-column
+// block and forms silu(gate) * up in registers (swiglu_epilogue_regs): 101-104
+// vs 106-107 us for the staged fp32 epilogue on the 512-token Mistral-shaped
+// gate/up, bit-identical output.
 template <int BM_, int BN_>
 struct SpecWTile {
   static constexpr int BM = BM_, BN = BN_, BK = 64, NST = 2;
@@ -1003,6 +1009,64 @@ struct SpecWTile {
   static_assert(EPI_ROWS % (BM / WM) == 0, "epilogue passes must hold whole consumer blocks");
 };
 using TileSW224 = SpecWTile<256, 224>;
+
+// SwiGLU column order of the wide wave-specialised kernel: tile column c is
+// FFN unit n0/2 + 8 (c / 16) + c % 8, a gate row in columns c % 16 < 8 and
+// the matching up row in c % 16 >= 8.  Every 16-column MFMA block then holds
+// eight units' gate and up values side by side, in lanes l and l ^ 8 of each
+// 16-lane row, so silu(gate) * up needs one lane swap and no fp32 staging.
+__device__ __forceinline__ const uint16_t* swiglu_pair_row(const GemmArgs& g, int c, int n0) {
+  const int unit = n0 / 2 + (c >> 4) * 8 + (c & 7);
+  return ((c & 8) ? g.w1 : g.w0) + (size_t)unit * g.K;
+}
+
+// Epilogue of the SwiGLU GEMM in that column order.  acc[i][j][e] is tile row
+// wm*WROWS + i*16 + 4*(lane>>4) + e, column wn*WCOLS + j*16 + (lane&15).  A
+// lane with (lane & 8) == 0 holds gate values; it swaps rows e = 2, 3 for the
+// partner's (lane ^ 8) up values of rows 0, 1 (a row_ror:8 DPP move, which
+// within a 16-lane row is exactly lane ^ 8), so each lane forms two outputs:
+// unit wn*WCOLS/2 + 8j + lane % 8, rows e = 0, 1 (gate lanes) or 2, 3 (up
+// lanes).  The bf16 outputs are staged row-major in LDS (one pass, 61 KB for
+// 256 x 112 units) and written out in 16-byte chunks.  Same arithmetic as the
+// staged epilogue: bit-identical outputs.
+template <class TL>
+__device__ __forceinline__ void swiglu_epilogue_regs(const GemmArgs& g, f32x4 (&acc)[TL::FM][TL::FN],
+                                                     unsigned char* smem, int m0, int n0, int wave, int wm, int wn,
+                                                     int lane, int tid) {
+  constexpr int BM = TL::BM, FM = TL::FM, FN = TL::FN, WROWS = BM / TL::WM, WCOLS = TL::BN / TL::WN;
+  constexpr int OLD = TL::BN / 2 + 8;   // staging row stride in bf16 (units + pad)
+  constexpr int CPRO = TL::BN / 16;     // 16-byte output chunks per row
+  static_assert(BM * OLD * 2 <= TL::LDS, "bf16 staging fits the kernel's LDS");
+  uint16_t* ob = reinterpret_cast<uint16_t*>(smem);
+  if (wave < TL::CONSUMERS) {
+    const bool gate_lane = (lane & 8) == 0;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const f32x4 a4 = acc[i][j];
+        const float s0 = gate_lane ? a4[2] : a4[0], s1 = gate_lane ? a4[3] : a4[1];
+        const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s0), 0x128, 0xf, 0xf, false));
+        const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s1), 0x128, 0xf, 0xf, false));
+        const float g0 = gate_lane ? a4[0] : r0, g1 = gate_lane ? a4[1] : r1;
+        const float u0 = gate_lane ? r0 : a4[2], u1 = gate_lane ? r1 : a4[3];
+        const uint32_t pk = pack2bf(g0 / (1.0f + __expf(-g0)) * u0, g1 / (1.0f + __expf(-g1)) * u1);
+        const int row = wm * WROWS + i * 16 + 4 * (lane >> 4) + (gate_lane ? 0 : 2);
+        const int unit = wn * (WCOLS / 2) + j * 8 + (lane & 7);
+        ob[row * OLD + unit] = (uint16_t)(pk & 0xffffu);
+        ob[(row + 1) * OLD + unit] = (uint16_t)(pk >> 16);
+      }
+  }
+  __syncthreads();
+  const int f0 = n0 / 2;
+  for (int idx = tid; idx < BM * CPRO; idx += TL::THREADS) {
+    const int r = idx / CPRO, c = idx % CPRO;
+    const int m = m0 + r;
+    if (m >= g.M) continue;
+    *reinterpret_cast<uint4*>(g.out_b + (size_t)m * g.ldo + f0 + c * 8) =
+        *reinterpret_cast<const uint4*>(ob + r * OLD + c * 8);
+  }
+}
 
 template <int MODE, class TL>
 __global__ __launch_bounds__(TL::THREADS) __attribute__((amdgpu_waves_per_eu(3))) void gemm_specw_kernel(GemmArgs g) {
@@ -1044,8 +1108,8 @@ __global__ __launch_bounds__(TL::THREADS) __attribute__((amdgpu_waves_per_eu(3))
       const int r = RPL * q + lane / CPR;
       const int rr = r < BM ? r : r - BM;
       const int c = swz<CPR>(rr, lane % CPR);
-      gsrc[i] = (r < BM ? g.a + (size_t)min(m0 + rr, g.M - 1) * g.lda : weight_row<MODE, TL::BN>(g, n0 + rr, n0)) +
-                (size_t)k_first * BK + c * 8;
+      const uint16_t* wrow = MODE == kGemmSwiglu ? swiglu_pair_row(g, rr, n0) : weight_row<MODE, TL::BN>(g, n0 + rr, n0);
+      gsrc[i] = (r < BM ? g.a + (size_t)min(m0 + rr, g.M - 1) * g.lda : wrow) + (size_t)k_first * BK + c * 8;
       ldst[i] = RPL * q * BK;
     }
     auto issue = [&](int kt) {
@@ -1113,7 +1177,10 @@ __global__ __launch_bounds__(TL::THREADS) __attribute__((amdgpu_waves_per_eu(3))
 #undef RD
   }
   __syncthreads();
-  gemm_epilogue<MODE, TL, false>(g, acc, smem, m0, n0, wm, wn, lane, tid);
+  if (MODE == kGemmSwiglu)   // never split: the planner keeps SwiGLU whole
+    swiglu_epilogue_regs<TL>(g, acc, smem, m0, n0, wave, wm, wn, lane, tid);
+  else
+    gemm_epilogue<MODE, TL, false>(g, acc, smem, m0, n0, wm, wn, lane, tid);
 }
 
 // y[m][:] = res[m][:] + sum_z part[z][m][:] (z in order); with norm_out, also
