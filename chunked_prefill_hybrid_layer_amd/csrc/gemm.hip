@@ -42,10 +42,10 @@
 //             halves of every head, so that each rotated pair is two adjacent
 //             GEMM columns and any tile width holds whole pairs.
 //   residual: out = res + acc (fp32).
-//   SwiGLU:   the first half of the tile's columns are gate rows, the second
-//             half the up rows of the same FFN units; out = silu(gate) * up (bf16).
-//             The wide wave-specialised kernel interleaves them per 16-column
-//             MFMA block instead and applies SwiGLU in registers.
+//   SwiGLU:   each 16-column MFMA block holds eight FFN units, their gate rows
+//             in its first eight columns and the matching up rows in the last
+//             eight; out = silu(gate) * up (bf16), formed in registers with one
+//             lane swap in the bf16 kernels.
 
 #include <cmath>
 
@@ -119,8 +119,9 @@ __device__ __forceinline__ const uint16_t* weight_row(const GemmArgs& g, int n, 
     if (n < g.n0 + g.n1) return g.w1 + (size_t)(n - g.n0) * g.K;
     return g.w2 + (size_t)(n - g.n0 - g.n1) * g.K;
   } else if (MODE == kGemmSwiglu) {
-    const int f0 = n0 / 2, c = n - n0;
-    return (c < BN / 2) ? g.w0 + (size_t)(f0 + c) * g.K : g.w1 + (size_t)(f0 + c - BN / 2) * g.K;
+    // tile column c: unit n0/2 + 8 (c / 16) + c % 8, gate for c % 16 < 8, else up
+    const int c = n - n0, unit = n0 / 2 + (c >> 4) * 8 + (c & 7);
+    return ((c & 8) ? g.w1 : g.w0) + (size_t)unit * g.K;
   } else {
     return g.w0 + (size_t)n * g.K;
   }
@@ -136,8 +137,8 @@ __device__ __forceinline__ float weight_scale(const GemmArgs& g, int n, int n0) 
     if (n < g.n0 + g.n1) return g.ws1[n - g.n0];
     return g.ws2[n - g.n0 - g.n1];
   } else if (MODE == kGemmSwiglu) {
-    const int f0 = n0 / 2, c = n - n0;
-    return (c < BN / 2) ? g.ws0[f0 + c] : g.ws1[f0 + c - BN / 2];
+    const int c = n - n0, unit = n0 / 2 + (c >> 4) * 8 + (c & 7);
+    return (c & 8) ? g.ws1[unit] : g.ws0[unit];
   } else {
     return g.ws0[n];
   }
@@ -276,8 +277,9 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x4 (&acc)[TL
         const int r = idx / (BN / 8), c4 = idx % (BN / 8);
         const int m = mb + r;
         if (m >= g.M) continue;
-        const float* gr = Cs + r * CS_LD + c4 * 4;
-        const float* ur = gr + BN / 2;
+        // units 4 c4 .. 4 c4 + 3: gate columns 16 (c4 / 2) + 4 (c4 % 2) .. +3, up 8 further
+        const float* gr = Cs + r * CS_LD + (c4 >> 1) * 16 + (c4 & 1) * 4;
+        const float* ur = gr + 8;
         float o[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -307,6 +309,72 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x4 (&acc)[TL
       }
     }
   }
+}
+
+// SwiGLU epilogue of the bf16 kernels.  Every SwiGLU tile orders its columns
+// so that each 16-column MFMA block holds eight FFN units: column c is unit
+// n0/2 + 8 (c / 16) + c % 8, a gate row for c % 16 < 8 and the matching up
+// row for c % 16 >= 8 (weight_row).  acc[i][j][e] is tile row
+// wm*WROWS + i*16 + 4*(lane>>4) + e, column wn*WCOLS + j*16 + (lane&15), so a
+// unit's gate and up values sit in lanes l and l ^ 8 of a 16-lane row.  A gate
+// lane swaps its rows e = 2, 3 for the partner's up values of rows 0, 1 (a
+// row_ror:8 DPP move, which within 16 lanes is exactly lane ^ 8), and each
+// lane forms two outputs: unit wn*WCOLS/2 + 8j + lane % 8, rows e = 0, 1 (gate
+// lanes) or 2, 3 (up lanes).  The bf16 outputs are staged row-major in LDS (one
+// pass) and written out in 16-byte chunks.  The arithmetic is the staged
+// epilogue's, so outputs are bit-identical; it saves the fp32 tile's LDS round
+// trip (wide specialised gate/up at 512 tokens: 106-107 -> 101-104 us).
+// has_acc: the calling wave holds an accumulator block (not a producer).
+template <class TL>
+__device__ __forceinline__ void swiglu_epilogue_regs(const GemmArgs& g, f32x4 (&acc)[TL::FM][TL::FN],
+                                                     unsigned char* smem, int m0, int n0, bool has_acc, int wm,
+                                                     int wn, int lane, int tid) {
+  constexpr int BM = TL::BM, FM = TL::FM, FN = TL::FN, WROWS = BM / TL::WM, WCOLS = TL::BN / TL::WN;
+  constexpr int OLD = TL::BN / 2 + 8;   // staging row stride in bf16 (units + pad)
+  constexpr int CPRO = TL::BN / 16;     // 16-byte output chunks per row
+  static_assert(BM * OLD * 2 <= TL::LDS, "bf16 staging fits the kernel's LDS");
+  uint16_t* ob = reinterpret_cast<uint16_t*>(smem);
+  if (has_acc) {
+    const bool gate_lane = (lane & 8) == 0;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const f32x4 a4 = acc[i][j];
+        const float s0 = gate_lane ? a4[2] : a4[0], s1 = gate_lane ? a4[3] : a4[1];
+        const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s0), 0x128, 0xf, 0xf, false));
+        const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s1), 0x128, 0xf, 0xf, false));
+        const float g0 = gate_lane ? a4[0] : r0, g1 = gate_lane ? a4[1] : r1;
+        const float u0 = gate_lane ? r0 : a4[2], u1 = gate_lane ? r1 : a4[3];
+        const uint32_t pk = pack2bf(g0 / (1.0f + __expf(-g0)) * u0, g1 / (1.0f + __expf(-g1)) * u1);
+        const int row = wm * WROWS + i * 16 + 4 * (lane >> 4) + (gate_lane ? 0 : 2);
+        const int unit = wn * (WCOLS / 2) + j * 8 + (lane & 7);
+        ob[row * OLD + unit] = (uint16_t)(pk & 0xffffu);
+        ob[(row + 1) * OLD + unit] = (uint16_t)(pk >> 16);
+      }
+  }
+  __syncthreads();
+  const int f0 = n0 / 2;
+  for (int idx = tid; idx < BM * CPRO; idx += TL::THREADS) {
+    const int r = idx / CPRO, c = idx % CPRO;
+    const int m = m0 + r;
+    if (m >= g.M) continue;
+    *reinterpret_cast<uint4*>(g.out_b + (size_t)m * g.ldo + f0 + c * 8) =
+        *reinterpret_cast<const uint4*>(ob + r * OLD + c * 8);
+  }
+}
+
+// bf16 kernels: SwiGLU in registers, the other modes through gemm_epilogue
+// (F8SCALE: whether that instantiation keeps the runtime FP8 column-scale
+// branch; each kernel keeps the variant its register allocation was tuned
+// with: compiling it out made the 256 x 128 specialised kernel spill 4 VGPRs).
+template <int MODE, class TL, bool F8SCALE = true>
+__device__ __forceinline__ void gemm_epilogue_bf16(const GemmArgs& g, f32x4 (&acc)[TL::FM][TL::FN], unsigned char* smem,
+                                                   int m0, int n0, bool has_acc, int wm, int wn, int lane, int tid) {
+  if (MODE == kGemmSwiglu)   // never split: the planner keeps SwiGLU whole
+    swiglu_epilogue_regs<TL>(g, acc, smem, m0, n0, has_acc, wm, wn, lane, tid);
+  else
+    gemm_epilogue<MODE, TL, F8SCALE>(g, acc, smem, m0, n0, wm, wn, lane, tid);
 }
 
 // F8: A and the weights are e4m3 codes (K counted in 16-bit units, so a 64-unit
@@ -539,7 +607,10 @@ __global__ __launch_bounds__(TL::THREADS) void gemm_kernel(GemmArgs g) {
   WAIT_VMCNT(0);
   __syncthreads();
 
-  gemm_epilogue<MODE, TL>(g, acc, smem, m0, n0, wm, wn, lane, tid);
+  if (F8)
+    gemm_epilogue<MODE, TL>(g, acc, smem, m0, n0, wm, wn, lane, tid);
+  else
+    gemm_epilogue_bf16<MODE, TL>(g, acc, smem, m0, n0, true, wm, wn, lane, tid);
 }
 
 // Sub-step pipeline (stages of BK = 64, two LDS buffers, one barrier per
@@ -684,7 +755,7 @@ __global__ __launch_bounds__(TL::THREADS) void gemm_sub_kernel(GemmArgs g) {
 #undef ISSUE_STAGE
   WAIT_VMCNT(0);
   __syncthreads();
-  gemm_epilogue<MODE, TL>(g, acc, smem, m0, n0, wm, wn, lane, tid);
+  gemm_epilogue_bf16<MODE, TL>(g, acc, smem, m0, n0, true, wm, wn, lane, tid);
 }
 
 // FP8 wide tiles (256 x 224, 256 x 256).  A 64-unit stage row is 128 codes,
@@ -972,7 +1043,7 @@ __global__ __launch_bounds__(TL::THREADS) void gemm_spec_kernel(GemmArgs g) {
 #undef RD
   }
   __syncthreads();
-  gemm_epilogue<MODE, TL>(g, acc, smem, m0, n0, wm, 0, lane, tid);
+  gemm_epilogue_bf16<MODE, TL>(g, acc, smem, m0, n0, wave < TL::CONSUMERS, wm, 0, lane, tid);
 }
 
 // Wide wave-specialised pipeline (256 x 224): 12 waves, three per SIMD.
@@ -984,10 +1055,6 @@ __global__ __launch_bounds__(TL::THREADS) void gemm_spec_kernel(GemmArgs g) {
 // of its MFMAs, and the other consumer of its SIMD hides those reads.  One
 // barrier per stage: after it every consumer is done with the stage before
 // (its buffer takes the stage after next) and the next stage has landed.
-// For SwiGLU the tile interleaves gate and up rows within each 16-column
-// block and forms silu(gate) * up in registers (swiglu_epilogue_regs): 101-104
-// vs 106-107 us for the staged fp32 epilogue on the 512-token Mistral-shaped
-// gate/up, bit-identical output.
 template <int BM_, int BN_>
 struct SpecWTile {
   static constexpr int BM = BM_, BN = BN_, BK = 64, NST = 2;
@@ -1010,63 +1077,6 @@ struct SpecWTile {
 };
 using TileSW224 = SpecWTile<256, 224>;
 
-// SwiGLU column order of the wide wave-specialised kernel: tile column c is
-// FFN unit n0/2 + 8 (c / 16) + c % 8, a gate row in columns c % 16 < 8 and
-// the matching up row in c % 16 >= 8.  Every 16-column MFMA block then holds
-// eight units' gate and up values side by side, in lanes l and l ^ 8 of each
-// 16-lane row, so silu(gate) * up needs one lane swap and no fp32 staging.
-__device__ __forceinline__ const uint16_t* swiglu_pair_row(const GemmArgs& g, int c, int n0) {
-  const int unit = n0 / 2 + (c >> 4) * 8 + (c & 7);
-  return ((c & 8) ? g.w1 : g.w0) + (size_t)unit * g.K;
-}
-
-// Epilogue of the SwiGLU GEMM in that column order.  acc[i][j][e] is tile row
-// wm*WROWS + i*16 + 4*(lane>>4) + e, column wn*WCOLS + j*16 + (lane&15).  A
-// lane with (lane & 8) == 0 holds gate values; it swaps rows e = 2, 3 for the
-// partner's (lane ^ 8) up values of rows 0, 1 (a row_ror:8 DPP move, which
-// within a 16-lane row is exactly lane ^ 8), so each lane forms two outputs:
-// unit wn*WCOLS/2 + 8j + lane % 8, rows e = 0, 1 (gate lanes) or 2, 3 (up
-// lanes).  The bf16 outputs are staged row-major in LDS (one pass, 61 KB for
-// 256 x 112 units) and written out in 16-byte chunks.  Same arithmetic as the
-// staged epilogue: bit-identical outputs.
-template <class TL>
-__device__ __forceinline__ void swiglu_epilogue_regs(const GemmArgs& g, f32x4 (&acc)[TL::FM][TL::FN],
-                                                     unsigned char* smem, int m0, int n0, int wave, int wm, int wn,
-                                                     int lane, int tid) {
-  constexpr int BM = TL::BM, FM = TL::FM, FN = TL::FN, WROWS = BM / TL::WM, WCOLS = TL::BN / TL::WN;
-  constexpr int OLD = TL::BN / 2 + 8;   // staging row stride in bf16 (units + pad)
-  constexpr int CPRO = TL::BN / 16;     // 16-byte output chunks per row
-  static_assert(BM * OLD * 2 <= TL::LDS, "bf16 staging fits the kernel's LDS");
-  uint16_t* ob = reinterpret_cast<uint16_t*>(smem);
-  if (wave < TL::CONSUMERS) {
-    const bool gate_lane = (lane & 8) == 0;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const f32x4 a4 = acc[i][j];
-        const float s0 = gate_lane ? a4[2] : a4[0], s1 = gate_lane ? a4[3] : a4[1];
-        const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s0), 0x128, 0xf, 0xf, false));
-        const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s1), 0x128, 0xf, 0xf, false));
-        const float g0 = gate_lane ? a4[0] : r0, g1 = gate_lane ? a4[1] : r1;
-        const float u0 = gate_lane ? r0 : a4[2], u1 = gate_lane ? r1 : a4[3];
-        const uint32_t pk = pack2bf(g0 / (1.0f + __expf(-g0)) * u0, g1 / (1.0f + __expf(-g1)) * u1);
-        const int row = wm * WROWS + i * 16 + 4 * (lane >> 4) + (gate_lane ? 0 : 2);
-        const int unit = wn * (WCOLS / 2) + j * 8 + (lane & 7);
-        ob[row * OLD + unit] = (uint16_t)(pk & 0xffffu);
-        ob[(row + 1) * OLD + unit] = (uint16_t)(pk >> 16);
-      }
-  }
-  __syncthreads();
-  const int f0 = n0 / 2;
-  for (int idx = tid; idx < BM * CPRO; idx += TL::THREADS) {
-    const int r = idx / CPRO, c = idx % CPRO;
-    const int m = m0 + r;
-    if (m >= g.M) continue;
-    *reinterpret_cast<uint4*>(g.out_b + (size_t)m * g.ldo + f0 + c * 8) =
-        *reinterpret_cast<const uint4*>(ob + r * OLD + c * 8);
-  }
-}
 
 template <int MODE, class TL>
 __global__ __launch_bounds__(TL::THREADS) __attribute__((amdgpu_waves_per_eu(3))) void gemm_specw_kernel(GemmArgs g) {
@@ -1108,8 +1118,8 @@ __global__ __launch_bounds__(TL::THREADS) __attribute__((amdgpu_waves_per_eu(3))
       const int r = RPL * q + lane / CPR;
       const int rr = r < BM ? r : r - BM;
       const int c = swz<CPR>(rr, lane % CPR);
-      const uint16_t* wrow = MODE == kGemmSwiglu ? swiglu_pair_row(g, rr, n0) : weight_row<MODE, TL::BN>(g, n0 + rr, n0);
-      gsrc[i] = (r < BM ? g.a + (size_t)min(m0 + rr, g.M - 1) * g.lda : wrow) + (size_t)k_first * BK + c * 8;
+      gsrc[i] = (r < BM ? g.a + (size_t)min(m0 + rr, g.M - 1) * g.lda : weight_row<MODE, TL::BN>(g, n0 + rr, n0)) +
+                (size_t)k_first * BK + c * 8;
       ldst[i] = RPL * q * BK;
     }
     auto issue = [&](int kt) {
@@ -1177,10 +1187,7 @@ __global__ __launch_bounds__(TL::THREADS) __attribute__((amdgpu_waves_per_eu(3))
 #undef RD
   }
   __syncthreads();
-  if (MODE == kGemmSwiglu)   // never split: the planner keeps SwiGLU whole
-    swiglu_epilogue_regs<TL>(g, acc, smem, m0, n0, wave, wm, wn, lane, tid);
-  else
-    gemm_epilogue<MODE, TL, false>(g, acc, smem, m0, n0, wm, wn, lane, tid);
+  gemm_epilogue_bf16<MODE, TL, false>(g, acc, smem, m0, n0, wave < TL::CONSUMERS, wm, wn, lane, tid);
 }
 
 // y[m][:] = res[m][:] + sum_z part[z][m][:] (z in order); with norm_out, also
