@@ -324,43 +324,60 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x4 (&acc)[TL
 // pass) and written out in 16-byte chunks.  The arithmetic is the staged
 // epilogue's, so outputs are bit-identical; it saves the fp32 tile's LDS round
 // trip (wide specialised gate/up at 512 tokens: 106-107 -> 101-104 us).
+// F8OUT (FP8 projections): each lane first scales its values by the input
+// scale and its column's weight-row scale, and the outputs are e4m3 codes of
+// out / a_scale (one byte each).
 // has_acc: the calling wave holds an accumulator block (not a producer).
-template <class TL>
+template <class TL, bool F8OUT = false>
 __device__ __forceinline__ void swiglu_epilogue_regs(const GemmArgs& g, f32x4 (&acc)[TL::FM][TL::FN],
                                                      unsigned char* smem, int m0, int n0, bool has_acc, int wm,
                                                      int wn, int lane, int tid) {
   constexpr int BM = TL::BM, FM = TL::FM, FN = TL::FN, WROWS = BM / TL::WM, WCOLS = TL::BN / TL::WN;
-  constexpr int OLD = TL::BN / 2 + 8;   // staging row stride in bf16 (units + pad)
-  constexpr int CPRO = TL::BN / 16;     // 16-byte output chunks per row
-  static_assert(BM * OLD * 2 <= TL::LDS, "bf16 staging fits the kernel's LDS");
+  constexpr int UNITS = TL::BN / 2;
+  // staging row stride in output elements (units + pad, rows 16-byte aligned)
+  constexpr int OLD = F8OUT ? UNITS + 16 : UNITS + 8;
+  constexpr int EB = F8OUT ? 1 : 2;             // bytes per output element
+  constexpr int CPRO = UNITS * EB / 16;         // 16-byte output chunks per row
+  static_assert(BM * OLD * EB <= TL::LDS, "output staging fits the kernel's LDS");
+  static_assert((UNITS * EB) % 16 == 0, "rows of whole 16-byte chunks");
   uint16_t* ob = reinterpret_cast<uint16_t*>(smem);
+  uint8_t* ob8 = smem;
   if (has_acc) {
     const bool gate_lane = (lane & 8) == 0;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const f32x4 a4 = acc[i][j];
+        f32x4 a4 = acc[i][j];
+        if (F8OUT)   // codes -> values: input scale times this lane's column (weight row) scale
+          a4 *= g.a_scale * weight_scale<kGemmSwiglu, TL::BN>(g, n0 + wn * WCOLS + j * 16 + (lane & 15), n0);
         const float s0 = gate_lane ? a4[2] : a4[0], s1 = gate_lane ? a4[3] : a4[1];
         const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s0), 0x128, 0xf, 0xf, false));
         const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s1), 0x128, 0xf, 0xf, false));
         const float g0 = gate_lane ? a4[0] : r0, g1 = gate_lane ? a4[1] : r1;
         const float u0 = gate_lane ? r0 : a4[2], u1 = gate_lane ? r1 : a4[3];
-        const uint32_t pk = pack2bf(g0 / (1.0f + __expf(-g0)) * u0, g1 / (1.0f + __expf(-g1)) * u1);
+        const float o0 = g0 / (1.0f + __expf(-g0)) * u0, o1 = g1 / (1.0f + __expf(-g1)) * u1;
         const int row = wm * WROWS + i * 16 + 4 * (lane >> 4) + (gate_lane ? 0 : 2);
         const int unit = wn * (WCOLS / 2) + j * 8 + (lane & 7);
-        ob[row * OLD + unit] = (uint16_t)(pk & 0xffffu);
-        ob[(row + 1) * OLD + unit] = (uint16_t)(pk >> 16);
+        if (F8OUT) {   // the down projection's input: FP8 codes of out / a_scale
+          ob8[row * OLD + unit] = fp8_code(o0 * g.out_inv_scale);
+          ob8[(row + 1) * OLD + unit] = fp8_code(o1 * g.out_inv_scale);
+        } else {
+          const uint32_t pk = pack2bf(o0, o1);
+          ob[row * OLD + unit] = (uint16_t)(pk & 0xffffu);
+          ob[(row + 1) * OLD + unit] = (uint16_t)(pk >> 16);
+        }
       }
   }
   __syncthreads();
   const int f0 = n0 / 2;
+  uint8_t* out = reinterpret_cast<uint8_t*>(g.out_b);
   for (int idx = tid; idx < BM * CPRO; idx += TL::THREADS) {
     const int r = idx / CPRO, c = idx % CPRO;
     const int m = m0 + r;
     if (m >= g.M) continue;
-    *reinterpret_cast<uint4*>(g.out_b + (size_t)m * g.ldo + f0 + c * 8) =
-        *reinterpret_cast<const uint4*>(ob + r * OLD + c * 8);
+    *reinterpret_cast<uint4*>(out + ((size_t)m * g.ldo + f0) * EB + c * 16) =
+        *reinterpret_cast<const uint4*>(smem + (size_t)r * OLD * EB + c * 16);
   }
 }
 
@@ -607,7 +624,9 @@ __global__ __launch_bounds__(TL::THREADS) void gemm_kernel(GemmArgs g) {
   WAIT_VMCNT(0);
   __syncthreads();
 
-  if (F8)
+  if (F8 && MODE == kGemmSwiglu)
+    swiglu_epilogue_regs<TL, true>(g, acc, smem, m0, n0, true, wm, wn, lane, tid);
+  else if (F8)
     gemm_epilogue<MODE, TL>(g, acc, smem, m0, n0, wm, wn, lane, tid);
   else
     gemm_epilogue_bf16<MODE, TL>(g, acc, smem, m0, n0, true, wm, wn, lane, tid);
@@ -863,7 +882,10 @@ __global__ __launch_bounds__(TL::THREADS) void gemm_f8w_kernel(GemmArgs g) {
 #undef ISSUE_STAGE
   WAIT_VMCNT(0);
   __syncthreads();
-  gemm_epilogue<MODE, TL>(g, acc, smem, m0, n0, wm, wn, lane, tid);
+  if (MODE == kGemmSwiglu)
+    swiglu_epilogue_regs<TL, true>(g, acc, smem, m0, n0, true, wm, wn, lane, tid);
+  else
+    gemm_epilogue<MODE, TL>(g, acc, smem, m0, n0, wm, wn, lane, tid);
 }
 
 // Wave-specialised pipeline.  Consumer waves 0-3 (one per SIMD) run every
