@@ -266,6 +266,47 @@ def test_layer_edge_cases(case):
     compare_cache(layer.cache_logical(), cache, b.num_pages, _new_slots(b), case)
 
 
+def _random_batch(seed):
+    """A seeded random hybrid batch: 0-4 chunk pieces (a third of them short
+    verify pieces of 1-8 tokens deep in a context, the rest 1-300 tokens at
+    prefixes 0-1500) and 0-12 decodes with contexts 0-2000, on one of three
+    small layer shapes (g = 4, 1 and 7)."""
+    rng = np.random.default_rng(1000 + seed)
+    shape = [dict(n_q=8, n_kv=2, head_dim=128),
+             dict(n_q=4, n_kv=4, head_dim=64, hidden=256, ffn=512),
+             dict(n_q=14, n_kv=2, head_dim=128, hidden=1024, ffn=1536)][seed % 3]
+    cl, cp = [], []
+    for _ in range(int(rng.integers(0, 5))):
+        if rng.random() < 1 / 3:
+            cl.append(int(rng.integers(1, 9)))
+            cp.append(int(rng.integers(1, 2001)))
+        else:
+            cl.append(int(rng.integers(1, 301)))
+            cp.append(int(rng.integers(0, 1501)))
+    dc = [int(c) for c in rng.integers(0, 2001, size=int(rng.integers(0, 13)))]
+    if not cl and not dc:
+        dc = [int(rng.integers(0, 2001))]
+    return dict(shape, chunk_len=tuple(cl), chunk_prefix=tuple(cp), decode_ctx=tuple(dc))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_layer_parity_random_batches(seed):
+    """Seeded random batch compositions (mixes of long chunks, short verify
+    pieces and decodes a fixed list of cases may not reach): every output row
+    and the whole cache against the oracle, at the literal bars."""
+    kw = _random_batch(seed)
+    log(f"random batch {seed}: chunks {kw['chunk_len']} at prefixes {kw['chunk_prefix']}, "
+        f"decodes {kw['decode_ctx']}, g={kw['n_q'] // kw['n_kv']} d={kw['head_dim']}")
+    wl = W.small(20 + seed, **kw)
+    b = wl.batch
+    layer = _layer_for(wl)
+    layer.fill_prefixes(b.block_table, range(b.n_seq), wl.prefix_k, wl.prefix_v)
+    y, _ = _run(layer, wl)
+    r, cache = oracle_forward(wl)
+    assert_close(y, r.y, f"random batch {seed}")
+    compare_cache(layer.cache_logical(), cache, b.num_pages, _new_slots(b), f"random batch {seed}")
+
+
 # ---------------------------------------------------------------- full-size configurations
 
 def _full_size(wl, n_random, bar_case=None):
