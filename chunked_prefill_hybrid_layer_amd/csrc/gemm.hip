@@ -150,16 +150,35 @@ __device__ __forceinline__ float weight_scale(const GemmArgs& g, int n, int n0) 
 // half: dim i pairs with dim i + d/2), q goes to the q buffer, k and v to the
 // paged cache at the token's slot (bf16, or FP8 codes of x / scale).  q and K
 // stores are 8 bytes (4 in FP8); V (dim-major in a page) takes one store per dim.
+// The rotation's cos/sin pairs of dims i0 .. i0 + 3 at the token's position
+// and the token's cache slot, requested on their own so that a caller can
+// issue them before its other loads.
+struct QkvTokenData {
+  float4 cs01, cs23;
+  int slot;
+};
+__device__ __forceinline__ QkvTokenData qkv_token_data(const GemmArgs& g, int m, int n) {
+  const int d = g.head_dim, half = d >> 1;
+  const int hb = n / d, i0 = (n - hb * d) >> 1;
+  const int c = hb * d + i0;
+  QkvTokenData t;
+  t.slot = g.slot[m];
+  if (c < (g.n_q_heads + g.n_kv_heads) * d) {
+    const float4* rp = reinterpret_cast<const float4*>(g.rope + ((size_t)g.tok_pos[m] * half + i0) * 2);
+    t.cs01 = rp[0];
+    t.cs23 = rp[1];
+  }
+  return t;
+}
+
 __device__ __forceinline__ void qkv_store4(const GemmArgs& g, int m, int n, const float (&x0)[4],
-                                           const float (&x1)[4]) {
+                                           const float (&x1)[4], const QkvTokenData& td) {
   const int d = g.head_dim, half = d >> 1;
   const int qdim = g.n_q_heads * d, kdim = g.n_kv_heads * d;
   const int hb = n / d, i0 = (n - hb * d) >> 1;
   const int c = hb * d + i0;  // natural column of dim i0
   if (c < qdim + kdim) {
-    const int pos = g.tok_pos[m];
-    const float4* rp = reinterpret_cast<const float4*>(g.rope + ((size_t)pos * half + i0) * 2);
-    const float4 cs01 = rp[0], cs23 = rp[1];
+    const float4 cs01 = td.cs01, cs23 = td.cs23;
     const float cs[4] = {cs01.x, cs01.z, cs23.x, cs23.z}, sn[4] = {cs01.y, cs01.w, cs23.y, cs23.w};
     float y0[4], y1[4];
 #pragma unroll
@@ -176,7 +195,7 @@ __device__ __forceinline__ void qkv_store4(const GemmArgs& g, int m, int n, cons
     } else if (g.kv_fp8) {
       // FP8 K page block: [d/32][16 slots][32] codes of k / k_scale
       const int kvh = (c - qdim) / d;
-      const int sl = g.slot[m];
+      const int sl = td.slot;
       uint8_t* kb = static_cast<uint8_t*>(g.k_cache) + ((size_t)(sl >> 4) * g.n_kv_heads + kvh) * 16 * d +
                     (sl & 15) * 32;
       const float s = g.k_inv_scale;
@@ -186,7 +205,7 @@ __device__ __forceinline__ void qkv_store4(const GemmArgs& g, int m, int n, cons
           pack4fp8(y1[0] * s, y1[1] * s, y1[2] * s, y1[3] * s);
     } else {
       const int kvh = (c - qdim) / d;
-      const int sl = g.slot[m];
+      const int sl = td.slot;
       // K page block: [d/32][16 slots][32]; dims i0 .. i0 + 3 share a 32-dim slice
       uint16_t* kb = static_cast<uint16_t*>(g.k_cache) + ((size_t)(sl >> 4) * g.n_kv_heads + kvh) * 16 * d +
                      (sl & 15) * 32;
@@ -195,7 +214,7 @@ __device__ __forceinline__ void qkv_store4(const GemmArgs& g, int m, int n, cons
     }
   } else {
     const int kvh = (c - qdim - kdim) / d;
-    const int sl = g.slot[m];
+    const int sl = td.slot;
     const size_t vo = (((size_t)(sl >> 4) * g.n_kv_heads + kvh) * d + i0) * 16 + (sl & 15);
     if (g.kv_fp8) {
       uint8_t* vp = static_cast<uint8_t*>(g.v_cache) + vo;
@@ -305,7 +324,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x4 (&acc)[TL
         const float4 a = *reinterpret_cast<const float4*>(Cs + r * CS_LD + c8 * 8);
         const float4 b = *reinterpret_cast<const float4*>(Cs + r * CS_LD + c8 * 8 + 4);
         const float x0[4] = {a.x, a.z, b.x, b.z}, x1[4] = {a.y, a.w, b.y, b.w};
-        qkv_store4(g, m, n0 + c8 * 8, x0, x1);
+        qkv_store4(g, m, n0 + c8 * 8, x0, x1, qkv_token_data(g, m, n0 + c8 * 8));
       }
     }
   }
@@ -1296,6 +1315,9 @@ __global__ __launch_bounds__(256) void qkv_reduce_kernel(GemmArgs g, int splits)
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (int64_t)g.M * groups) return;
   const int m = (int)(idx / groups), n = (int)(idx % groups) * 8;
+  // the position -> rotation-table chain is requested first, so that it
+  // overlaps the slices' loads instead of following them
+  const QkvTokenData td = qkv_token_data(g, m, n);
   float4 u[kMaxSplits], v[kMaxSplits];   // every slice loaded before any is added
 #pragma unroll
   for (int z = 0; z < kMaxSplits; ++z) {
@@ -1314,7 +1336,7 @@ __global__ __launch_bounds__(256) void qkv_reduce_kernel(GemmArgs g, int splits)
     }
   }
   const float x0[4] = {a.x, a.z, b.x, b.z}, x1[4] = {a.y, a.w, b.y, b.w};
-  qkv_store4(g, m, n, x0, x1);
+  qkv_store4(g, m, n, x0, x1, td);
 }
 
 enum { kTile256 = 1, kTileW256 = 2, kTileW224 = 3, kTile128W8 = 4, kTile128N96 = 5, kTileS256 = 6, kTileSW224 = 7 };
