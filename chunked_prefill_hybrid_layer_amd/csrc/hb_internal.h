@@ -20,6 +20,7 @@ constexpr int kDecodeKeyStep = 32;    // keys per decode step (2 pages)
 constexpr int kDecodeKvSplit = 256;   // keys per decode attention item, at least (multiple of 32)
 constexpr int kDecodeKvSplitMax = 1024;  // at most: the decode kernel holds an item's page ids one per lane
 constexpr int kDecodeWavesTarget = 16384;  // decode items x kv heads beyond which the decode split doubles
+constexpr int kDecodeSlots = 3072;    // decode waves the machine runs at once (3 per SIMD x 1024 SIMDs)
 constexpr int kPageSize = 16;
 constexpr uint32_t kMetaVersion = 3;
 constexpr int kMaxGroup = 16;         // decode path holds a kv group in one 16-row MFMA tile

@@ -297,9 +297,13 @@ hb_status hb_pack_metadata(const hb_dims* dims, int32_t n_chunks, const int32_t*
     std::stable_sort(citems.begin(), citems.end(), [](const hb_attn_item& x, const hb_attn_item& y) {
       return (x.key1 - x.key0) / 256 > (y.key1 - y.key0) / 256;
     });
-    // Keys per decode item: kDecodeKvSplit, doubled (up to kDecodeKvSplitMax)
-    // while a large decode batch would still make more than
-    // kDecodeWavesTarget (item, kv head) waves: past that the split buys no
+    // Keys per decode item: kDecodeKvSplit, unless its (item, kv head) waves
+    // would spill past one round of the machine (kDecodeSlots) while a
+    // longer split, still a multiple of kDecodeKeyStep and at most
+    // kDecodeKvSplitMax, fits them in one: then the smallest such split, so
+    // that no nearly empty second round trails the stream.  A batch too large
+    // for one round keeps kDecodeKvSplit, doubled while it would still make
+    // more than kDecodeWavesTarget waves: past that the split buys no
     // parallelism, only partial results to write and merge.
     int dsplit = kDecodeKvSplit;
     auto decode_items = [&](int split) {
@@ -308,7 +312,17 @@ hb_status hb_pack_metadata(const hb_dims* dims, int32_t n_chunks, const int32_t*
         if (decode_path(s)) n += (kv_len[s] + split - 1) / split;
       return n;
     };
-    while (dsplit < kDecodeKvSplitMax && decode_items(dsplit) * dims->n_kv_heads > kDecodeWavesTarget) dsplit *= 2;
+    const int64_t nkv_d = dims->n_kv_heads;
+    if (decode_items(dsplit) * nkv_d > kDecodeSlots && decode_items(kDecodeKvSplitMax) * nkv_d <= kDecodeSlots) {
+      int lo = kDecodeKvSplit / kDecodeKeyStep, hi = kDecodeKvSplitMax / kDecodeKeyStep;   // in key steps
+      while (lo < hi) {   // decode_items is non-increasing in the split: bisect
+        const int mid = (lo + hi) / 2;
+        if (decode_items(mid * kDecodeKeyStep) * nkv_d <= kDecodeSlots) hi = mid;
+        else lo = mid + 1;
+      }
+      dsplit = lo * kDecodeKeyStep;
+    }
+    while (dsplit < kDecodeKvSplitMax && decode_items(dsplit) * nkv_d > kDecodeWavesTarget) dsplit *= 2;
     for (int s = 0; s < S; ++s) {
       if (!decode_path(s)) continue;
       const int t = q_start[s], n = newtok[s];

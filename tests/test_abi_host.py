@@ -179,8 +179,9 @@ def test_large_decode_batch_widens_the_decode_key_split():
     """512 decodes of 1000-6000 context keys: the decode split grows past its
     256-key minimum (at most 1024, the page ids one decode wave can hold), the
     items still cover every decode's keys exactly once, and both item lists
-    run longest key range first (chunk items in 256-key buckets).  32 decodes
-    keep 256."""
+    run longest key range first (chunk items in 256-key buckets).  32 decodes,
+    whose 256-key items would spill just past one round of the machine (3072
+    waves), take the smallest multiple of 32 keys that fits them in one."""
     rng = np.random.default_rng(7)
     dc = rng.integers(1000, 6000, 512)
     cl, cp = np.array([64]), np.array([100])
@@ -208,7 +209,14 @@ def test_large_decode_batch_widens_the_decode_key_split():
     kv2 = np.concatenate([cp + cl, small + 1])
     bt2, npg2 = W.deal_block_tables(kv2, 16, rng)
     blob2, _ = _pack(W.YI, cl, cp, small, bt2, npg2)
-    assert hb.header(blob2).decode_kv_split == 256
+    h2 = hb.header(blob2)
+    waves = lambda split: int(np.sum((small + 1 + split - 1) // split)) * W.YI.n_kv_heads
+    assert waves(256) > 3072
+    assert h2.decode_kv_split % 32 == 0 and waves(h2.decode_kv_split) <= 3072 < waves(h2.decode_kv_split - 32)
+    assert h2.n_decode_items * W.YI.n_kv_heads == waves(h2.decode_kv_split)
+    # 8 decodes fit one round at 256 keys and keep it
+    blob3, _ = _pack(W.YI, cl, cp, small[:8], bt2, npg2)
+    assert hb.header(blob3).decode_kv_split == 256
 
 
 def test_worked_example_through_pack():
