@@ -35,7 +35,8 @@
 // Split-K (grid.z > 1, when the tiles alone leave CUs idle): each K slice writes an fp32 partial tile and a reduce kernel adds the slices in a
 // fixed order (results do not depend on timing) before applying the epilogue.
 //
-// Epilogues (the accumulator tile is staged through LDS as fp32):
+// Epilogues (the accumulator tile is staged through LDS as fp32, except
+// SwiGLU, which stages only its bf16 or FP8 outputs):
 //   QKV:      RoPE (rotate-half, table-driven) on q and k; q -> bf16 buffer;
 //             k and v -> the paged KV cache at the tokens' slots (KV append).
 //             The weight rows are read in an order that interleaves the two
@@ -44,8 +45,8 @@
 //   residual: out = res + acc (fp32).
 //   SwiGLU:   each 16-column MFMA block holds eight FFN units, their gate rows
 //             in its first eight columns and the matching up rows in the last
-//             eight; out = silu(gate) * up (bf16), formed in registers with one
-//             lane swap in the bf16 kernels.
+//             eight; out = silu(gate) * up (bf16, or FP8 codes), formed in
+//             registers after one lane swap.
 
 #include <cmath>
 
