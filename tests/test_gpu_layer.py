@@ -266,15 +266,15 @@ def test_layer_edge_cases(case):
     compare_cache(layer.cache_logical(), cache, b.num_pages, _new_slots(b), case)
 
 
-def _random_batch(seed):
+def _random_batch(seed, shapes=3):
     """A seeded random hybrid batch: 0-4 chunk pieces (a third of them short
     verify pieces of 1-8 tokens deep in a context, the rest 1-300 tokens at
-    prefixes 0-1500) and 0-12 decodes with contexts 0-2000, on one of three
-    small layer shapes (g = 4, 1 and 7)."""
+    prefixes 0-1500) and 0-12 decodes with contexts 0-2000, on one of the
+    first `shapes` of three small layer shapes (g = 4, 1 and 7)."""
     rng = np.random.default_rng(1000 + seed)
     shape = [dict(n_q=8, n_kv=2, head_dim=128),
              dict(n_q=4, n_kv=4, head_dim=64, hidden=256, ffn=512),
-             dict(n_q=14, n_kv=2, head_dim=128, hidden=1024, ffn=1536)][seed % 3]
+             dict(n_q=14, n_kv=2, head_dim=128, hidden=1024, ffn=1536)][seed % shapes]
     cl, cp = [], []
     for _ in range(int(rng.integers(0, 5))):
         if rng.random() < 1 / 3:
@@ -305,6 +305,24 @@ def test_layer_parity_random_batches(seed):
     r, cache = oracle_forward(wl)
     assert_close(y, r.y, f"random batch {seed}")
     compare_cache(layer.cache_logical(), cache, b.num_pages, _new_slots(b), f"random batch {seed}")
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_layer_parity_random_batches_kv_fp8(seed):
+    """The same random compositions over an FP8 cache (g = 4 and 1): y within
+    the literal bars of the oracle reading the same quantised K/V, untouched
+    cache bytes bit-exact and new codes within one e4m3 step."""
+    kw = _random_batch(100 + seed, shapes=2)
+    log(f"random batch kv fp8 {seed}: chunks {kw['chunk_len']} at prefixes {kw['chunk_prefix']}, "
+        f"decodes {kw['decode_ctx']}, g={kw['n_q'] // kw['n_kv']} d={kw['head_dim']}")
+    wl = W.with_kv_fp8(W.small(40 + seed, **kw))
+    b = wl.batch
+    layer = _layer_for(wl)
+    layer.fill_prefixes(b.block_table, range(b.n_seq), wl.prefix_k, wl.prefix_v)
+    y, _ = _run(layer, wl)
+    r, cache = oracle_forward(wl)
+    assert_close(y, r.y, f"random batch kv fp8 {seed}")
+    compare_cache(layer.cache_logical(), cache, b.num_pages, _new_slots(b), f"random batch kv fp8 {seed}")
 
 
 # ---------------------------------------------------------------- full-size configurations
