@@ -29,8 +29,8 @@
 // one run (sched_group_barrier interleaves them).  The narrow tiles keep a
 // ring of 3-4 LDS stages; the wide tiles keep two 64 KB stages with one
 // barrier per stage (see gemm_sub_kernel).  Workgroups are renumbered so that
-// each XCD (own L2) walks a contiguous run of tiles, M fastest: the M tiles
-// sharing a weight tile run on one XCD.
+// each XCD (own L2) walks a contiguous run of tiles, M fastest, and keeps to
+// one K slice of a split (block_tile).
 //
 // Split-K (grid.z > 1, when the tiles alone leave CUs idle): each K slice writes an fp32 partial tile and a reduce kernel adds the slices in a
 // fixed order (results do not depend on timing) before applying the epilogue.
@@ -236,6 +236,37 @@ __device__ __forceinline__ void qkv_store4(const GemmArgs& g, int m, int n, cons
 }
 
 
+// Which tile (tm, tn) and K slice z a workgroup takes.  Workgroups reach the
+// eight XCDs (each with its own L2) round-robin in launch order, x fastest,
+// then z.  Each XCD gets a contiguous run of tiles, M fastest, so the row
+// tiles that share a weight tile run on one XCD.  With a K split into z
+// slices (8 % z == 0) each XCD also keeps to one slice, 8 / z XCDs per slice:
+// the slice's activation columns, which every tile of the XCD reads, can then
+// stay in its L2, where handing every XCD tiles of every slice made each one
+// stream the whole activation matrix (the 4-way split down projection at 512
+// tokens read its 14.7 MB of activations once per XCD).
+struct BlockTile {
+  int tm, tn, z;
+};
+__device__ __forceinline__ bool xcd_slices() {
+  return ((gridDim.x * gridDim.z) & 7) == 0 && (8 % gridDim.z) == 0;
+}
+__device__ __forceinline__ int block_slice() {
+  if (!xcd_slices()) return blockIdx.z;
+  const int xcd = (blockIdx.x + gridDim.x * blockIdx.z) & 7;
+  return xcd / (8 / gridDim.z);
+}
+__device__ __forceinline__ BlockTile block_tile(int tiles_m) {
+  int tile = blockIdx.x, z = blockIdx.z;
+  if (xcd_slices()) {
+    const int L = blockIdx.x + gridDim.x * blockIdx.z;   // launch order
+    const int xcd = L & 7, i = L >> 3, per_slice = 8 / gridDim.z;
+    z = xcd / per_slice;
+    tile = (xcd % per_slice) * (gridDim.x * gridDim.z / 8) + i;
+  }
+  return BlockTile{tile % tiles_m, tile / tiles_m, z};
+}
+
 // Epilogue, in passes of EPI_ROWS tile rows staged through LDS as fp32:
 // acc[i][j][e] is C[wm*WROWS + i*16 + 4*(lane>>4) + e][wn*WCOLS + j*16 + (lane&15)].
 template <int MODE, class TL, bool F8 = true>
@@ -269,8 +300,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x4 (&acc)[TL
     }
     __syncthreads();
     const int mb = m0 + p * ER;   // first token of this pass
-    if (gridDim.z > 1) {  // split-K: raw fp32 partial into slice blockIdx.z
-      float* out = g.part + (size_t)blockIdx.z * g.M * g.N;
+    if (gridDim.z > 1) {  // split-K: raw fp32 partial into this workgroup's slice
+      float* out = g.part + (size_t)block_slice() * g.M * g.N;
       for (int idx = tid; idx < ER * BN / 4; idx += NT) {
         const int r = idx / (BN / 4), c4 = idx % (BN / 4);
         const int m = mb + r;
@@ -429,14 +460,12 @@ __global__ __launch_bounds__(TL::THREADS) void gemm_kernel(GemmArgs g) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / TL::WN, wn = wave % TL::WN;
   const int tiles_m = (g.M + BM - 1) / BM;
-  int bid = blockIdx.x;
-  const int nblk = gridDim.x;
-  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
-  const int tm = bid % tiles_m, tn = bid / tiles_m;
+  const BlockTile btile = block_tile(tiles_m);
+  const int tm = btile.tm, tn = btile.tn;
   const int m0 = tm * BM, n0 = tn * BN;
   // K slice of this workgroup (split-K along grid.z)
   const int nk = (g.K / BK) / gridDim.z;
-  const int k_first = blockIdx.z * nk;
+  const int k_first = btile.z * nk;
 
   // DMA mapping: load q = wave + WAVES * i covers rows [RPL q, RPL q + RPL) of
   // the stage image (A rows first, then B rows); lane l lands at row
@@ -672,13 +701,11 @@ __global__ __launch_bounds__(TL::THREADS) void gemm_sub_kernel(GemmArgs g) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / TL::WN, wn = wave % TL::WN;
   const int tiles_m = (g.M + BM - 1) / BM;
-  int bid = blockIdx.x;
-  const int nblk = gridDim.x;
-  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
-  const int tm = bid % tiles_m, tn = bid / tiles_m;
+  const BlockTile btile = block_tile(tiles_m);
+  const int tm = btile.tm, tn = btile.tn;
   const int m0 = tm * BM, n0 = tn * BN;
   const int nk = (g.K / BK) / gridDim.z;
-  const int k_first = blockIdx.z * nk;
+  const int k_first = btile.z * nk;
 
   // Load split: the A rows' loads (activations, L2-resident) go to waves
   // 4-7, the weight rows' loads (first touch from HBM) to waves 0-3.  Waves
@@ -823,13 +850,11 @@ __global__ __launch_bounds__(TL::THREADS) void gemm_f8w_kernel(GemmArgs g) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / TL::WN, wn = wave % TL::WN;
   const int tiles_m = (g.M + BM - 1) / BM;
-  int bid = blockIdx.x;
-  const int nblk = gridDim.x;
-  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
-  const int tm = bid % tiles_m, tn = bid / tiles_m;
+  const BlockTile btile = block_tile(tiles_m);
+  const int tm = btile.tm, tn = btile.tn;
   const int m0 = tm * BM, n0 = tn * BN;
   const int nk = (g.K / BK) / gridDim.z;
-  const int k_first = blockIdx.z * nk;
+  const int k_first = btile.z * nk;
 
   // DMA mapping of the ring kernel: load q = wave + WAVES * i covers rows
   // [RPL q, RPL q + RPL) of the stage image; waves short of a load repeat the
@@ -952,13 +977,11 @@ __global__ __launch_bounds__(TL::THREADS) void gemm_spec_kernel(GemmArgs g) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tiles_m = (g.M + BM - 1) / BM;
-  int bid = blockIdx.x;
-  const int nblk = gridDim.x;
-  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
-  const int tm = bid % tiles_m, tn = bid / tiles_m;
+  const BlockTile btile = block_tile(tiles_m);
+  const int tm = btile.tm, tn = btile.tn;
   const int m0 = tm * BM, n0 = tn * TL::BN;
   const int nk = (g.K / BK) / gridDim.z;
-  const int k_first = blockIdx.z * nk;
+  const int k_first = btile.z * nk;
 
   f32x4 acc[FM][FN];
 #pragma unroll
@@ -1133,13 +1156,11 @@ __global__ __launch_bounds__(TL::THREADS) __attribute__((amdgpu_waves_per_eu(3))
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tiles_m = (g.M + BM - 1) / BM;
-  int bid = blockIdx.x;
-  const int nblk = gridDim.x;
-  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
-  const int tm = bid % tiles_m, tn = bid / tiles_m;
+  const BlockTile btile = block_tile(tiles_m);
+  const int tm = btile.tm, tn = btile.tn;
   const int m0 = tm * BM, n0 = tn * TL::BN;
   const int nk = (g.K / BK) / gridDim.z;
-  const int k_first = blockIdx.z * nk;
+  const int k_first = btile.z * nk;
 
   // accumulators: set in each branch, so they are not live through the
   // producers' loop
