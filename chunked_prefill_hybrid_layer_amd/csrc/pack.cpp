@@ -322,7 +322,8 @@ hb_status hb_pack_metadata(const hb_dims* dims, int32_t n_chunks, const int32_t*
       }
       dsplit = lo * kDecodeKeyStep;
     }
-    while (dsplit < kDecodeKvSplitMax && decode_items(dsplit) * nkv_d > kDecodeWavesTarget) dsplit *= 2;
+    while (dsplit < kDecodeKvSplitMax && decode_items(dsplit) * nkv_d > kDecodeWavesTarget)
+      dsplit = std::min(2 * dsplit, kDecodeKvSplitMax);   // an item's page ids fill at most one wave's lanes
     for (int s = 0; s < S; ++s) {
       if (!decode_path(s)) continue;
       const int t = q_start[s], n = newtok[s];
