@@ -28,6 +28,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 #include "device_common.h"
 
 namespace hb {
@@ -659,36 +661,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 
 // ----------------------------------------------------------------------------
 // merge: o = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p over a token's
-// partials, in one pass with a running maximum (the sums are rescaled when it
-// grows), four partials in flight at a time, in partial order (deterministic).
-// D/4 lanes per (token, head), each owning 4 consecutive dims.  A partial that
-// saw no key of its token has m = -inf and weight 0.
+// partials, with a running maximum (the sums are rescaled when it grows), in
+// a fixed order (deterministic).  D/4 lanes per lane group, each owning 4
+// consecutive dims.  A partial that saw no key of its token has m = -inf and
+// weight 0.
+//
+// Partials first, first + stride, ... (count of them) of the (token, head)
+// pair whose first partial is p0, into the running (M, L, o): rounds of four
+// loaded together, slots past the last counting as empty (m = -inf).
 template <int D>
-__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
-  constexpr int LPH = D / 4;                 // lanes per (token, head)
-  constexpr int PER_BLOCK = 256 / LPH;
-  const int sub = threadIdx.x / LPH, l4 = threadIdx.x % LPH;
-  const int64_t wid = (int64_t)blockIdx.x * PER_BLOCK + sub;
+__device__ __forceinline__ void merge_partials(const AttnArgs& a, int h, int l4, int p0, int first, int stride,
+                                               int count, float& M, float& L, float4& o) {
   const int nq = a.n_q_heads;
-  if (wid >= (int64_t)a.n_tokens * nq) return;
-  const int t = (int)(wid / nq), h = (int)(wid % nq);
-  const int p0 = a.meta.part_off[t], pc = a.meta.part_cnt[t];
-  if (pc <= 1) return;   // written by its one attention item
-  const float2* ml = reinterpret_cast<const float2*>(a.part_ml) + (size_t)p0 * nq + h;
-  const float* src = a.part_o + ((size_t)p0 * nq + h) * D + l4 * 4;
-  float M = -INFINITY, L = 0.f;
-  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-  // Steps of four partials, loaded together; slots past the token's last
-  // partial count as empty (m = -inf), so a token with 1..4 partials takes one
-  // round of loads.
-  for (int p = 0; p < pc; p += 4) {
+  const float2* ml = reinterpret_cast<const float2*>(a.part_ml) + (size_t)(p0 + first) * nq + h;
+  const float* src = a.part_o + ((size_t)(p0 + first) * nq + h) * D + l4 * 4;
+  for (int p = 0; p < count; p += 4) {
     float2 mv[4];
     float4 v[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      if (p + u < pc) {
-        mv[u] = ml[(size_t)(p + u) * nq];
-        v[u] = *reinterpret_cast<const float4*>(src + (size_t)(p + u) * nq * D);
+      if (p + u < count) {
+        const size_t q = (size_t)(p + u) * stride;
+        mv[u] = ml[q * nq];
+        v[u] = *reinterpret_cast<const float4*>(src + q * nq * D);
       } else {
         mv[u] = make_float2(-INFINITY, 0.f);
         v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -709,8 +704,103 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
       M = mn;
     }
   }
-  // FP8: codes of o / o_scale (the O projection's input)
-  store_out4(a, (size_t)t * nq * D + (size_t)h * D + l4 * 4, o.x, o.y, o.z, o.w, 1.0f / L);
+}
+
+// One lane group per (token, head) pair, except with G > 1: the decode
+// tokens [a.merge_tok0, n_tokens) then take G lane groups per pair, in the
+// workgroups from chunk_blocks on.  Group g merges partials g, g + G, ..., and
+// group 0 combines the groups' results through LDS in group order, so a pair
+// with up to 4 G partials takes one round of loads.  With G = 1 every token
+// takes the plain running-maximum pass.
+constexpr int kMergeMaxGroups = 4;
+
+template <int D, int G>
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int chunk_blocks) {
+  constexpr int LPH = D / 4;                       // lanes per group
+  constexpr int PER_BLOCK = 256 / LPH;             // lane groups per workgroup
+  static_assert(PER_BLOCK % G == 0, "whole (token, head) pairs per workgroup");
+  const int sub = threadIdx.x / LPH, l4 = threadIdx.x % LPH;
+  const int nq = a.n_q_heads;
+  if (G == 1 || (int)blockIdx.x < chunk_blocks) {
+    const int64_t wid = (int64_t)blockIdx.x * PER_BLOCK + sub;
+    if (wid >= (int64_t)(G == 1 ? a.n_tokens : a.merge_tok0) * nq) return;
+    const int t = (int)(wid / nq), h = (int)(wid % nq);
+    const int p0 = a.meta.part_off[t], pc = a.meta.part_cnt[t];
+    if (pc <= 1) return;   // written by its one attention item
+    float M = -INFINITY, L = 0.f;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    merge_partials<D>(a, h, l4, p0, 0, 1, pc, M, L, o);
+    // FP8: codes of o / o_scale (the O projection's input)
+    store_out4(a, (size_t)t * nq * D + (size_t)h * D + l4 * 4, o.x, o.y, o.z, o.w, 1.0f / L);
+    return;
+  }
+  // decode tokens, G groups per pair: every thread of these workgroups
+  // reaches the barrier
+  __shared__ float4 sm_o[PER_BLOCK][LPH];
+  __shared__ float2 sm_ml[PER_BLOCK];
+  const int pair = sub / G, grp = sub % G;
+  const int64_t wid = (int64_t)a.merge_tok0 * nq + (int64_t)((int)blockIdx.x - chunk_blocks) * (PER_BLOCK / G) + pair;
+  int t = 0, h = 0, p0 = 0, pc = 0;
+  if (wid < (int64_t)a.n_tokens * nq) {
+    t = (int)(wid / nq);
+    h = (int)(wid % nq);
+    p0 = a.meta.part_off[t];
+    pc = a.meta.part_cnt[t];
+  }
+  const bool active = pc > 1;   // else none, or written by its one attention item
+  float M = -INFINITY, L = 0.f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (active && grp < pc) merge_partials<D>(a, h, l4, p0, grp, G, (pc - grp + G - 1) / G, M, L, o);
+  sm_o[sub][l4] = o;
+  if (l4 == 0) sm_ml[sub] = make_float2(M, L);
+  __syncthreads();
+  if (!active || grp != 0) return;
+  float Mx = -INFINITY;
+#pragma unroll
+  for (int g = 0; g < G; ++g) Mx = fmaxf(Mx, sm_ml[sub + g].x);
+  float Lx = 0.f;
+  float4 ox = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float2 mlg = sm_ml[sub + g];
+    const float w = (mlg.x == -INFINITY) ? 0.f : fast_exp2(mlg.x - Mx);
+    const float4 og = sm_o[sub + g][l4];
+    Lx += w * mlg.y;
+    ox.x += w * og.x; ox.y += w * og.y; ox.z += w * og.z; ox.w += w * og.w;
+  }
+  store_out4(a, (size_t)t * nq * D + (size_t)h * D + l4 * 4, ox.x, ox.y, ox.z, ox.w, 1.0f / Lx);
+}
+
+// Lane groups per decode (token, head) pair, from the packed partial counts.
+// Chunk tokens keep one: their few partials (the tile's key splits) load in
+// one or two rounds, and grouping them measured slower (at tau = 128, 8
+// partials each: 9.2-10.1 us for the whole merge with two groups against
+// 8.0-8.5 with one).  Decode tokens take the fewest groups (1, 2 or 4)
+// that minimise the region's residency rounds (workgroups over the 8 per CU
+// that fit: 4 waves each, about 55 VGPRs) times the load rounds of its
+// longest pair: at tau = 128 (64 decodes, up to 26 partials) four groups took
+// the merge from 10.6-10.9 to 8.0-8.5 us; at Yi tau = 2048 (28672 decode
+// pairs, mostly 2-5 partials) more workgroups cost more rounds than they save
+// (four groups: 27 -> 32 us), and the plan keeps one.
+void merge_plan(const hb_meta_header* h, const void* meta_host, int* tok0, int* groups) {
+  const int T = h->n_tokens, nq = h->n_q_heads;
+  const int per_block = 1024 / h->head_dim;           // lane groups per 256-thread workgroup
+  const int32_t* pc = reinterpret_cast<const int32_t*>(static_cast<const char*>(meta_host) + h->off_part_cnt);
+  *tok0 = T - h->n_decodes;                           // decodes are the last tokens of the packed order
+  *groups = 1;
+  int max_pc = 0;
+  for (int t = *tok0; t < T; ++t) max_pc = std::max(max_pc, (int)pc[t]);
+  if (max_pc <= 4) return;
+  const int64_t pairs = (int64_t)h->n_decodes * nq;
+  int64_t best = -1;
+  for (int g = 1; g <= kMergeMaxGroups; g *= 2) {
+    const int64_t wgs = (pairs * g + per_block - 1) / per_block;
+    const int64_t cost = ((wgs + 8 * kNumCU - 1) / (8 * kNumCU)) * ((max_pc + 4 * g - 1) / (4 * g));
+    if (best < 0 || cost < best) {
+      best = cost;
+      *groups = g;
+    }
+  }
 }
 
 template <int D, bool F8>
@@ -731,10 +821,19 @@ static hb_status launch_attention_d(const AttnArgs& a, stream_t s, void* const* 
     hipLaunchKernelGGL((attn_decode_kernel<D, F8>), dim3((unsigned)a.n_decode_items * a.n_kv_heads), dim3(64), 0, st,
                        a, scale_log2);
   if (!mark(2)) return fail(HB_E_HIP, "attention: stage event record failed");
-  const int64_t pairs = (int64_t)a.n_tokens * a.n_q_heads, per_block = 256 / (D / 4);
-  if (a.n_merge_tokens > 0)
-    hipLaunchKernelGGL(attn_merge_kernel<D>, dim3((unsigned)((pairs + per_block - 1) / per_block)), dim3(256), 0, st,
-                       a);
+  if (a.n_merge_tokens > 0) {
+    const int64_t per_block = 256 / (D / 4), nq = a.n_q_heads, G = a.merge_groups;
+    if (G != 1 && G != 2 && G != kMergeMaxGroups) return fail(HB_E_SHAPE, "attention merge: 1, 2 or 4 lane groups");
+    if (a.merge_tok0 < 0 || a.merge_tok0 > a.n_tokens) return fail(HB_E_SHAPE, "attention merge: bad decode start");
+    const int64_t first = G == 1 ? a.n_tokens : a.merge_tok0;   // tokens of one group per pair
+    const int64_t chunk_blocks = (first * nq + per_block - 1) / per_block;
+    const int64_t blocks = chunk_blocks + ((a.n_tokens - first) * nq * G + per_block - 1) / per_block;
+    if (blocks > INT32_MAX) return fail(HB_E_SHAPE, "attention merge: grid too large");
+    const dim3 grid((unsigned)blocks);
+    if (G == 1) hipLaunchKernelGGL((attn_merge_kernel<D, 1>), grid, dim3(256), 0, st, a, (int)chunk_blocks);
+    else if (G == 2) hipLaunchKernelGGL((attn_merge_kernel<D, 2>), grid, dim3(256), 0, st, a, (int)chunk_blocks);
+    else hipLaunchKernelGGL((attn_merge_kernel<D, kMergeMaxGroups>), grid, dim3(256), 0, st, a, (int)chunk_blocks);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(HB_E_HIP, std::string("attention launch: ") + hipGetErrorString(e));
   return HB_OK;

@@ -142,6 +142,8 @@ struct AttnArgs {
   int n_q_heads, n_kv_heads, head_dim, group;
   int n_chunk_items, n_decode_items, n_tokens;
   int n_merge_tokens;      // tokens with more than one partial (0: no merge pass)
+  int merge_tok0;          // first decode token
+  int merge_groups;        // lane groups per decode (token, head) pair in the merge (1, 2 or 4)
   float* part_o;           // [n_partials][n_q][d]
   float* part_ml;          // [n_partials][n_q][2]
   void* out;               // [T][n_q * d] bf16, or FP8 codes of o * out_inv_scale (> 0)
@@ -151,5 +153,8 @@ struct AttnArgs {
 // tokens with more than one partial); ev, if not NULL, holds the events to
 // record before each launch (3 entries).
 hb_status launch_attention(const AttnArgs& a, stream_t s, void* const* ev);
+// The merge's first decode token and lane groups per decode (token, head)
+// pair, from the host copy of the metadata.
+void merge_plan(const hb_meta_header* h, const void* meta_host, int* tok0, int* groups);
 
 }  // namespace hb

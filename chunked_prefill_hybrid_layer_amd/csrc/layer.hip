@@ -204,6 +204,7 @@ static hb_status layer_forward_impl(const hb_dims* dims, const hb_weights* w, co
   at.n_decode_items = h->n_decode_items;
   at.n_tokens = T;
   at.n_merge_tokens = h->n_merge_tokens;
+  merge_plan(h, meta_host, &at.merge_tok0, &at.merge_groups);
   at.part_o = (float*)(ws + L.part_o);
   at.part_ml = (float*)(ws + L.part_ml);
   at.out = ob;

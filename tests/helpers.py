@@ -81,13 +81,20 @@ def conditioning_floor(wl, rows, cache_seqs, seed=0, eps=1e-7):
 # ---------------------------------------------------------------- workloads shared by tests and golden files
 
 # small layers for full-output parity (ragged chunks starting mid-page, decodes
-# around page boundaries; g = n_q / n_kv = 4, 7, 1, 16)
+# around page boundaries; g = n_q / n_kv = 4, 7, 1, 16).  The last two give
+# the decodes up to twelve attention partials (contexts of 3 K keys in
+# 256-key ranges), so the merge takes four lane groups per decode (token,
+# head), at d = 64 and 128; g16_d128 takes two.
 SMALL = {
     "g4_d128": dict(n_q=8, n_kv=2, head_dim=128),
     "g7_d128": dict(n_q=14, n_kv=2, head_dim=128, hidden=896 + 128, ffn=1536),
     "g1_d64": dict(n_q=4, n_kv=4, head_dim=64, hidden=256, ffn=512),
     "g16_d128": dict(n_q=16, n_kv=1, head_dim=128, chunk_len=(40,), chunk_prefix=(1100,),
                      decode_ctx=(0, 2047, 5)),
+    "g1_d64_many_partials": dict(n_q=4, n_kv=4, head_dim=64, hidden=256, ffn=512, chunk_len=(40,),
+                                 chunk_prefix=(3000,), decode_ctx=(3000, 1500, 7, 2900)),
+    "g4_d128_many_partials": dict(n_q=8, n_kv=2, head_dim=128, chunk_len=(40,), chunk_prefix=(3000,),
+                                  decode_ctx=(3000, 1500, 3)),
 }
 
 
