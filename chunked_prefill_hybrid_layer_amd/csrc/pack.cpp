@@ -94,6 +94,23 @@ hb_status check_meta(const hb_dims* d, const void* meta_host) {
   if (h->n_kv_heads != d->n_kv_heads || h->n_q_heads != d->n_q_heads || h->head_dim != d->head_dim ||
       h->page_size != d->page_size || h->group != d->n_q_heads / d->n_kv_heads)
     return fail(HB_E_META, "metadata was built for other dims");
+  // counts consistent and every array inside the blob (the host reads some
+  // of them, the kernels all of them at these offsets)
+  const int64_t hdr = (int64_t)sizeof(hb_meta_header);
+  auto in_blob = [&](int64_t off, int64_t count, int64_t elem) {
+    return count >= 0 && off >= hdr && off <= h->bytes && count * elem <= h->bytes - off;
+  };
+  const int64_t S = h->n_seq, T = h->n_tokens;
+  if (S < 1 || T < 0 || h->n_decodes < 0 || h->n_decodes > T || h->n_chunks < 0 || h->max_pages < 1 ||
+      h->n_partials < 0 || h->n_merge_tokens < 0 || h->n_merge_tokens > T || h->bytes < hdr ||
+      !in_blob(h->off_q_start, S + 1, 4) || !in_blob(h->off_cached, S, 4) || !in_blob(h->off_kv_len, S, 4) ||
+      !in_blob(h->off_tok_seq, T, 4) || !in_blob(h->off_tok_pos, T, 4) || !in_blob(h->off_slot, T, 4) ||
+      !in_blob(h->off_part_off, T, 4) || !in_blob(h->off_part_cnt, T, 4) ||
+      !in_blob(h->off_block_table, S * h->max_pages, 4) ||
+      !in_blob(h->off_chunk_items, h->n_chunk_items, (int64_t)sizeof(hb_attn_item)) ||
+      !in_blob(h->off_decode_items, h->n_decode_items, (int64_t)sizeof(hb_attn_item)) ||
+      !in_blob(h->off_append_runs, h->n_append_runs, (int64_t)sizeof(hb_append_run)))
+    return fail(HB_E_META, "metadata counts or array offsets do not fit the blob");
   return HB_OK;
 }
 

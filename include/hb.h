@@ -66,7 +66,9 @@ typedef enum {
   HB_E_ALIAS = 6,     /* one physical page is referenced twice */
   HB_E_CAPACITY = 7,  /* a caller buffer (metadata, workspace, rope table) is too small */
   HB_E_HIP = 8,       /* a HIP launch or runtime call failed */
-  HB_E_META = 9       /* the metadata blob is not one hb_pack_metadata wrote for these dims */
+  HB_E_META = 9       /* the metadata blob is not one hb_pack_metadata wrote for these dims
+                         (bad magic or version, other dims, or counts and array offsets
+                         that do not fit the blob's size) */
 } hb_status;
 
 /* Layer shape.  Supported: head_dim 64 or 128; n_q_heads % n_kv_heads == 0

@@ -336,6 +336,27 @@ def test_workspace_views_are_disjoint_regions_of_the_workspace(w8a8):
         hb.workspace_views(dims, np.zeros(64, np.uint8))
 
 
+def test_tampered_metadata_is_rejected():
+    """The library reads the blob's arrays at the offsets its header names
+    (the host the partial counts, the kernels all of them): a header whose
+    counts or offsets do not fit the blob is refused with HB_E_META before
+    anything reads it."""
+    wl = W.small(2, n_q=8, n_kv=2, head_dim=128)
+    b = wl.batch
+    dims = hb.make_dims(wl.dims)
+    blob, T = hb.pack_metadata(dims, b.chunk_len, b.chunk_prefix, b.decode_ctx, b.block_table, b.num_pages,
+                               b.token_budget)
+    assert hb.workspace_bytes(dims, blob) > 0
+    edits = [("n_decodes", T + 1), ("n_tokens", -1), ("n_seq", 0), ("off_part_cnt", None),
+             ("off_block_table", -8), ("bytes", 64), ("n_decode_items", 1 << 30)]
+    for field, value in edits:
+        bad = blob.copy()
+        h = hb.MetaHeader.from_buffer(bad)
+        setattr(h, field, int(h.bytes) if value is None else value)
+        with pytest.raises(hb.HbError, match="counts or array offsets"):
+            hb.workspace_bytes(dims, bad)
+
+
 def test_schedule_worked_example():
     """The worked Yi-34B iteration ("Sarathi-Serve reading notes" §7.6): tau
     2048, chunk 1024, six running decodes, R_A mid-prefill (4500-token prompt,
