@@ -777,9 +777,9 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int chunk_b
 // partials each: 9.2-10.1 us for the whole merge with two groups against
 // 8.0-8.5 with one).  Decode tokens take the fewest groups (1, 2 or 4)
 // that minimise the region's residency rounds (workgroups over the 8 per CU
-// that fit: 4 waves each, about 55 VGPRs) times the load rounds of its
+// that fit: 4 waves each, about 52 VGPRs) times the load rounds of its
 // longest pair: at tau = 128 (64 decodes, up to 26 partials) four groups took
-// the merge from 10.6-10.9 to 8.0-8.5 us; at Yi tau = 2048 (28672 decode
+// the merge kernel from 8.0 to 5.2 us; at Yi tau = 2048 (28672 decode
 // pairs, mostly 2-5 partials) more workgroups cost more rounds than they save
 // (four groups: 27 -> 32 us), and the plan keeps one.
 void merge_plan(const hb_meta_header* h, const void* meta_host, int* tok0, int* groups) {
